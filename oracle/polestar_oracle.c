@@ -244,7 +244,9 @@ int pso_kmeans_init(const pso_shape* s, int dtype, const void* H, int init, floa
  * One Lloyd iteration:
  *   assign  a_j = argmax_k <h_j, b(c_k)>   (b = bf16 rounding on the bf16
  *           path, identity on fp32; argmax is invariant to n_j > 0, so raw h)
- *   update  S_k = sum_{a_j = k} h_j / n_j (fp64), c_k = S_k / ||S_k||;
+ *   update  S_k = sum_{a_j = k} h_j / n_j in fp64, each term added as one
+ *           fused multiply-add of h by the fp64 reciprocal of n_j, members in
+ *           ascending j; c_k = S_k / ||S_k|| rounded to fp32;
  *           a cluster with no members (or ||S_k|| = 0) keeps its centre.
  * Returned assign is the last assignment, C the last update, so every c_k is
  * the normalised mean of its members.  objective = sum_k ||S_k||.
@@ -306,8 +308,9 @@ int pso_kmeans_fit(const pso_shape* s, int dtype, const void* H, const void* Kr,
                     if (aw[j] != k) continue;
                     ++cnt;
                     if (!(rn[j] > 0.0f)) continue;
+                    const double inv = 1.0 / (double)rn[j];
                     for (int e = 0; e < d; ++e)
-                        S[e] += (double)ld(H, dtype, hb + (size_t)j * d + e) / (double)rn[j];
+                        S[e] = fma((double)ld(H, dtype, hb + (size_t)j * d + e), inv, S[e]);
                 }
                 nw[k] = cnt;
                 double ss = 0.0;
