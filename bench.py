@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the Polestar-Cache drift-detection step on one MI355X.
+
+A step is one pass of the whole path over one batch of W windows:
+  spherical K-Means (warm start, `iters` Lloyd iterations) + centroid keys ->
+  NVFP4 residuals -> proxy attention + KL drift + cluster scores ->
+  top-k clusters -> refresh gather (positions, rebuilt hidden rows, K/V rows).
+Inputs are seeded synthetic tensors already resident in HBM (one snapshot per
+denoising step, generated on the device before the timed region).
+
+Prints one JSON line: metric, value (window-token-layers scored per second),
+the roofline of the dominant kernel (its HIP-event average launch time over the
+timed region against its algorithmic bytes) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--config C4] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "window-token-layers drift-scored/sec per step at 1 GPU; % HBM/MFMA roofline"
+UNIT = "window-token-layers/s"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def kernel_work(name, cfg):
+    """Algorithmic (bytes, flops) of ONE launch of a library kernel over all W
+    windows: every input the kernel needs read once, every output written once."""
+    W, N, d, K = cfg.W, cfg.N, cfg.d, cfg.K
+    e = 2 if cfg.bf16 else 4
+    KV = cfg.Hkv * cfg.dh
+    L = W * cfg.Hq * cfg.Nb * K
+    if name.startswith("k_assign"):
+        return W * N * d * e + W * K * d * e + W * N * 4, 2.0 * W * N * K * d
+    if name.startswith("k_update"):
+        return W * N * d * e + 2 * W * N * 4 + W * K * d * (4 + e) + W * (K + 1) * 4, W * N * d * 2.0
+    if name.startswith("k_residual"):
+        return (W * N * d * e + W * K * d * 4 + 3 * W * N * 4 + W * N * d // 2 + W * N * d // 16,
+                W * N * d * 8.0)
+    if name.startswith("k_keys"):
+        return W * N * KV * e + W * N * 4 + W * K * KV * e, W * N * KV * 1.0
+    if name.startswith("k_proxy"):
+        return (W * cfg.Nb * cfg.Hq * cfg.dh * e + W * K * KV * e + L * 4,
+                2.0 * W * cfg.Hq * cfg.Nb * K * cfg.dh)
+    if name.startswith("k_drift"):
+        return 2 * L * 4 + W * (cfg.Hq * cfg.Nb + cfg.Nb + K) * 4, L * 4.0
+    if name.startswith("k_bucket"):
+        return 2 * W * N * 4 + W * (K + 1) * 4, 0.0
+    return None
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle, unchanged, on a bounded sample: one steady-state step
+    (warm-started K-Means, residuals, proxy attention + KL, top-k, gather) of
+    independent windows, fanned out over host threads (ctypes releases the
+    GIL).  The formation step that produces each window's state is untimed."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle as O
+    import synth
+
+    P = min(16, os.cpu_count() or 1)
+    s = O.Shape(W=1, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
+    dt = O.BF16 if cfg.bf16 else O.F32
+
+    def prepare(w):
+        data = synth.generate(cfg, w0=w, Wc=1)
+        init = O.INIT_FARTHEST if cfg.init0 == "farthest" else O.INIT_STRIDED
+        r = O.kmeans_fit(s, dt, data["H"], data["Kr"], init, cfg.iters,
+                         np.zeros((1, cfg.K, cfg.d), np.float32))
+        lp = O.proxy_attn(s, dt, data["Q"], r["Ck"], cfg.softmax_scale)["logp"]
+        synth.apply_drift(cfg, data, 1, w0=w)
+        return data, r["C"], r["Ck"], lp
+
+    def step(args):
+        data, C, Ck, lp = args
+        t0 = time.perf_counter()
+        r = O.kmeans_fit(s, dt, data["H"], data["Kr"], O.INIT_GIVEN, cfg.iters, C.copy(), Ck.copy())
+        q = O.residual_nvfp4(s, dt, data["H"], r["row_norm"], r["C"], r["assign"])
+        pa = O.proxy_attn(s, dt, data["Q"], r["Ck"], cfg.softmax_scale, lp)
+        tk = O.topk_clusters(s, pa["score"], cfg.k)
+        O.refresh_gather(s, dt, r["assign"], tk["idx"], cfg.k, cfg.N, q["codes"], q["bscale"],
+                         q["rscale"], r["C"], r["row_norm"], True, data["Kr"], data["V"])
+        return time.perf_counter() - t0
+
+    # size the sample from one window timed alone: n windows, one per thread,
+    # about budget_s seconds of CPU work in total
+    one = step(prepare(0))
+    n = max(1, min(P, int(round(budget_s / max(one, 1e-3)))))
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        states = list(ex.map(prepare, range(1, n + 1)))
+        t0 = time.perf_counter()
+        list(ex.map(step, states))
+        wall = time.perf_counter() - t0
+    return {"value": n * cfg.N / wall, "unit": UNIT, "cores": n, "kind": "oracle",
+            "sample": f"{n} windows x 1 steady-state step of {cfg.name} "
+                      f"(N={cfg.N}, d={cfg.d}, K={cfg.K}, {cfg.iters} iterations), one window per "
+                      f"thread on {n} threads; one window's step alone took {one:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="C4", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timer")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this path runs on one GPU; windows are independent, so more GPUs "
+                                   "would each run their own share of the windows with no "
+                                   "communication (see DESIGN.md); --gpus must be 1"}))
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 1:
+        print("need --steps >= 1 and --warmup >= 1 (the first warmup step is window formation)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import drift_aware_kv_amd as P
+    import synth
+    from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
+    from synth.device import DeviceWorkload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    P.lib()
+    cfg = synth.CONFIGS[args.config]
+    total = args.warmup + args.steps
+    free = torch.cuda.mem_get_info()[0]
+    snap = DeviceWorkload.snapshot_bytes(cfg)
+    out_bytes = 3 * snap  # gather outputs at cap = N, plus state: generous
+    n_snap = max(2, min(total, int((0.6 * free - out_bytes) // snap)))
+    print(f"[bench] {cfg.name}: generating {n_snap} input snapshots of {snap / 2**30:.1f} GiB",
+          file=sys.stderr, flush=True)
+    wl = DeviceWorkload(cfg, n_snap)
+    spec = StepSpec(W=cfg.W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb,
+                    K=cfg.K, k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
+                    softmax_scale=cfg.softmax_scale, cap=cfg.N)
+    path = DriftPath(spec)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        path.step(*wl.inputs(i))
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    if not args.no_profile:
+        P.profile_begin(64 * args.steps * (cfg.iters + 8))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        path.step(*wl.inputs(i))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = {}
+    if not args.no_profile:
+        P.profile_end()
+        prof = P.profile_summary()
+    elapsed = t1 - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = args.steps * cfg.W * cfg.N / elapsed
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    kernels = {k: v for k, v in prof.items() if not k.startswith("#")}
+    breakdown = {k: {"launches": v[0], "avg_ms": v[1] / v[0], "total_ms_per_step": v[1] / args.steps}
+                 for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][1])}
+    roof = None
+    if kernels:
+        name, (n, tot, mn, mx) = max(kernels.items(), key=lambda kv: kv[1][1])
+        work = kernel_work(name, cfg)
+        avg_s = tot / n / 1e3
+        if work:
+            byts, flops = work
+            ai = flops / byts
+            if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+                ach = flops / avg_s / 1e12
+                roof = {"kernel": name, "bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
+            else:
+                ach = byts / avg_s / 1e9
+                roof = {"kernel": name, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+            roof.update({"algorithmic_bytes_per_launch": byts, "flops_per_launch": flops,
+                         "avg_launch_ms": avg_s * 1e3, "launches": n})
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, args.cpu_budget)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "windows": cfg.W, "window_tokens": cfg.N, "hidden": cfg.d,
+                   "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.dh, "block": cfg.Nb,
+                   "clusters": cfg.K, "top_k": cfg.k, "lloyd_iters": cfg.iters,
+                   "drift": f"{cfg.drift} {cfg.drift_frac:.0%} rows x {cfg.drift_mag}",
+                   "input_snapshots": n_snap, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": breakdown,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,408 @@
+// ps_attn.hip -- proxy attention of the decode block against the centroid
+// keys, the KL drift between consecutive steps, and the top-k selection of
+// the most drifted clusters (Polestar technical summary 2.A: drift
+// measurement; sparse updates), for gfx950.
+#include "ps_common.h"
+
+using namespace ps;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// proxy attention, bf16: z[k][i] = sigma * <Ck[k][g(h)], Q[i][h]> on MFMA
+// 16x16x32, one workgroup per window, one head per wave at a time.
+// Lane l holds clusters 16*mb + 4*(l/16) + r of query 16*nb + (l % 16).
+// ---------------------------------------------------------------------------
+template <int KB, int NBQ>
+__global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__ Q,
+                                                     const uint16_t* __restrict__ Ck, float sigma,
+                                                     float* __restrict__ logp, int Hq, int Hkv, int dh,
+                                                     int Nb, int K)
+{
+    const int w = blockIdx.x;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int G = Hq / Hkv;
+    for (int h = wave; h < Hq; h += 4) {
+        const int g = h / G;
+        floatx4 acc[KB][NBQ];
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int e0 = 0; e0 < dh; e0 += 32) {
+            const int e = e0 + 8 * q;
+            uint4 bq[NBQ];
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) {
+                const int i = 16 * nb + r16;
+                bq[nb] = (i < Nb && e < dh)
+                             ? *reinterpret_cast<const uint4*>(Q + (((size_t)w * Nb + i) * Hq + h) * dh + e)
+                             : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int mb = 0; mb < KB; ++mb) {
+                const int kk = 16 * mb + r16;
+                const uint4 av = (kk < K && e < dh)
+                                     ? *reinterpret_cast<const uint4*>(Ck + (((size_t)w * K + kk) * Hkv + g) * dh + e)
+                                     : make_uint4(0, 0, 0, 0);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+                for (int nb = 0; nb < NBQ; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bq[nb]),
+                                                                          acc[mb][nb], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) {
+            const int i = 16 * nb + r16;
+            float zmax = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int kk = 16 * mb + 4 * q + r;
+                    const float z = acc[mb][nb][r] * sigma;
+                    acc[mb][nb][r] = z;
+                    if (kk < K) zmax = fmaxf(zmax, z);
+                }
+            zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+            zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+            float se = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int kk = 16 * mb + 4 * q + r;
+                    if (kk < K) se += expf(acc[mb][nb][r] - zmax);
+                }
+            se += __shfl_xor(se, 16, 64);
+            se += __shfl_xor(se, 32, 64);
+            const float lse = zmax + logf(se);
+            if (i < Nb) {
+                float* out = logp + (((size_t)w * Hq + h) * Nb + i) * K;
+#pragma unroll
+                for (int mb = 0; mb < KB; ++mb) {
+                    const int k0 = 16 * mb + 4 * q;
+                    const float4 v = make_float4(acc[mb][nb][0] - lse, acc[mb][nb][1] - lse,
+                                                 acc[mb][nb][2] - lse, acc[mb][nb][3] - lse);
+                    if (k0 + 3 < K && (K & 3) == 0) {
+                        *reinterpret_cast<float4*>(out + k0) = v;
+                    } else {
+                        if (k0 < K) out[k0] = v.x;
+                        if (k0 + 1 < K) out[k0 + 1] = v.y;
+                        if (k0 + 2 < K) out[k0 + 2] = v.z;
+                        if (k0 + 3 < K) out[k0 + 3] = v.w;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// proxy attention, fp32 path: one thread per (h, i), three passes over K
+__global__ __launch_bounds__(256) void k_proxy_f32(const float* __restrict__ Q, const float* __restrict__ Ck,
+                                                    float sigma, float* __restrict__ logp, int Hq, int Hkv,
+                                                    int dh, int Nb, int K)
+{
+    const int w = blockIdx.y;
+    const int pair = blockIdx.x * 256 + threadIdx.x;
+    if (pair >= Hq * Nb) return;
+    const int h = pair / Nb, i = pair - h * Nb;
+    const int g = h / (Hq / Hkv);
+    const float* qv = Q + (((size_t)w * Nb + i) * Hq + h) * dh;
+    auto zk = [&](int k) {
+        const float* kv = Ck + (((size_t)w * K + k) * Hkv + g) * dh;
+        float s = 0.0f;
+        for (int e = 0; e < dh; ++e) s = fmaf(qv[e], kv[e], s);
+        return s * sigma;
+    };
+    float zmax = -INFINITY;
+    for (int k = 0; k < K; ++k) zmax = fmaxf(zmax, zk(k));
+    float se = 0.0f;
+    for (int k = 0; k < K; ++k) se += expf(zk(k) - zmax);
+    const float lse = zmax + logf(se);
+    float* out = logp + (((size_t)w * Hq + h) * Nb + i) * K;
+    for (int k = 0; k < K; ++k) out[k] = zk(k) - lse;
+}
+
+// ---------------------------------------------------------------------------
+// drift: D_{h,i} = sum_k p (l - l'), D_i = mean_h, per-cluster score
+// One workgroup per window; every sum in a fixed order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_drift_kl(const float* __restrict__ cur, const float* __restrict__ prev,
+                                                   int kind, float* __restrict__ D_hi, float* __restrict__ D_i,
+                                                   float* __restrict__ score, int Hq, int Nb, int K)
+{
+    extern __shared__ float dsh[];  // Hq * Nb drift values
+    const int w = blockIdx.x, lane = lane_id(), wave = threadIdx.x >> 6;
+    const size_t base = (size_t)w * Hq * Nb * K;
+    for (int pr = wave; pr < Hq * Nb; pr += 4) {
+        const float* lc = cur + base + (size_t)pr * K;
+        const float* lp = prev + base + (size_t)pr * K;
+        float part = 0.0f;
+        for (int k = lane; k < K; k += 64) {
+            const float l = lc[k];
+            part += expf(l) * (l - lp[k]);
+        }
+        const float D = wave_sum(part);
+        if (lane == 0) {
+            dsh[pr] = D;
+            if (D_hi) D_hi[(size_t)w * Hq * Nb + pr] = D;
+        }
+    }
+    __syncthreads();
+    const float invH = 1.0f / (float)Hq;
+    for (int i = threadIdx.x; i < Nb; i += 256) {
+        float s = 0.0f;
+        for (int h = 0; h < Hq; ++h) s += dsh[h * Nb + i];
+        D_i[(size_t)w * Nb + i] = s * invH;
+    }
+    for (int k = threadIdx.x; k < K; k += 256) {
+        float s = 0.0f;
+        for (int pr = 0; pr < Hq * Nb; ++pr) {
+            const float l = cur[base + (size_t)pr * K + k];
+            const float p = expf(l);
+            float t;
+            if (kind == PS_SCORE_ATTN_WEIGHTED) t = p * dsh[pr];
+            else {
+                t = p * (l - prev[base + (size_t)pr * K + k]);
+                if (kind == PS_SCORE_KL_SHARE_ABS) t = fabsf(t);
+            }
+            s += t;
+        }
+        score[(size_t)w * K + k] = s * invH;
+    }
+}
+
+__global__ void k_zero(float* __restrict__ p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// top-k: wave-level radix select on order-preserving 32-bit keys, one wave
+// per window.  key(s): larger is better; NaN -> 0 (after every number);
+// -0 -> +0.  Four 8-bit digit passes find the k-th largest key T; the result
+// is every key > T plus the lowest-index keys == T, sorted by (key desc,
+// index asc).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    if (f != f) return 0u;
+    if (f == 0.0f) f = 0.0f;
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(64) void k_topk(const float* __restrict__ score, int K, int k,
+                                              int32_t* __restrict__ idx, float* __restrict__ val)
+{
+    __shared__ uint32_t keys[kMaxK];
+    __shared__ int hist[256];
+    __shared__ uint64_t sel[kMaxTopK];
+    const int w = blockIdx.x, lane = lane_id();
+    const float* sw = score + (size_t)w * K;
+    for (int c = lane; c < K; c += 64) keys[c] = order_key(sw[c]);
+    uint32_t prefix = 0, pmask = 0;
+    int kr = k;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int b = lane; b < 256; b += 64) hist[b] = 0;
+        __syncthreads();
+        for (int c = lane; c < K; c += 64) {
+            const uint32_t key = keys[c];
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        // lane l owns bins 4l..4l+3; suffix sums over lanes from the top
+        int hb[4], own = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) { hb[t] = hist[4 * lane + t]; own += hb[t]; }
+        int suf = own;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+        for (int s = 1; s < 64; s <<= 1) {
+            const int o = __shfl_down(suf, s, 64);
+            if (lane + s < 64) suf += o;
+        }
+        int cum = suf - own;  // count in bins above this lane's
+        int found = -1, newkr = 0;
+#pragma unroll
+        for (int t = 3; t >= 0; --t) {
+            if (found < 0 && cum < kr && cum + hb[t] >= kr) { found = 4 * lane + t; newkr = kr - cum; }
+            cum += hb[t];
+        }
+        const uint64_t fb = __ballot(found >= 0);
+        const int src = __ffsll((unsigned long long)fb) - 1;
+        const int digit = __shfl(found, src, 64);
+        kr = __shfl(newkr, src, 64);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 255u << shift;
+        __syncthreads();
+    }
+    // collect: keys > T, then the first kr keys == T in ascending index
+    const uint32_t T = prefix;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int ngt = 0, neq = 0;
+    const int want_gt = k - kr;
+    for (int base = 0; base < K; base += 64) {
+        const int c = base + lane;
+        const uint32_t key = c < K ? keys[c] : 0u;
+        const bool gt = c < K && key > T;
+        const bool eq = c < K && key == T;
+        const uint64_t mg = __ballot(gt), me = __ballot(eq);
+        const uint64_t comp = ((uint64_t)key << 32) | (uint32_t)(0xffffffffu - (uint32_t)c);
+        if (gt) {
+            const int r = ngt + __popcll(mg & lt);
+            if (r < want_gt) sel[r] = comp;
+        }
+        if (eq) {
+            const int r = neq + __popcll(me & lt);
+            if (r < kr) sel[want_gt + r] = comp;
+        }
+        ngt += __popcll(mg);
+        neq += __popcll(me);
+    }
+    __syncthreads();
+    if (lane < k) {
+        const uint64_t mine = sel[lane];
+        int rank = 0;
+        for (int t = 0; t < k; ++t) rank += sel[t] > mine;
+        const int c = (int)(0xffffffffu - (uint32_t)(mine & 0xffffffffu));
+        idx[(size_t)w * k + rank] = c;
+        if (val) val[(size_t)w * k + rank] = sw[c];
+    }
+}
+
+template <int KB, int NBQ>
+void launch_proxy(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, hipStream_t st)
+{
+    PS_LAUNCH("k_proxy_bf16<KB, NBQ>", (k_proxy_bf16<KB, NBQ>), dim3(s->W), dim3(256), 0, st, (const uint16_t*)Q,
+                       (const uint16_t*)Ck, sigma, logp, s->Hq, s->Hkv, s->dh, s->Nb, s->K);
+}
+
+template <int KB>
+void launch_proxy_nb(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, hipStream_t st)
+{
+    const int nbq = (s->Nb + 15) / 16;
+    if (nbq <= 1)      launch_proxy<KB, 1>(s, Q, Ck, sigma, logp, st);
+    else if (nbq <= 2) launch_proxy<KB, 2>(s, Q, Ck, sigma, logp, st);
+    else               launch_proxy<KB, 4>(s, Q, Ck, sigma, logp, st);
+}
+
+ps_status check_drift_shape(const ps_shape* s)
+{
+    if (!s) return PS_ERR_NULL;
+    if (s->W < 0 || s->Hq < 1 || s->Nb < 1 || s->K < 1 || s->K > kMaxK) return PS_ERR_SHAPE;
+    if ((int64_t)s->Hq * s->Nb > 16384) return PS_ERR_SHAPE;
+    return PS_OK;
+}
+
+ps_status enqueue_drift(const ps_shape* s, const float* cur, const float* prev, ps_score kind, float* D_hi,
+                        float* D_i, float* score, hipStream_t st)
+{
+    const size_t shm = (size_t)s->Hq * s->Nb * sizeof(float);
+    PS_LAUNCH("k_drift_kl", k_drift_kl, dim3(s->W), dim3(256), shm, st, cur, prev, (int)kind, D_hi, D_i, score,
+                       s->Hq, s->Nb, s->K);
+    return PS_OK;
+}
+
+void enqueue_zero(float* p, size_t n, hipStream_t st)
+{
+    if (!p || n == 0) return;
+    const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+    PS_LAUNCH("k_zero", k_zero, dim3(blocks), dim3(256), 0, st, p, n);
+}
+
+}  // namespace
+
+extern "C" ps_status ps_drift_kl(const ps_shape* s, const float* logp_cur, const float* logp_prev,
+                                 ps_score kind, float* D_hi, float* D_i, float* score, void* stream)
+{
+    using namespace ps_host;
+    if (!s || !logp_cur || !logp_prev || !D_i || !score) return PS_ERR_NULL;
+    ps_status st = check_drift_shape(s);
+    if (st != PS_OK) return st;
+    if (kind < PS_SCORE_KL_SHARE || kind > PS_SCORE_ATTN_WEIGHTED) return PS_ERR_RANGE;
+    if (!aligned16(logp_cur) || !aligned16(logp_prev) || !aligned16(D_i) || !aligned16(score) ||
+        (D_hi && !aligned16(D_hi)))
+        return PS_ERR_ALIGN;
+    if (s->W == 0) return PS_OK;
+    hipStream_t stm = (hipStream_t)stream;
+    (void)hipGetLastError();
+    enqueue_drift(s, logp_cur, logp_prev, kind, D_hi, D_i, score, stm);
+    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
+}
+
+extern "C" ps_status ps_proxy_attn(const ps_shape* s, ps_dtype dtype, const void* Q, const void* Ck,
+                                   float softmax_scale, float* logp_cur, const float* logp_prev,
+                                   ps_score kind, float* D_hi, float* D_i, float* score, void* stream)
+{
+    using namespace ps_host;
+    if (!s || !Q || !Ck || !logp_cur || !D_i || !score) return PS_ERR_NULL;
+    if (!dtype_ok(dtype)) return PS_ERR_DTYPE;
+    ps_status st = check_drift_shape(s);
+    if (st != PS_OK) return st;
+    if (s->Hkv < 1 || s->Hq % s->Hkv != 0 || s->dh < 8 || s->dh % 8 != 0) return PS_ERR_SHAPE;
+    if (s->Nb > 64) return PS_ERR_SHAPE;
+    if (kind < PS_SCORE_KL_SHARE || kind > PS_SCORE_ATTN_WEIGHTED) return PS_ERR_RANGE;
+    if (logp_prev == logp_cur) return PS_ERR_RANGE;
+    if (!aligned16(Q) || !aligned16(Ck) || !aligned16(logp_cur) || !aligned16(D_i) || !aligned16(score) ||
+        (logp_prev && !aligned16(logp_prev)) || (D_hi && !aligned16(D_hi)))
+        return PS_ERR_ALIGN;
+    if (s->W == 0) return PS_OK;
+    hipStream_t stm = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (dtype == PS_BF16) {
+        const int kb = (s->K + 15) / 16;
+        if (kb <= 1)       launch_proxy_nb<1>(s, Q, Ck, softmax_scale, logp_cur, stm);
+        else if (kb <= 2)  launch_proxy_nb<2>(s, Q, Ck, softmax_scale, logp_cur, stm);
+        else if (kb <= 4)  launch_proxy_nb<4>(s, Q, Ck, softmax_scale, logp_cur, stm);
+        else if (kb <= 8)  launch_proxy_nb<8>(s, Q, Ck, softmax_scale, logp_cur, stm);
+        else if (kb <= 16) launch_proxy_nb<16>(s, Q, Ck, softmax_scale, logp_cur, stm);
+        else return PS_ERR_SHAPE;
+    } else {
+        const int pairs = s->Hq * s->Nb;
+        PS_LAUNCH("k_proxy_f32", k_proxy_f32, dim3((pairs + 255) / 256, s->W), dim3(256), 0, stm, (const float*)Q,
+                           (const float*)Ck, softmax_scale, logp_cur, s->Hq, s->Hkv, s->dh, s->Nb, s->K);
+    }
+    if (logp_prev) {
+        enqueue_drift(s, logp_cur, logp_prev, kind, D_hi, D_i, score, stm);
+    } else {
+        enqueue_zero(D_i, (size_t)s->W * s->Nb, stm);
+        enqueue_zero(score, (size_t)s->W * s->K, stm);
+        enqueue_zero(D_hi, (size_t)s->W * s->Hq * s->Nb, stm);
+    }
+    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
+}
+
+extern "C" ps_status ps_topk_clusters(const ps_shape* s, const float* score, int32_t k, int32_t* idx, float* val,
+                                      void* stream)
+{
+    using namespace ps_host;
+    if (!s || !score || !idx) return PS_ERR_NULL;
+    if (s->W < 0 || s->K < 1 || s->K > kMaxK) return PS_ERR_SHAPE;
+    if (k < 1 || k > s->K || k > kMaxTopK) return PS_ERR_RANGE;
+    if (!aligned16(score) || !aligned16(idx) || (val && !aligned16(val))) return PS_ERR_ALIGN;
+    if (s->W == 0) return PS_OK;
+    hipStream_t stm = (hipStream_t)stream;
+    (void)hipGetLastError();
+    PS_LAUNCH("k_topk", k_topk, dim3(s->W), dim3(64), 0, stm, score, s->K, k, idx, val);
+    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
+}
+
+extern "C" const char* ps_status_string(ps_status st)
+{
+    switch (st) {
+    case PS_OK: return "PS_OK";
+    case PS_ERR_NULL: return "PS_ERR_NULL: a required pointer is NULL";
+    case PS_ERR_SHAPE: return "PS_ERR_SHAPE: a dimension is outside the supported limits";
+    case PS_ERR_DTYPE: return "PS_ERR_DTYPE: unsupported element type";
+    case PS_ERR_ALIGN: return "PS_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case PS_ERR_RANGE: return "PS_ERR_RANGE: a scalar argument is out of range";
+    case PS_ERR_WORKSPACE: return "PS_ERR_WORKSPACE: workspace missing or too small";
+    case PS_ERR_DEVICE: return "PS_ERR_DEVICE: a HIP launch or runtime call failed";
+    }
+    return "unknown ps_status";
+}

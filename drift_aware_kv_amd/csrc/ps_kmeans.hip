@@ -1,0 +1,665 @@
+// ps_kmeans.hip -- spherical K-Means of the local window's hidden states and
+// the centroid keys (Polestar technical summary 2.A, local window and
+// clustering; sparse updates), for gfx950.
+//
+// One Lloyd iteration over all W windows is three launches:
+//   assign  bf16 MFMA (16x16x32) scores of 128-row tiles against every centre,
+//           argmax in registers; the first iteration also writes the fp64
+//           row norms.  Centres are staged through LDS in 64-wide d-chunks.
+//   bucket  stable counting sort of each window's rows by cluster (wave
+//           ballots), giving every cluster its ascending member list.
+//   update  one workgroup per (window, cluster): fp64 fused multiply-add of
+//           the member rows scaled by 1/n_j in ascending order, fp64 norm,
+//           fp32 centre plus its bf16 copy for the next assignment.
+// After the last iteration the keys kernel averages the member key rows.
+#include "ps_common.h"
+
+#include <math.h>
+
+using namespace ps;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// seeding
+// ---------------------------------------------------------------------------
+
+// c_k = x_{floor(kN/K)} = h / n (fp32 division), n from an fp64 sum of squares
+template <typename T>
+__global__ __launch_bounds__(256) void k_init_strided(const T* __restrict__ H, float* __restrict__ C,
+                                                       int N, int d, int K)
+{
+    const int w = blockIdx.y, k = blockIdx.x;
+    const int j = (int)(((int64_t)k * N) / K);
+    const T* h = H + ((size_t)w * N + j) * d;
+    __shared__ double red[4];
+    double ss = 0.0;
+    for (int e = threadIdx.x; e < d; e += 256) {
+        double v = (double)Elem<T>::get(h, e);
+        ss = fma(v, v, ss);
+    }
+    ss = wave_sum_d(ss);
+    if (lane_id() == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float n = (float)sqrt(red[0] + red[1] + red[2] + red[3]);
+    float* c = C + ((size_t)w * K + k) * d;
+    for (int e = threadIdx.x; e < d; e += 256) {
+        float v = Elem<T>::get(h, e);
+        c[e] = n > 0.0f ? v / n : 0.0f;
+    }
+}
+
+// Farthest-first traversal under cosine similarity, one workgroup per window:
+// c_0 = x_0; then the non-zero row least similar to all chosen centres.
+// m (the running best similarity) and the norms live in the workspace.
+template <typename T>
+__global__ __launch_bounds__(256) void k_init_farthest(const T* __restrict__ H, float* __restrict__ C,
+                                                        double* __restrict__ mbuf,
+                                                        float* __restrict__ nbuf, int N, int d, int K)
+{
+    extern __shared__ float cdyn[];  // the current centre, d floats
+    __shared__ double redv[4];
+    __shared__ int redi[4];
+    const int w = blockIdx.x, wave = threadIdx.x >> 6, lane = lane_id();
+    const T* Hw = H + (size_t)w * N * d;
+    double* m = mbuf + (size_t)w * N;
+    float* nrm = nbuf + (size_t)w * N;
+    for (int j = wave; j < N; j += 4) {
+        double ss = 0.0;
+        for (int e = lane; e < d; e += 64) {
+            double v = (double)Elem<T>::get(Hw, (size_t)j * d + e);
+            ss = fma(v, v, ss);
+        }
+        ss = wave_sum_d(ss);
+        if (lane == 0) nrm[j] = (float)sqrt(ss);
+    }
+    __threadfence_block();
+    __syncthreads();
+    int seed = 0;
+    for (int k = 0; k < K; ++k) {
+        if (k > 0) {
+            double bv = 0.0;
+            int bi = -1;
+            for (int j = threadIdx.x; j < N; j += 256) {
+                if (!(nrm[j] > 0.0f)) continue;
+                if (bi < 0 || m[j] < bv) { bv = m[j]; bi = j; }
+            }
+#pragma unroll
+            for (int s = 32; s >= 1; s >>= 1) {
+                double ov = __shfl_xor(bv, s, 64);
+                int oi = __shfl_xor(bi, s, 64);
+                if (oi >= 0 && (bi < 0 || ov < bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+            }
+            if (lane == 0) { redv[wave] = bv; redi[wave] = bi; }
+            __syncthreads();
+            bv = redv[0];
+            bi = redi[0];
+            for (int q = 1; q < 4; ++q) {
+                int oi = redi[q];
+                double ov = redv[q];
+                if (oi >= 0 && (bi < 0 || ov < bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+            }
+            seed = bi < 0 ? 0 : bi;
+            __syncthreads();
+        }
+        const float ns = nrm[seed];
+        for (int e = threadIdx.x; e < d; e += 256) {
+            float v = Elem<T>::get(Hw, (size_t)seed * d + e);
+            float x = ns > 0.0f ? v / ns : 0.0f;
+            cdyn[e] = x;
+            C[((size_t)w * K + k) * d + e] = x;
+        }
+        __syncthreads();
+        for (int j = wave; j < N; j += 4) {
+            const float nj = nrm[j];
+            double dot = 0.0;
+            for (int e = lane; e < d; e += 64) {
+                float v = Elem<T>::get(Hw, (size_t)j * d + e);
+                float x = nj > 0.0f ? v / nj : 0.0f;
+                dot = fma((double)x, (double)cdyn[e], dot);
+            }
+            dot = wave_sum_d(dot);
+            if (lane == 0 && (k == 0 || dot > m[j])) m[j] = dot;
+        }
+        __threadfence_block();
+        __syncthreads();
+    }
+}
+
+// bf16 copy of the centres: the operand of the assignment step
+__global__ __launch_bounds__(256) void k_centres_to_bf16(const float* __restrict__ C,
+                                                          uint16_t* __restrict__ Cb, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        Cb[i] = (uint16_t)f32_to_bf16(C[i]);
+}
+
+// ---------------------------------------------------------------------------
+// assignment, bf16: scores D[cluster][token] = Cb . H^T on MFMA 16x16x32
+// ---------------------------------------------------------------------------
+// Workgroup = 4 waves = 128 tokens of one window; wave = 32 tokens (two
+// 16-token N-blocks); the M dimension runs over up to 16*KB clusters per pass
+// (more passes when K > 16*KB).  MFMA operand layout (16x16x32 bf16): lane l
+// supplies row/column (l % 16) and reduction elements 8*(l/16)..+8; the
+// result element r of lane l is D[4*(l/16) + r][l % 16].
+template <int KB>
+__global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict__ H,
+                                                      const uint16_t* __restrict__ Cb,
+                                                      int32_t* __restrict__ assign,
+                                                      float* __restrict__ row_norm, int N, int d,
+                                                      int K, int tiles, int nblocks, int want_norm)
+{
+    constexpr int DK = 64;                 // d elements per LDS stage
+    constexpr int ROWB = DK * 2 + 16;      // padded LDS row stride (bytes): conflict-free reads
+    constexpr int MROWS = 16 * KB;
+    constexpr int NPIECE = MROWS * (DK / 8);        // 16-byte pieces per stage
+    constexpr int PIECES = (NPIECE + 255) / 256;      // per thread
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][MROWS * ROWB];
+
+    const int L = xcd_remap(blockIdx.x, nblocks);
+    const int w = L / tiles, tile = L - w * tiles;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const uint16_t* Hw = H + (size_t)w * N * d;
+    const uint16_t* Cw = Cb + (size_t)w * K * d;
+
+    int tok[2];
+    bool tv[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        tok[nb] = tile * 128 + wave * 32 + nb * 16 + r16;
+        tv[nb] = tok[nb] < N;
+    }
+    float bestv[2] = {-INFINITY, -INFINITY};
+    int besti[2] = {0, 0};
+    double ss[2] = {0.0, 0.0};
+    const int nchunks = (d + DK - 1) / DK;
+
+    for (int cg = 0; cg < K; cg += MROWS) {
+        const bool norm_pass = want_norm && cg == 0;
+        floatx4 acc[KB][2];
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+        uint4 cpre[PIECES];
+        uint4 hcur[2][2], hnext[2][2];
+        auto load_c = [&](int c0) {
+#pragma unroll
+            for (int p = 0; p < PIECES; ++p) {
+                const int piece = p * 256 + threadIdx.x;
+                const int row = piece >> 3, col = (piece & 7) * 8;
+                const int cl = cg + row, e = c0 + col;
+                cpre[p] = (piece < NPIECE && cl < K && e < d)
+                              ? *reinterpret_cast<const uint4*>(Cw + (size_t)cl * d + e)
+                              : make_uint4(0, 0, 0, 0);
+            }
+        };
+        auto store_c = [&](int buf) {
+#pragma unroll
+            for (int p = 0; p < PIECES; ++p) {
+                const int piece = p * 256 + threadIdx.x;
+                const int row = piece >> 3, col = (piece & 7) * 8;
+                if (piece < NPIECE) *reinterpret_cast<uint4*>(&lds[buf][row * ROWB + col * 2]) = cpre[p];
+            }
+        };
+        auto load_h = [&](int c0, uint4 (&hr)[2][2]) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int e = c0 + 32 * s + 8 * q;
+                    hr[nb][s] = (tv[nb] && e < d)
+                                    ? *reinterpret_cast<const uint4*>(Hw + (size_t)tok[nb] * d + e)
+                                    : make_uint4(0, 0, 0, 0);
+                }
+        };
+
+        load_c(0);
+        load_h(0, hcur);
+        store_c(0);
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            const bool more = c + 1 < nchunks;
+            if (more) {
+                load_c((c + 1) * DK);
+                load_h((c + 1) * DK, hnext);
+            }
+            const uint8_t* buf = lds[c & 1];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const uint4 hv = hcur[nb][s];
+                    if (norm_pass) {
+                        const uint32_t wv[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const double lo = (double)__uint_as_float(wv[i] << 16);
+                            const double hi = (double)__uint_as_float(wv[i] & 0xffff0000u);
+                            ss[nb] = fma(lo, lo, ss[nb]);
+                            ss[nb] = fma(hi, hi, ss[nb]);
+                        }
+                    }
+                    const bf16x8 b = __builtin_bit_cast(bf16x8, hv);
+#pragma unroll
+                    for (int mb = 0; mb < KB; ++mb) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                            buf + (16 * mb + r16) * ROWB + 64 * s + 16 * q);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mb][nb], 0, 0, 0);
+                    }
+                }
+            }
+            if (more) store_c((c + 1) & 1);
+            __syncthreads();
+            if (more) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) hcur[nb][s] = hnext[nb][s];
+            }
+        }
+        // merge this cluster group's scores into the running argmax (ascending
+        // cluster order within a lane; strict > keeps the lowest index)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int cl = cg + 16 * mb + 4 * q + r;
+                    const float v = acc[mb][nb][r];
+                    if (cl < K && v > bestv[nb]) { bestv[nb] = v; besti[nb] = cl; }
+                }
+    }
+    // combine the four lanes (q = 0..3) that hold the same token
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int m = 16; m <= 32; m <<= 1) {
+            const float ov = __shfl_xor(bestv[nb], m, 64);
+            const int oi = __shfl_xor(besti[nb], m, 64);
+            if (ov > bestv[nb] || (ov == bestv[nb] && oi < besti[nb])) { bestv[nb] = ov; besti[nb] = oi; }
+            if (want_norm) ss[nb] += shfl_xor_d(ss[nb], m);
+        }
+        if (q == 0 && tv[nb]) {
+            assign[(size_t)w * N + tok[nb]] = besti[nb];
+            if (want_norm) row_norm[(size_t)w * N + tok[nb]] = (float)sqrt(ss[nb]);
+        }
+    }
+}
+
+// assignment, fp32 path (exact centres): one thread per row
+__global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ H, const float* __restrict__ C,
+                                                     int32_t* __restrict__ assign,
+                                                     float* __restrict__ row_norm, int W, int N, int d,
+                                                     int K, int want_norm)
+{
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= (int64_t)W * N) return;
+    const int w = (int)(row / N);
+    const float* h = H + (size_t)row * d;
+    const float* Cw = C + (size_t)w * K * d;
+    float bestv = -INFINITY;
+    int besti = 0;
+    for (int k = 0; k < K; ++k) {
+        float s = 0.0f;
+        for (int e = 0; e < d; ++e) s = fmaf(h[e], Cw[(size_t)k * d + e], s);
+        if (s > bestv) { bestv = s; besti = k; }
+    }
+    assign[row] = besti;
+    if (want_norm) {
+        double ss = 0.0;
+        for (int e = 0; e < d; ++e) ss = fma((double)h[e], (double)h[e], ss);
+        row_norm[row] = (float)sqrt(ss);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bucket: stable counting sort of rows by cluster, one wave per window
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_bucket(const int32_t* __restrict__ assign, int32_t* __restrict__ perm,
+                                                int32_t* __restrict__ offs, int N, int K)
+{
+    __shared__ int cur[kMaxK];
+    const int w = blockIdx.x, lane = lane_id();
+    const int32_t* a = assign + (size_t)w * N;
+    for (int k = lane; k < K; k += 64) cur[k] = 0;
+    __syncthreads();
+    for (int j = lane; j < N; j += 64) {
+        int c = a[j];
+        c = (c < 0 || c >= K) ? 0 : c;
+        atomicAdd(&cur[c], 1);
+    }
+    __syncthreads();
+    int running = 0;
+    for (int base = 0; base < K; base += 64) {
+        const int k = base + lane;
+        const int v = k < K ? cur[k] : 0;
+        int incl = v;
+#pragma unroll
+        for (int s = 1; s < 64; s <<= 1) {
+            const int o = __shfl_up(incl, s, 64);
+            if (lane >= s) incl += o;
+        }
+        const int excl = running + incl - v;
+        if (k < K) {
+            offs[(size_t)w * (K + 1) + k] = excl;
+            cur[k] = excl;
+        }
+        running += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) offs[(size_t)w * (K + 1) + K] = running;
+    __syncthreads();
+    const int nbits = K > 1 ? 32 - __clz(K - 1) : 0;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < N; base += 64) {
+        const int j = base + lane;
+        const bool valid = j < N;
+        int c = valid ? a[j] : 0;
+        c = (c < 0 || c >= K) ? 0 : c;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t bb = __ballot(valid && ((c >> b) & 1));
+            peers &= ((c >> b) & 1) ? bb : ~bb;
+        }
+        int rank = 0, total = 0, start = 0;
+        if (valid) {
+            rank = __popcll(peers & lt);
+            total = __popcll(peers);
+            start = cur[c];
+        }
+        __syncthreads();
+        if (valid) {
+            perm[(size_t)w * N + start + rank] = j;
+            if (rank == total - 1) cur[c] = start + total;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// update: one workgroup per (window, cluster)
+// ---------------------------------------------------------------------------
+template <typename T, int CH>
+__global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const float* __restrict__ row_norm,
+                                                 const int32_t* __restrict__ perm,
+                                                 const int32_t* __restrict__ offs, float* __restrict__ C,
+                                                 uint16_t* __restrict__ Cb, int32_t* __restrict__ counts,
+                                                 double* __restrict__ nrm_out, int N, int d, int K,
+                                                 int nblocks)
+{
+    __shared__ double red[4];
+    const int Lg = xcd_remap(blockIdx.x, nblocks);
+    const int w = Lg / K, k = Lg - w * K;
+    const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
+    const int32_t* pm = perm + (size_t)w * N;
+    const T* Hw = H + (size_t)w * N * d;
+    const float* rn = row_norm + (size_t)w * N;
+
+    double acc[CH][8];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[c][i] = 0.0;
+
+    int m = beg;
+    for (; m + 2 <= end; m += 2) {
+        const int j0 = pm[m], j1 = pm[m + 1];
+        const float n0 = rn[j0], n1 = rn[j1];
+        float v0[CH][8], v1[CH][8];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int e = (threadIdx.x + 256 * c) * 8;
+            if (e < d) {
+                load8(Hw + (size_t)j0 * d + e, v0[c]);
+                load8(Hw + (size_t)j1 * d + e, v1[c]);
+            }
+        }
+        if (n0 > 0.0f) {
+            const double inv = 1.0 / (double)n0;
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[c][i] = fma((double)v0[c][i], inv, acc[c][i]);
+        }
+        if (n1 > 0.0f) {
+            const double inv = 1.0 / (double)n1;
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[c][i] = fma((double)v1[c][i], inv, acc[c][i]);
+        }
+    }
+    for (; m < end; ++m) {
+        const int j0 = pm[m];
+        const float n0 = rn[j0];
+        if (!(n0 > 0.0f)) continue;
+        const double inv = 1.0 / (double)n0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int e = (threadIdx.x + 256 * c) * 8;
+            if (e < d) {
+                float v0[8];
+                load8(Hw + (size_t)j0 * d + e, v0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[c][i] = fma((double)v0[i], inv, acc[c][i]);
+            }
+        }
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fma(acc[c][i], acc[c][i], ss);
+    ss = wave_sum_d(ss);
+    if (lane_id() == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const double nrm = sqrt(red[0] + red[1] + red[2] + red[3]);
+    const int nk = end - beg;
+    if (threadIdx.x == 0) {
+        counts[(size_t)w * K + k] = nk;
+        nrm_out[(size_t)w * K + k] = nrm;
+    }
+    if (nk > 0 && nrm > 0.0) {
+        float* c_out = C + ((size_t)w * K + k) * d;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int e = (threadIdx.x + 256 * c) * 8;
+            if (e < d) {
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = (float)(acc[c][i] / nrm);
+                store8(c_out + e, v);
+                if (Cb) store8(Cb + ((size_t)w * K + k) * d + e, v);
+            }
+        }
+    }
+}
+
+// centroid keys: mean of the member key rows, fp64, rounded to fp32 then dtype
+template <typename T>
+__global__ __launch_bounds__(256) void k_keys(const T* __restrict__ Kr, const int32_t* __restrict__ perm,
+                                               const int32_t* __restrict__ offs, T* __restrict__ Ck,
+                                               int N, int KV, int K, int nblocks)
+{
+    const int Lg = xcd_remap(blockIdx.x, nblocks);
+    const int w = Lg / K, k = Lg - w * K;
+    const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
+    if (end == beg) return;
+    const int32_t* pm = perm + (size_t)w * N;
+    const T* Kw = Kr + (size_t)w * N * KV;
+    for (int e = threadIdx.x * 8; e < KV; e += 256 * 8) {
+        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int m = beg; m < end; ++m) {
+            float v[8];
+            load8(Kw + (size_t)pm[m] * KV + e, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += (double)v[i];
+        }
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (float)(acc[i] / (double)(end - beg));
+        store8(Ck + ((size_t)w * K + k) * KV + e, o);
+    }
+}
+
+__global__ void k_objective(const double* __restrict__ nrm, double* __restrict__ obj, int W, int K)
+{
+    const int w = blockIdx.x * blockDim.x + threadIdx.x;
+    if (w >= W) return;
+    double s = 0.0;
+    for (int k = 0; k < K; ++k) s += nrm[(size_t)w * K + k];
+    obj[w] = s;
+}
+
+// workspace layout
+struct KmWs {
+    uint16_t* Cb;
+    int32_t* perm;
+    int32_t* offs;
+    double* nrm;
+    double* fm;
+    float* fn;
+    size_t bytes;
+};
+
+KmWs km_layout(const ps_shape* s, int dtype, void* base)
+{
+    using ps_host::round256;
+    const size_t W = (size_t)s->W, N = (size_t)s->N, K = (size_t)s->K, d = (size_t)s->d;
+    size_t off = 0;
+    KmWs L{};
+    char* b = (char*)base;
+    auto take = [&](size_t bytes) {
+        char* p = b ? b + off : nullptr;
+        off += round256(bytes);
+        return p;
+    };
+    L.Cb = dtype == PS_BF16 ? (uint16_t*)take(W * K * d * 2) : nullptr;
+    L.perm = (int32_t*)take(W * N * 4);
+    L.offs = (int32_t*)take(W * (K + 1) * 4);
+    L.nrm = (double*)take(W * K * 8);
+    L.fm = (double*)take(W * N * 8);
+    L.fn = (float*)take(W * N * 4);
+    L.bytes = off;
+    return L;
+}
+
+template <typename T, int CH>
+void launch_update(const ps_shape* s, const void* H, const float* rn, const KmWs& ws, float* C,
+                   int32_t* counts, hipStream_t st)
+{
+    const int nblocks = s->W * s->K;
+    PS_LAUNCH("k_update<T, CH>", (k_update<T, CH>), dim3(nblocks), dim3(256), 0, st, (const T*)H, rn, ws.perm,
+                       ws.offs, C, ws.Cb, counts, ws.nrm, s->N, s->d, s->K, nblocks);
+}
+
+template <int KB>
+void launch_assign_bf16(const ps_shape* s, const void* H, const KmWs& ws, int32_t* assign, float* rn,
+                        int want_norm, hipStream_t st)
+{
+    const int tiles = (s->N + 127) / 128;
+    const int nblocks = s->W * tiles;
+    PS_LAUNCH("k_assign_bf16<KB>", (k_assign_bf16<KB>), dim3(nblocks), dim3(256), 0, st, (const uint16_t*)H, ws.Cb,
+                       assign, rn, s->N, s->d, s->K, tiles, nblocks, want_norm);
+}
+
+}  // namespace
+
+extern "C" ps_status ps_workspace_size(const ps_shape* s, ps_dtype dtype, size_t* bytes)
+{
+    if (!s || !bytes) return PS_ERR_NULL;
+    if (!ps_host::dtype_ok(dtype)) return PS_ERR_DTYPE;
+    ps_status st = ps_host::check_clusters(s);
+    if (st != PS_OK) return st;
+    *bytes = km_layout(s, dtype, nullptr).bytes;
+    return PS_OK;
+}
+
+extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void* H, const void* Kr,
+                                   ps_init init, int32_t iters, float* C, int32_t* assign,
+                                   int32_t* counts, float* row_norm, void* Ck, double* objective,
+                                   void* ws, size_t ws_bytes, void* stream)
+{
+    using namespace ps_host;
+    if (!s || !H || !C || !assign || !counts || !row_norm) return PS_ERR_NULL;
+    if ((Kr == nullptr) != (Ck == nullptr)) return PS_ERR_NULL;
+    if (!dtype_ok(dtype)) return PS_ERR_DTYPE;
+    ps_status st = check_clusters(s);
+    if (st != PS_OK) return st;
+    if (Kr && (st = check_heads(s)) != PS_OK) return st;
+    if (iters < 1) return PS_ERR_RANGE;
+    if (init != PS_INIT_GIVEN && init != PS_INIT_STRIDED && init != PS_INIT_FARTHEST) return PS_ERR_RANGE;
+    if (s->d > 8192) return PS_ERR_SHAPE;  // update kernel: at most 4 chunks of 2048 per thread
+    if (!aligned16(H) || !aligned16(C) || !aligned16(assign) || !aligned16(counts) ||
+        !aligned16(row_norm) || (Kr && (!aligned16(Kr) || !aligned16(Ck))) ||
+        (objective && !aligned16(objective)))
+        return PS_ERR_ALIGN;
+    const KmWs need = km_layout(s, dtype, nullptr);
+    if (!ws || ws_bytes < need.bytes) return PS_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PS_ERR_ALIGN;
+    if (s->W == 0) return PS_OK;
+
+    hipStream_t stm = (hipStream_t)stream;
+    (void)hipGetLastError();
+    const KmWs L = km_layout(s, dtype, ws);
+    const int W = s->W, N = s->N, d = s->d, K = s->K;
+    const bool bf = dtype == PS_BF16;
+
+    if (init == PS_INIT_STRIDED) {
+        if (bf) PS_LAUNCH("k_init_strided<uint16_t>", k_init_strided<uint16_t>, dim3(K, W), dim3(256), 0, stm, (const uint16_t*)H, C, N, d, K);
+        else    PS_LAUNCH("k_init_strided<float>", k_init_strided<float>, dim3(K, W), dim3(256), 0, stm, (const float*)H, C, N, d, K);
+    } else if (init == PS_INIT_FARTHEST) {
+        const size_t shm = (size_t)d * sizeof(float);
+        if (bf) PS_LAUNCH("k_init_farthest<uint16_t>", k_init_farthest<uint16_t>, dim3(W), dim3(256), shm, stm, (const uint16_t*)H, C, L.fm, L.fn, N, d, K);
+        else    PS_LAUNCH("k_init_farthest<float>", k_init_farthest<float>, dim3(W), dim3(256), shm, stm, (const float*)H, C, L.fm, L.fn, N, d, K);
+    }
+    if (bf) {
+        const size_t n = (size_t)W * K * d;
+        const int blocks = (int)std::min<size_t>((n + 255) / 256, 65536);
+        PS_LAUNCH("k_centres_to_bf16", k_centres_to_bf16, dim3(blocks), dim3(256), 0, stm, C, L.Cb, n);
+    }
+    const int CH = (d + 2047) / 2048;
+    const int KBn = (K + 15) / 16;
+    for (int it = 0; it < iters; ++it) {
+        const int want_norm = it == 0;
+        if (bf) {
+            if (KBn <= 1)      launch_assign_bf16<1>(s, H, L, assign, row_norm, want_norm, stm);
+            else if (KBn <= 2) launch_assign_bf16<2>(s, H, L, assign, row_norm, want_norm, stm);
+            else if (KBn <= 4) launch_assign_bf16<4>(s, H, L, assign, row_norm, want_norm, stm);
+            else if (KBn <= 8) launch_assign_bf16<8>(s, H, L, assign, row_norm, want_norm, stm);
+            else               launch_assign_bf16<16>(s, H, L, assign, row_norm, want_norm, stm);
+        } else {
+            const int64_t rows = (int64_t)W * N;
+            PS_LAUNCH("k_assign_f32", k_assign_f32, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stm,
+                               (const float*)H, C, assign, row_norm, W, N, d, K, want_norm);
+        }
+        PS_LAUNCH("k_bucket", k_bucket, dim3(W), dim3(64), 0, stm, assign, L.perm, L.offs, N, K);
+        if (bf) {
+            switch (CH) {
+            case 1: launch_update<uint16_t, 1>(s, H, row_norm, L, C, counts, stm); break;
+            case 2: launch_update<uint16_t, 2>(s, H, row_norm, L, C, counts, stm); break;
+            case 3: launch_update<uint16_t, 3>(s, H, row_norm, L, C, counts, stm); break;
+            default: launch_update<uint16_t, 4>(s, H, row_norm, L, C, counts, stm); break;
+            }
+        } else {
+            switch (CH) {
+            case 1: launch_update<float, 1>(s, H, row_norm, L, C, counts, stm); break;
+            case 2: launch_update<float, 2>(s, H, row_norm, L, C, counts, stm); break;
+            case 3: launch_update<float, 3>(s, H, row_norm, L, C, counts, stm); break;
+            default: launch_update<float, 4>(s, H, row_norm, L, C, counts, stm); break;
+            }
+        }
+    }
+    if (Kr) {
+        const int KV = s->Hkv * s->dh;
+        const int nblocks = W * K;
+        if (bf) PS_LAUNCH("k_keys<uint16_t>", k_keys<uint16_t>, dim3(nblocks), dim3(256), 0, stm, (const uint16_t*)Kr, L.perm, L.offs, (uint16_t*)Ck, N, KV, K, nblocks);
+        else    PS_LAUNCH("k_keys<float>", k_keys<float>, dim3(nblocks), dim3(256), 0, stm, (const float*)Kr, L.perm, L.offs, (float*)Ck, N, KV, K, nblocks);
+    }
+    if (objective)
+        PS_LAUNCH("k_objective", k_objective, dim3((W + 63) / 64), dim3(64), 0, stm, L.nrm, objective, W, K);
+    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
+}

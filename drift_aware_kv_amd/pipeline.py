@@ -1,0 +1,119 @@
+"""One denoising step of the drift-detection path over W windows.
+
+``DriftPath`` owns the cross-step state that the C ABI leaves to the caller
+(centres C, centroid keys Ck, the previous step's log-probabilities) plus the
+output buffers, all allocated once with torch on the device, and issues the six
+library calls in the order of one step:
+
+  kmeans_fit -> residual_nvfp4 -> proxy_attn (+ drift) -> topk -> refresh_gather
+
+Step 0 (window formation) seeds the clusters and stores the first proxy
+distribution; there is no previous distribution, so no drift, selection or
+gather happens (Polestar technical summary 2.A, schedule: a refresh follows
+formation).  Later steps warm-start K-Means from the previous centres, so
+cluster k at step t continues cluster k at step t-1 and the KL between the two
+proxy distributions is defined.
+"""
+from dataclasses import dataclass
+
+import torch
+
+from . import (PS_BF16, PS_F32, PS_INIT_FARTHEST, PS_INIT_GIVEN, PS_INIT_STRIDED,
+               PS_SCORE_KL_SHARE, Shape, ps_kmeans_fit, ps_proxy_attn, ps_refresh_gather,
+               ps_residual_nvfp4, ps_topk_clusters, workspace)
+
+
+@dataclass
+class StepSpec:
+    W: int
+    N: int
+    d: int
+    Hq: int
+    Hkv: int
+    dh: int
+    Nb: int
+    K: int
+    k: int
+    iters: int
+    bf16: bool
+    init0: str = "strided"
+    softmax_scale: float = None
+    cap: int = None
+    score_kind: int = PS_SCORE_KL_SHARE
+    gather_rows: bool = True
+
+    @property
+    def shape(self) -> Shape:
+        return Shape(self.W, self.N, self.d, self.Hq, self.Hkv, self.dh, self.Nb, self.K)
+
+
+class DriftPath:
+    def __init__(self, spec: StepSpec, device="cuda"):
+        self.spec = spec
+        self.device = torch.device(device)
+        s = spec.shape
+        self.shape = s
+        self.dtype = PS_BF16 if spec.bf16 else PS_F32
+        et = torch.bfloat16 if spec.bf16 else torch.float32
+        self.cap = spec.N if spec.cap is None else spec.cap
+        self.scale = spec.softmax_scale if spec.softmax_scale is not None else spec.dh ** -0.5
+        dev = self.device
+        f32, i32 = torch.float32, torch.int32
+        self.C = torch.zeros(s.W, s.K, s.d, dtype=f32, device=dev)
+        self.Ck = torch.zeros(s.W, s.K, s.Hkv, s.dh, dtype=et, device=dev)
+        self.assign = torch.zeros(s.W, s.N, dtype=i32, device=dev)
+        self.counts = torch.zeros(s.W, s.K, dtype=i32, device=dev)
+        self.row_norm = torch.zeros(s.W, s.N, dtype=f32, device=dev)
+        self.objective = torch.zeros(s.W, dtype=torch.float64, device=dev)
+        self.ws = workspace(s, self.dtype, dev)
+        self.codes = torch.zeros(s.W, s.N, s.d // 2, dtype=torch.uint8, device=dev)
+        self.bscale = torch.zeros(s.W, s.N, s.d // 16, dtype=torch.uint8, device=dev)
+        self.rscale = torch.zeros(s.W, s.N, dtype=f32, device=dev)
+        self.logp = [torch.zeros(s.W, s.Hq, s.Nb, s.K, dtype=f32, device=dev) for _ in range(2)]
+        self.D_hi = torch.zeros(s.W, s.Hq, s.Nb, dtype=f32, device=dev)
+        self.D_i = torch.zeros(s.W, s.Nb, dtype=f32, device=dev)
+        self.score = torch.zeros(s.W, s.K, dtype=f32, device=dev)
+        self.idx = torch.zeros(s.W, spec.k, dtype=i32, device=dev)
+        self.val = torch.zeros(s.W, spec.k, dtype=f32, device=dev)
+        self.pos = torch.full((s.W, max(self.cap, 1)), -1, dtype=i32, device=dev)
+        self.count = torch.zeros(s.W, dtype=i32, device=dev)
+        if spec.gather_rows and self.cap > 0:
+            self.H_hat = torch.zeros(s.W, self.cap, s.d, dtype=et, device=dev)
+            self.K_out = torch.zeros(s.W, self.cap, s.Hkv, s.dh, dtype=et, device=dev)
+            self.V_out = torch.zeros(s.W, self.cap, s.Hkv, s.dh, dtype=et, device=dev)
+        else:
+            self.H_hat = self.K_out = self.V_out = None
+        self.t = 0
+
+    @property
+    def logp_cur(self):
+        return self.logp[self.t & 1]
+
+    @property
+    def logp_prev(self):
+        return self.logp[(self.t - 1) & 1]
+
+    def step(self, H, Kr, V, Q, stream=None):
+        """Run one step on device tensors H [W][N][d], Kr/V [W][N][Hkv][dh],
+        Q [W][Nb][Hq][dh]; returns t of the step just run."""
+        sp, s, dt = self.spec, self.shape, self.dtype
+        first = self.t == 0
+        init = {"strided": PS_INIT_STRIDED, "farthest": PS_INIT_FARTHEST}[sp.init0] if first \
+            else PS_INIT_GIVEN
+        ps_kmeans_fit(s, dt, H, Kr, init, sp.iters, self.C, self.assign, self.counts, self.row_norm,
+                      self.Ck, self.objective, self.ws, stream)
+        ps_residual_nvfp4(s, dt, H, self.row_norm, self.C, self.assign, self.codes, self.bscale,
+                          self.rscale, stream)
+        ps_proxy_attn(s, dt, Q, self.Ck, self.scale, self.logp_cur, None if first else self.logp_prev,
+                      sp.score_kind, self.D_hi, self.D_i, self.score, stream)
+        if not first:
+            ps_topk_clusters(s, self.score, sp.k, self.idx, self.val, stream)
+            gather = self.K_out is not None
+            ps_refresh_gather(s, dt, self.assign, self.idx, sp.k, self.cap,
+                              self.pos if self.cap > 0 else None, self.count, self.codes,
+                              self.bscale, self.rscale, self.C, self.row_norm, self.H_hat,
+                              Kr if gather else None, V if gather else None, self.K_out,
+                              self.V_out, stream)
+        t = self.t
+        self.t += 1
+        return t

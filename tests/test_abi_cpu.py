@@ -1,0 +1,147 @@
+"""CPU-side checks of the C ABI: the HIP library loads, exports every entry
+point that include/*.h declares, and rejects bad host-known arguments with the
+documented status codes before anything is enqueued (no GPU is touched: every
+case here fails validation, so no kernel launch is attempted)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIBPATH = os.path.join(ROOT, "drift_aware_kv_amd", "libpolestar_drift.so")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, RANGE, WORKSPACE, DEVICE = range(8)
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+char\s*\*|ps_status)\s+(ps_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIBPATH):
+        import drift_aware_kv_amd.build as b
+        b.build()
+    import drift_aware_kv_amd as P
+    return P.lib()
+
+
+def test_header_declares_the_six_calls():
+    names = declared_functions()
+    for n in ("ps_kmeans_fit", "ps_residual_nvfp4", "ps_proxy_attn", "ps_drift_kl",
+              "ps_topk_clusters", "ps_refresh_gather", "ps_status_string", "ps_workspace_size"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(LIBPATH)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(L):
+    import drift_aware_kv_amd as P
+    for st in range(8):
+        assert P.status_string(st).startswith("PS_")
+    assert "unknown" in P.status_string(99)
+
+
+def _shape(**kw):
+    import drift_aware_kv_amd as P
+    base = dict(W=2, N=64, d=32, Hq=4, Hkv=2, dh=16, Nb=8, K=4)
+    base.update(kw)
+    return P._CShape(*[base[k] for k in ("W", "N", "d", "Hq", "Hkv", "dh", "Nb", "K")])
+
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced in these cases
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def test_workspace_size(L):
+    n = ctypes.c_size_t(0)
+    assert L.ps_workspace_size(ctypes.byref(_shape()), 1, ctypes.byref(n)) == OK
+    bf = n.value
+    assert bf >= 2 * 4 * 32 * 2 + 2 * 64 * 4  # bf16 centres + member lists
+    assert L.ps_workspace_size(ctypes.byref(_shape()), 0, ctypes.byref(n)) == OK
+    assert n.value < bf                        # the fp32 path keeps no bf16 copy
+    assert L.ps_workspace_size(ctypes.byref(_shape(K=65)), 1, ctypes.byref(n)) == SHAPE
+    assert L.ps_workspace_size(ctypes.byref(_shape()), 7, ctypes.byref(n)) == DTYPE
+    assert L.ps_workspace_size(None, 1, ctypes.byref(n)) == NULL
+
+
+def _fit(L, shape, dtype=1, init=1, iters=2, H=FAKE, ws=FAKE, ws_bytes=1 << 30, C=FAKE, Kr=None,
+         Ck=None):
+    return L.ps_kmeans_fit(ctypes.byref(shape), dtype, H, Kr, init, iters, C, FAKE, FAKE, FAKE, Ck,
+                           None, ws, ws_bytes, None)
+
+
+def test_kmeans_fit_argument_checks(L):
+    s = _shape()
+    assert _fit(L, s, H=None) == NULL
+    assert _fit(L, s, C=None) == NULL
+    assert _fit(L, s, Kr=FAKE, Ck=None) == NULL           # Kr and Ck come together
+    assert _fit(L, s, dtype=3) == DTYPE
+    assert _fit(L, _shape(d=24)) == SHAPE                   # d % 16
+    assert _fit(L, _shape(K=65)) == SHAPE                   # K > N
+    assert _fit(L, _shape(K=0)) == SHAPE
+    assert _fit(L, _shape(Hq=3, Hkv=2), Kr=FAKE, Ck=FAKE) == SHAPE   # Hq % Hkv
+    assert _fit(L, _shape(dh=12), Kr=FAKE, Ck=FAKE) == SHAPE         # dh % 8
+    assert _fit(L, s, iters=0) == RANGE
+    assert _fit(L, s, init=9) == RANGE
+    assert _fit(L, s, H=MISALIGNED) == ALIGN
+    assert _fit(L, s, ws=None) == WORKSPACE
+    assert _fit(L, s, ws_bytes=16) == WORKSPACE
+    # W = 0 is a valid no-op and enqueues nothing
+    assert _fit(L, _shape(W=0)) == OK
+
+
+def test_residual_argument_checks(L):
+    s = _shape()
+    f = lambda s=s, dt=1, H=FAKE: L.ps_residual_nvfp4(ctypes.byref(s), dt, H, FAKE, FAKE, FAKE, FAKE,
+                                                      FAKE, FAKE, None)
+    assert f(H=None) == NULL
+    assert f(dt=5) == DTYPE
+    assert f(s=_shape(d=8)) == SHAPE
+    assert f(H=MISALIGNED) == ALIGN
+    assert f(s=_shape(W=0)) == OK
+
+
+def test_proxy_and_drift_argument_checks(L):
+    s = _shape()
+    f = lambda s=s, Q=FAKE, prev=FAKE, kind=0, cur=FAKE: L.ps_proxy_attn(
+        ctypes.byref(s), 1, Q, FAKE, ctypes.c_float(0.25), cur, prev, kind, None, FAKE, FAKE, None)
+    assert f(Q=None) == NULL
+    assert f(kind=3) == RANGE
+    assert f(prev=FAKE, cur=FAKE) == RANGE                 # logp_prev aliases logp_cur
+    assert f(s=_shape(Hq=3)) == SHAPE
+    assert f(s=_shape(Nb=65)) == SHAPE
+    assert f(s=_shape(W=0), prev=None) == OK
+    g = lambda s=s, kind=0: L.ps_drift_kl(ctypes.byref(s), FAKE, ctypes.c_void_p(0x20000), kind, None,
+                                          FAKE, FAKE, None)
+    assert g(kind=-1) == RANGE
+    assert g(s=_shape(K=2000)) == SHAPE
+    assert g(s=_shape(W=0)) == OK
+
+
+def test_topk_and_gather_argument_checks(L):
+    s = _shape()
+    t = lambda k, s=s: L.ps_topk_clusters(ctypes.byref(s), FAKE, k, FAKE, None, None)
+    assert t(0) == RANGE
+    assert t(5) == RANGE                                   # k > K
+    assert t(4, s=_shape(W=0)) == OK
+    g = lambda k=2, cap=8, pos=FAKE, Hh=None, codes=None: L.ps_refresh_gather(
+        ctypes.byref(s), 1, FAKE, FAKE, k, cap, pos, FAKE, codes, None, None, None, None, Hh, None,
+        None, None, None, None)
+    assert g(k=0) == RANGE
+    assert g(cap=-1) == RANGE
+    assert g(pos=None) == NULL                             # cap > 0 needs pos
+    assert g(Hh=FAKE) == NULL                              # H_hat needs the residual inputs
+    assert L.ps_refresh_gather(ctypes.byref(_shape(W=0)), 1, FAKE, FAKE, 2, 0, None, FAKE, None,
+                               None, None, None, None, None, None, None, None, None, None) == OK

@@ -1,0 +1,360 @@
+"""GPU parity of each library call against the oracle, stage-fed: the oracle
+gets exactly the inputs the GPU call got (read back from the device where they
+came from an earlier GPU stage).  Integer and byte results are bit-exact except
+documented near-ties; floating-point results within 1e-3 relative / 1e-5
+absolute.  Shapes span several tiles with ragged tails (N not a multiple of
+128, K not a multiple of 16, d not a multiple of 64, dh not a multiple of 32)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from parity_helpers import (assignment_mismatches, bf16f, close, dev, host, max_rel,
+                            topk_equivalent)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import drift_aware_kv_amd as P
+    P.lib()
+    return P
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rnd_bf16(rng, shape, scale=1.0):
+    return O.f32_to_bf16((rng.standard_normal(shape) * scale).astype(np.float32)) if np.prod(shape) < 4e6 \
+        else _fast_bf16(rng, shape, scale)
+
+
+def _fast_bf16(rng, shape, scale):
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    u = x.view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+KM_CASES = [
+    # name, W, N, d, K, Hkv, dh, bf16
+    ("ragged-bf16", 3, 300, 80, 37, 2, 24, True),
+    ("k300-two-groups", 1, 600, 64, 300, 1, 32, True),
+    ("tiny-f32", 2, 200, 64, 8, 1, 64, False),
+    ("llada-row", 1, 256, 4096, 64, 32, 128, True),
+    ("k1", 2, 130, 48, 1, 1, 16, True),
+]
+
+
+@pytest.mark.parametrize("case", KM_CASES, ids=[c[0] for c in KM_CASES])
+def test_kmeans_lockstep(P, case):
+    """Each Lloyd iteration on the GPU against the oracle's iteration from the
+    same centres (init STRIDED on both sides first, then GIVEN)."""
+    name, W, N, d, K, Hkv, dh, bf = case
+    say("kmeans lockstep", name)
+    rng = np.random.default_rng(abs(hash(name)) % 2**32)
+    dt = P.PS_BF16 if bf else P.PS_F32
+    H = rnd_bf16(rng, (W, N, d)) if bf else rng.standard_normal((W, N, d)).astype(np.float32)
+    Kr = rnd_bf16(rng, (W, N, Hkv, dh)) if bf else rng.standard_normal((W, N, Hkv, dh)).astype(np.float32)
+    s = P.Shape(W=W, N=N, d=d, Hq=Hkv, Hkv=Hkv, dh=dh, Nb=1, K=K)
+    so = O.Shape(W=W, N=N, d=d, Hq=Hkv, Hkv=Hkv, dh=dh, Nb=1, K=K)
+    Hd, Krd = dev(H), dev(Kr)
+    C = torch.zeros(W, K, d, dtype=torch.float32, device="cuda")
+    a = torch.zeros(W, N, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(W, K, dtype=torch.int32, device="cuda")
+    rn = torch.zeros(W, N, dtype=torch.float32, device="cuda")
+    Ck = torch.zeros(W, K, Hkv, dh, dtype=torch.bfloat16 if bf else torch.float32, device="cuda")
+    obj = torch.zeros(W, dtype=torch.float64, device="cuda")
+    ws = P.workspace(s, dt)
+    Ck_o = np.zeros((W, K, Hkv, dh), np.uint16 if bf else np.float32)
+    odt = O.BF16 if bf else O.F32
+    seeds = O.kmeans_init(so, odt, H, O.INIT_STRIDED)
+    ties_total = 0
+    for it in range(4):
+        init = P.PS_INIT_STRIDED if it == 0 else P.PS_INIT_GIVEN
+        C_in = seeds.copy() if it == 0 else host(C).copy()   # centres this iteration assigns against
+        Ck_in = host(Ck).copy()
+        P.ps_kmeans_fit(s, dt, Hd, Krd, init, 1, C, a, cnt, rn, Ck, obj, ws)
+        torch.cuda.synchronize()
+        r = O.kmeans_fit(so, odt, H, Kr, init, 1, C_in.copy(), Ck_in.copy())
+        ga, gC, gn, gcnt, gCk, gobj = host(a), host(C), host(rn), host(cnt), host(Ck), host(obj)
+        assert max_rel(gn, r["row_norm"]) <= 1.2e-7, "row norms"
+        ties_it = 0
+        for w in range(W):
+            ties, real = assignment_mismatches(H[w], C_in[w], bf, ga[w], r["assign"][w],
+                                               r["row_norm"][w])
+            assert not real, f"iter {it} window {w}: {len(real)} assignment disagreements"
+            ties_it += len(ties)
+        ties_total += ties_it
+        if ties_it == 0:
+            assert np.array_equal(gcnt, r["counts"])
+            assert close(gC, r["C"], 1e-6, 1e-7), f"centres iter {it}: {max_rel(gC, r['C'])}"
+            if bf:
+                assert np.array_equal(gCk, r["Ck"]), "centroid keys"
+            else:
+                assert close(gCk, r["Ck"], 1e-6, 1e-7)
+            assert close(gobj, r["objective"], 1e-9, 1e-9)
+        # the next iteration starts both sides from the GPU's centres (lockstep)
+    say("  near-ties:", ties_total)
+
+
+def test_kmeans_chained_planted_exact(P):
+    """The tiny planted case, chained end to end from FARTHEST seeding over 10
+    iterations, must equal the oracle exactly."""
+    import synth
+    cfg = synth.CONFIGS["C1"]
+    data = synth.generate(cfg)
+    s = P.Shape(W=1, N=cfg.N, d=cfg.d, Hq=1, Hkv=1, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
+    so = O.Shape(W=1, N=cfg.N, d=cfg.d, Hq=1, Hkv=1, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
+    C = torch.zeros(1, cfg.K, cfg.d, device="cuda")
+    a = torch.zeros(1, cfg.N, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, cfg.K, dtype=torch.int32, device="cuda")
+    rn = torch.zeros(1, cfg.N, device="cuda")
+    Ck = torch.zeros(1, cfg.K, 1, cfg.dh, device="cuda")
+    obj = torch.zeros(1, dtype=torch.float64, device="cuda")
+    P.ps_kmeans_fit(s, P.PS_F32, dev(data["H"]), dev(data["Kr"]), P.PS_INIT_FARTHEST, cfg.iters, C, a,
+                    cnt, rn, Ck, obj, P.workspace(s, P.PS_F32))
+    torch.cuda.synchronize()
+    r = O.kmeans_fit(so, O.F32, data["H"], data["Kr"], O.INIT_FARTHEST, cfg.iters,
+                     np.zeros((1, cfg.K, cfg.d), np.float32))
+    assert np.array_equal(host(a), r["assign"])
+    assert np.array_equal(host(cnt), r["counts"])
+    assert close(host(C), r["C"], 1e-6, 1e-7)
+    assert close(host(Ck), r["Ck"], 1e-6, 1e-7)
+    assert max_rel(host(rn), r["row_norm"]) <= 1.2e-7
+
+
+@pytest.mark.parametrize("bf", [True, False])
+def test_farthest_seeding_matches(P, bf):
+    rng = np.random.default_rng(5)
+    W, N, d, K = 2, 333, 96, 11
+    H = rnd_bf16(rng, (W, N, d)) if bf else rng.standard_normal((W, N, d)).astype(np.float32)
+    H[0, 7] = 0  # a zero row is never a seed
+    dt = P.PS_BF16 if bf else P.PS_F32
+    s = P.Shape(W=W, N=N, d=d, K=K)
+    C = torch.zeros(W, K, d, device="cuda")
+    a = torch.zeros(W, N, dtype=torch.int32, device="cuda")
+    P.ps_kmeans_fit(s, dt, dev(H), None, P.PS_INIT_FARTHEST, 1, C, a,
+                    torch.zeros(W, K, dtype=torch.int32, device="cuda"),
+                    torch.zeros(W, N, device="cuda"), None, None, P.workspace(s, dt))
+    torch.cuda.synchronize()
+    seeds = O.kmeans_init(O.Shape(W=W, N=N, d=d, K=K), O.BF16 if bf else O.F32, H, O.INIT_FARTHEST)
+    r = O.kmeans_fit(O.Shape(W=W, N=N, d=d, K=K), O.BF16 if bf else O.F32, H, None, O.INIT_GIVEN, 1,
+                     seeds.copy())
+    assert np.array_equal(host(a), r["assign"])
+    assert close(host(C), r["C"], 1e-6, 1e-7)
+
+
+RES_CASES = [("bf16-4096", 2, 97, 4096, 5, True), ("bf16-80", 3, 50, 80, 4, True),
+             ("f32-64", 2, 64, 64, 3, False), ("bf16-8192", 1, 9, 8192, 2, True)]
+
+
+@pytest.mark.parametrize("case", RES_CASES, ids=[c[0] for c in RES_CASES])
+def test_residual_bit_exact(P, case):
+    name, W, N, d, K, bf = case
+    say("residual", name)
+    rng = np.random.default_rng(11)
+    H32 = (rng.standard_normal((W, N, d)) * np.exp(rng.uniform(-4, 4, (W, N, 1)))).astype(np.float32)
+    H32[0, 1] = 0.0                                   # zero row
+    H32[0, 2, 16:48] *= 1e-6                          # blocks far below the row max
+    H = O.f32_to_bf16(H32) if bf else H32
+    Hf = bf16f(H) if bf else H
+    rn = np.sqrt((Hf.astype(np.float64) ** 2).sum(-1)).astype(np.float32)
+    C = rng.standard_normal((W, K, d)).astype(np.float32)
+    C /= np.linalg.norm(C, axis=-1, keepdims=True)
+    assign = rng.integers(0, K, (W, N)).astype(np.int32)
+    assign[0, 3] = -5                                   # out of range reads cluster 0
+    # a row whose residual is exactly zero: h = c * n with n = 1 exactly representable
+    if not bf:
+        C[0, 0] = 0
+        C[0, 0, 0] = 1.0
+        H[0, 4] = 0
+        H[0, 4, 0] = 1.0
+        rn[0, 4] = 1.0
+        assign[0, 4] = 0
+    s = P.Shape(W=W, N=N, d=d, K=K)
+    dt = P.PS_BF16 if bf else P.PS_F32
+    codes = torch.zeros(W, N, d // 2, dtype=torch.uint8, device="cuda")
+    bsc = torch.zeros(W, N, d // 16, dtype=torch.uint8, device="cuda")
+    rsc = torch.zeros(W, N, device="cuda")
+    P.ps_residual_nvfp4(s, dt, dev(H), dev(rn), dev(C), dev(assign), codes, bsc, rsc)
+    torch.cuda.synchronize()
+    r = O.residual_nvfp4(O.Shape(W=W, N=N, d=d, K=K), O.BF16 if bf else O.F32, H, rn, C, assign)
+    assert np.array_equal(host(rsc).view(np.uint32), r["rscale"].view(np.uint32))
+    assert np.array_equal(host(bsc), r["bscale"])
+    assert np.array_equal(host(codes), r["codes"])
+
+
+def test_residual_ties_and_saturation(P):
+    """Rows built so that many elements land exactly on E2M1 midpoints and
+    block scales on E4M3 midpoints and on the 448 saturation edge."""
+    rng = np.random.default_rng(12)
+    N, d = 256, 256
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.5, 3.0], np.float64)
+    H = np.zeros((1, N, d), np.float32)
+    for j in range(N):
+        g = 2.0 ** rng.integers(-12, -2)
+        for b in range(d // 16):
+            sc = float(O.e4m3_decode(int(rng.integers(8, 126))))
+            if rng.random() < 0.3:  # a scale exactly between two E4M3 values
+                c0 = int(rng.integers(8, 125))
+                sc = (float(O.e4m3_decode(c0)) + float(O.e4m3_decode(c0 + 1))) / 2
+            v = rng.choice(mids, 16) * rng.choice([-1, 1], 16)
+            v[0] = 6.0
+            H[0, j, 16 * b:16 * b + 16] = (v * sc * g).astype(np.float32)
+        H[0, j, 0] = np.float32(6.0 * 448 * g)
+    rn = np.ones((1, N), np.float32)
+    C = np.zeros((1, 1, d), np.float32)
+    a = np.zeros((1, N), np.int32)
+    s = P.Shape(W=1, N=N, d=d, K=1)
+    codes = torch.zeros(1, N, d // 2, dtype=torch.uint8, device="cuda")
+    bsc = torch.zeros(1, N, d // 16, dtype=torch.uint8, device="cuda")
+    rsc = torch.zeros(1, N, device="cuda")
+    P.ps_residual_nvfp4(s, P.PS_F32, dev(H), dev(rn), dev(C), dev(a), codes, bsc, rsc)
+    torch.cuda.synchronize()
+    r = O.residual_nvfp4(O.Shape(W=1, N=N, d=d, K=1), O.F32, H, rn, C, a)
+    assert np.array_equal(host(rsc).view(np.uint32), r["rscale"].view(np.uint32))
+    assert np.array_equal(host(bsc), r["bscale"])
+    assert np.array_equal(host(codes), r["codes"])
+
+
+ATT_CASES = [
+    # name, W, Nb, Hq, Hkv, dh, K, bf16
+    ("llada", 2, 32, 32, 32, 128, 64, True),
+    ("dream-gqa", 1, 32, 28, 4, 128, 128, True),
+    ("ragged", 3, 13, 6, 3, 24, 37, True),
+    ("k256", 1, 32, 8, 8, 128, 256, True),
+    ("k1000", 1, 5, 2, 1, 32, 1000, True),
+    ("f32", 2, 16, 1, 1, 64, 8, False),
+]
+
+
+@pytest.mark.parametrize("case", ATT_CASES, ids=[c[0] for c in ATT_CASES])
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_proxy_attn_and_drift(P, case, kind):
+    name, W, Nb, Hq, Hkv, dh, K, bf = case
+    say("proxy", name, kind)
+    rng = np.random.default_rng(13)
+    if bf:
+        Q, Ck = rnd_bf16(rng, (W, Nb, Hq, dh)), rnd_bf16(rng, (W, K, Hkv, dh), 0.5)
+    else:
+        Q = rng.standard_normal((W, Nb, Hq, dh)).astype(np.float32)
+        Ck = (rng.standard_normal((W, K, Hkv, dh)) * 0.5).astype(np.float32)
+    s = P.Shape(W=W, N=K, d=16, Hq=Hq, Hkv=Hkv, dh=dh, Nb=Nb, K=K)
+    so = O.Shape(W=W, N=K, d=16, Hq=Hq, Hkv=Hkv, dh=dh, Nb=Nb, K=K)
+    sigma = float(np.float32(dh ** -0.5))
+    prev = O.proxy_attn(so, O.BF16 if bf else O.F32, Q, Ck, sigma)["logp"]
+    prev = (prev + rng.standard_normal(prev.shape).astype(np.float32) * 0.05).astype(np.float32)
+    dt = P.PS_BF16 if bf else P.PS_F32
+    lc = torch.zeros(W, Hq, Nb, K, device="cuda")
+    Dhi = torch.zeros(W, Hq, Nb, device="cuda")
+    Di = torch.zeros(W, Nb, device="cuda")
+    sc = torch.zeros(W, K, device="cuda")
+    P.ps_proxy_attn(s, dt, dev(Q), dev(Ck), sigma, lc, dev(prev), kind, Dhi, Di, sc)
+    torch.cuda.synchronize()
+    ro = O.proxy_attn(so, O.BF16 if bf else O.F32, Q, Ck, sigma)
+    gl = host(lc)
+    assert close(gl, ro["logp"]), f"logp {max_rel(gl, ro['logp'])}"
+    kl = O.drift_kl(so, gl, prev, kind)   # stage-fed: the GPU's logp
+    assert close(host(Dhi), kl["D_hi"])
+    assert close(host(Di), kl["D_i"])
+    assert close(host(sc), kl["score"])
+    # window formation: no previous distribution -> zeros
+    P.ps_proxy_attn(s, dt, dev(Q), dev(Ck), sigma, lc, None, kind, Dhi, Di, sc)
+    torch.cuda.synchronize()
+    assert not host(Di).any() and not host(sc).any() and not host(Dhi).any()
+
+
+def test_drift_identical_is_exactly_zero(P):
+    rng = np.random.default_rng(14)
+    W, Hq, Nb, K = 2, 8, 16, 64
+    lp = O.proxy_attn(O.Shape(W=W, N=K, d=16, Hq=Hq, Hkv=Hq, dh=16, Nb=Nb, K=K), O.F32,
+                      rng.standard_normal((W, Nb, Hq, 16)).astype(np.float32),
+                      rng.standard_normal((W, K, Hq, 16)).astype(np.float32), 0.25)["logp"]
+    s = P.Shape(W=W, N=K, d=16, Hq=Hq, Hkv=Hq, dh=16, Nb=Nb, K=K)
+    Dhi, Di, sc = (torch.ones(W, Hq, Nb, device="cuda"), torch.ones(W, Nb, device="cuda"),
+                   torch.ones(W, K, device="cuda"))
+    P.ps_drift_kl(s, dev(lp), dev(lp.copy()), 0, Dhi, Di, sc)
+    torch.cuda.synchronize()
+    assert not host(Dhi).any() and not host(Di).any() and not host(sc).any()
+
+
+@pytest.mark.parametrize("K,k", [(8, 2), (64, 4), (128, 8), (256, 16), (1000, 64), (5, 5), (1, 1)])
+def test_topk_bit_exact(P, K, k):
+    rng = np.random.default_rng(K * 7 + k)
+    W = 9
+    sc = rng.standard_normal((W, K)).astype(np.float32)
+    sc[1, ::2] = 0.25                       # planted ties
+    sc[2, : K // 2] = -0.0
+    sc[2, K // 2:] = 0.0
+    sc[3, rng.integers(0, K, max(1, K // 5))] = np.nan
+    sc[4, 0] = np.inf
+    sc[4, -1] = -np.inf
+    sc[5, :] = np.nan
+    sc[6] = np.round(sc[6], 1)              # many ties
+    sc[7] = 1e-30 * sc[7]                   # subnormal-range scores
+    s = P.Shape(W=W, N=K, d=16, K=K)
+    idx = torch.zeros(W, k, dtype=torch.int32, device="cuda")
+    val = torch.zeros(W, k, device="cuda")
+    P.ps_topk_clusters(s, dev(sc), k, idx, val)
+    torch.cuda.synchronize()
+    r = O.topk_clusters(O.Shape(W=W, N=K, d=16, K=K), sc, k)
+    assert np.array_equal(host(idx), r["idx"])
+    assert np.array_equal(host(val), r["val"], equal_nan=True)
+
+
+@pytest.mark.parametrize("bf", [True, False])
+@pytest.mark.parametrize("cap_mode", ["ample", "short", "zero"])
+def test_refresh_gather_bit_exact(P, bf, cap_mode):
+    rng = np.random.default_rng(15)
+    W, N, d, K, k, Hkv, dh = 3, 517, 96, 23, 4, 2, 16
+    H32 = rng.standard_normal((W, N, d)).astype(np.float32)
+    H = O.f32_to_bf16(H32) if bf else H32
+    Hf = bf16f(H) if bf else H
+    rn = np.sqrt((Hf.astype(np.float64) ** 2).sum(-1)).astype(np.float32)
+    C = rng.standard_normal((W, K, d)).astype(np.float32)
+    C /= np.linalg.norm(C, axis=-1, keepdims=True)
+    assign = rng.integers(0, K, (W, N)).astype(np.int32)
+    so = O.Shape(W=W, N=N, d=d, Hq=Hkv, Hkv=Hkv, dh=dh, K=K)
+    q = O.residual_nvfp4(so, O.BF16 if bf else O.F32, H, rn, C, assign)
+    idx = np.stack([rng.choice(K, k, replace=False) for _ in range(W)]).astype(np.int32)
+    idx[2, 0] = K + 3   # out of range: selects nothing
+    Kc = rnd_bf16(rng, (W, N, Hkv, dh)) if bf else rng.standard_normal((W, N, Hkv, dh)).astype(np.float32)
+    Vc = rnd_bf16(rng, (W, N, Hkv, dh)) if bf else rng.standard_normal((W, N, Hkv, dh)).astype(np.float32)
+    cap = {"ample": N, "short": 17, "zero": 0}[cap_mode]
+    r = O.refresh_gather(so, O.BF16 if bf else O.F32, assign, idx, k, cap, q["codes"], q["bscale"],
+                         q["rscale"], C, rn, True, Kc, Vc)
+    s = P.Shape(W=W, N=N, d=d, Hq=Hkv, Hkv=Hkv, dh=dh, K=K)
+    et = torch.bfloat16 if bf else torch.float32
+    pos = torch.full((W, max(cap, 1)), -1, dtype=torch.int32, device="cuda")
+    count = torch.zeros(W, dtype=torch.int32, device="cuda")
+    Hh = torch.zeros(W, max(cap, 1), d, dtype=et, device="cuda")
+    Ko = torch.zeros(W, max(cap, 1), Hkv, dh, dtype=et, device="cuda")
+    Vo = torch.zeros(W, max(cap, 1), Hkv, dh, dtype=et, device="cuda")
+    P.ps_refresh_gather(s, P.PS_BF16 if bf else P.PS_F32, dev(assign), dev(idx), k, cap,
+                        pos if cap else None, count, dev(q["codes"]), dev(q["bscale"]),
+                        dev(q["rscale"]), dev(C), dev(rn), Hh if cap else None,
+                        dev(Kc) if cap else None, dev(Vc) if cap else None,
+                        Ko if cap else None, Vo if cap else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(count), r["count"])
+    if cap:
+        for w in range(W):
+            m = min(int(r["count"][w]), cap)
+            assert np.array_equal(host(pos)[w, :m], r["pos"][w, :m])
+            assert np.array_equal(host(Hh)[w, :m].view(np.uint16 if bf else np.uint32),
+                                  r["H_hat"][w, :m].view(np.uint16 if bf else np.uint32))
+            assert np.array_equal(host(Ko)[w, :m], r["K_out"][w, :m])
+            assert np.array_equal(host(Vo)[w, :m], r["V_out"][w, :m])
+            assert np.all(host(pos)[w, m:] == -1)       # slots past count untouched
+
+
+def test_w_zero_is_a_no_op(P):
+    s = P.Shape(W=0, N=64, d=32, K=4)
+    z = torch.zeros(16, dtype=torch.int32, device="cuda")
+    P.ps_topk_clusters(s, torch.zeros(16, device="cuda"), 2, z)
+    torch.cuda.synchronize()

@@ -1,0 +1,273 @@
+"""Chained end-to-end parity of whole steps (kmeans -> residual -> proxy
+attention + drift -> top-k -> gather) against the oracle run from the same
+seeded inputs, on the workloads of the benchmark: the tiny planted case, a
+LLaDA-8B layer, a Dream-7B layer (GQA), and at full size the 512-window
+LLaDA-8B batch and the 128-window long-window batch on sampled windows (every
+window is independent, so a sampled window's results depend on its own data
+only; the other windows carry random data of the same shape).
+
+Where the two sides assign a row differently the test classifies the
+difference: it must be a near-tie (oracle fp64 gap <= 1e-6 on the cosine
+scale) found by replaying that step one Lloyd iteration at a time from the
+GPU's centres; everything downstream is then compared stage-fed."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from parity_helpers import (assignment_mismatches, bf16f, close, dev, host, max_rel,
+                            topk_equivalent)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import drift_aware_kv_amd as P
+    P.lib()
+    return P
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def oshape(cfg, W=1):
+    return O.Shape(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
+
+
+def oracle_step(cfg, st, data, t, iters=None):
+    """One oracle step for one window; st carries C, Ck, logp between steps."""
+    s = oshape(cfg)
+    dt = O.BF16 if cfg.bf16 else O.F32
+    iters = cfg.iters if iters is None else iters
+    if t == 0:
+        init = O.INIT_FARTHEST if cfg.init0 == "farthest" else O.INIT_STRIDED
+        C = np.zeros((1, cfg.K, cfg.d), np.float32)
+        Ck = np.zeros((1, cfg.K, cfg.Hkv, cfg.dh), np.uint16 if cfg.bf16 else np.float32)
+    else:
+        init, C, Ck = O.INIT_GIVEN, st["C"].copy(), st["Ck"].copy()
+    r = O.kmeans_fit(s, dt, data["H"], data["Kr"], init, iters, C, Ck)
+    q = O.residual_nvfp4(s, dt, data["H"], r["row_norm"], r["C"], r["assign"])
+    pa = O.proxy_attn(s, dt, data["Q"], r["Ck"], cfg.softmax_scale,
+                      None if t == 0 else st["logp"])
+    out = dict(C=r["C"], Ck=r["Ck"], assign=r["assign"], counts=r["counts"], row_norm=r["row_norm"],
+               codes=q["codes"], bscale=q["bscale"], rscale=q["rscale"], logp=pa["logp"],
+               D_i=pa["D_i"], D_hi=pa["D_hi"], score=pa["score"])
+    if t > 0:
+        tk = O.topk_clusters(s, pa["score"], cfg.k)
+        g = O.refresh_gather(s, dt, r["assign"], tk["idx"], cfg.k, cfg.N, q["codes"], q["bscale"],
+                             q["rscale"], r["C"], r["row_norm"], True, data["Kr"], data["V"])
+        out.update(idx=tk["idx"], pos=g["pos"], count=g["count"], H_hat=g["H_hat"],
+                   K_out=g["K_out"], V_out=g["V_out"])
+    return out
+
+
+def gpu_snapshot(path, w, t):
+    o = dict(C=host(path.C[w:w + 1]), Ck=host(path.Ck[w:w + 1]), assign=host(path.assign[w:w + 1]),
+             counts=host(path.counts[w:w + 1]), row_norm=host(path.row_norm[w:w + 1]),
+             codes=host(path.codes[w:w + 1]), bscale=host(path.bscale[w:w + 1]),
+             rscale=host(path.rscale[w:w + 1]), logp=host(path.logp[t & 1][w:w + 1]),
+             D_i=host(path.D_i[w:w + 1]), D_hi=host(path.D_hi[w:w + 1]),
+             score=host(path.score[w:w + 1]))
+    if t > 0:
+        o.update(idx=host(path.idx[w:w + 1]), pos=host(path.pos[w:w + 1]),
+                 count=host(path.count[w:w + 1]), H_hat=host(path.H_hat[w:w + 1]),
+                 K_out=host(path.K_out[w:w + 1]), V_out=host(path.V_out[w:w + 1]))
+    return o
+
+
+def compare_downstream(cfg, g, data, t, prev_logp):
+    """Everything after K-Means, stage-fed from the GPU's own upstream."""
+    s = oshape(cfg)
+    dt = O.BF16 if cfg.bf16 else O.F32
+    q = O.residual_nvfp4(s, dt, data["H"], g["row_norm"], g["C"], g["assign"])
+    assert np.array_equal(g["codes"], q["codes"]), "codes"
+    assert np.array_equal(g["bscale"], q["bscale"]), "block scales"
+    assert np.array_equal(g["rscale"].view(np.uint32), q["rscale"].view(np.uint32)), "row scales"
+    pa = O.proxy_attn(s, dt, data["Q"], g["Ck"], cfg.softmax_scale)
+    assert close(g["logp"], pa["logp"]), f"logp {max_rel(g['logp'], pa['logp'])}"
+    if t == 0:
+        assert not g["D_i"].any() and not g["score"].any()
+        return
+    kl = O.drift_kl(s, g["logp"], prev_logp)
+    assert close(g["D_i"], kl["D_i"]) and close(g["score"], kl["score"]) and close(g["D_hi"], kl["D_hi"])
+    tk = O.topk_clusters(s, g["score"], cfg.k)
+    assert np.array_equal(g["idx"], tk["idx"]), "top-k on the GPU's scores"
+    ga = O.refresh_gather(s, dt, g["assign"], g["idx"], cfg.k, cfg.N, g["codes"], g["bscale"],
+                          g["rscale"], g["C"], g["row_norm"], True, data["Kr"], data["V"])
+    m = int(ga["count"][0])
+    assert int(g["count"][0]) == m
+    assert np.array_equal(g["pos"][0, :m], ga["pos"][0, :m])
+    assert np.array_equal(g["H_hat"][0, :m].view(np.uint16 if cfg.bf16 else np.uint32),
+                          ga["H_hat"][0, :m].view(np.uint16 if cfg.bf16 else np.uint32))
+    assert np.array_equal(g["K_out"][0, :m], ga["K_out"][0, :m])
+    assert np.array_equal(g["V_out"][0, :m], ga["V_out"][0, :m])
+
+
+def lockstep_replay(P, cfg, data, C_start, Ck_start, t):
+    """Replay one step's K-Means one iteration at a time on the GPU from the
+    given centres, feeding each iteration's GPU centres to the oracle; return
+    the number of near-tie flips (asserting there is no real disagreement)."""
+    s = P.Shape(W=1, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
+    dt = P.PS_BF16 if cfg.bf16 else P.PS_F32
+    odt = O.BF16 if cfg.bf16 else O.F32
+    C = dev(C_start)
+    Ck = dev(Ck_start)
+    a = torch.zeros(1, cfg.N, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, cfg.K, dtype=torch.int32, device="cuda")
+    rn = torch.zeros(1, cfg.N, device="cuda")
+    ws = P.workspace(s, dt)
+    Hd, Krd = dev(data["H"]), dev(data["Kr"])
+    flips = 0
+    for it in range(cfg.iters):
+        init = P.PS_INIT_GIVEN
+        if t == 0 and it == 0:
+            init = P.PS_INIT_FARTHEST if cfg.init0 == "farthest" else P.PS_INIT_STRIDED
+            C_in = O.kmeans_init(oshape(cfg), odt, data["H"],
+                                 O.INIT_FARTHEST if cfg.init0 == "farthest" else O.INIT_STRIDED)
+        else:
+            C_in = host(C).copy()
+        P.ps_kmeans_fit(s, dt, Hd, Krd, init, 1, C, a, cnt, rn, Ck, None, ws)
+        torch.cuda.synchronize()
+        r = O.kmeans_fit(oshape(cfg), odt, data["H"], None, O.INIT_GIVEN, 1, C_in.copy())
+        ties, real = assignment_mismatches(data["H"][0], C_in[0], cfg.bf16, host(a)[0],
+                                           r["assign"][0], r["row_norm"][0])
+        assert not real, f"step {t} iteration {it}: {len(real)} real disagreements"
+        flips += len(ties)
+    return flips
+
+
+def run_chained(P, cfg, steps, windows=None, W=None):
+    """GPU DriftPath over `steps` steps; for each sampled window the oracle
+    runs chained; on an assignment difference the step is replayed in
+    lockstep and the oracle re-synchronised to the GPU state."""
+    from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
+    W = cfg.W if W is None else W
+    windows = list(range(W)) if windows is None else windows
+    spec = StepSpec(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K,
+                    k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
+                    softmax_scale=cfg.softmax_scale, cap=cfg.N)
+    path = DriftPath(spec)
+    et = torch.bfloat16 if cfg.bf16 else torch.float32
+    # device inputs: sampled windows from the generator, the rest random
+    host_data = {w: synth.generate(cfg, w0=w, Wc=1) for w in windows}
+    g = torch.Generator(device="cuda").manual_seed(1)
+
+    def fill(shape):
+        return torch.randn(shape, device="cuda", generator=g).to(et)
+
+    Hd = fill((W, cfg.N, cfg.d))
+    Krd = fill((W, cfg.N, cfg.Hkv, cfg.dh))
+    Vd = fill((W, cfg.N, cfg.Hkv, cfg.dh))
+    Qd = fill((W, cfg.Nb, cfg.Hq, cfg.dh))
+
+    def upload(w):
+        for key, dst in (("H", Hd), ("Kr", Krd), ("V", Vd), ("Q", Qd)):
+            src = dev(host_data[w][key][0])
+            dst[w].copy_(src.view(et) if cfg.bf16 else src)
+
+    ost = {w: None for w in windows}
+    total_flips = 0
+    for t in range(steps):
+        if t > 0:
+            for w in windows:
+                synth.apply_drift(cfg, host_data[w], t, w0=w)
+            Hd.add_(fill(Hd.shape) * 0.01)  # unchecked windows drift too
+        for w in windows:
+            upload(w)
+        say(f"  {cfg.name} step {t}: GPU")
+        prevC = {w: host(path.C[w:w + 1]).copy() for w in windows}
+        prevCk = {w: host(path.Ck[w:w + 1]).copy() for w in windows}
+        path.step(Hd, Krd, Vd, Qd)
+        torch.cuda.synchronize()
+        for w in windows:
+            say(f"  {cfg.name} step {t}: oracle window {w}")
+            gs = gpu_snapshot(path, w, t)
+            o = oracle_step(cfg, ost[w], host_data[w], t)
+            if np.array_equal(gs["assign"], o["assign"]):
+                assert np.array_equal(gs["counts"], o["counts"])
+                assert close(gs["C"], o["C"], 1e-6, 1e-7), f"centres {max_rel(gs['C'], o['C'])}"
+                assert np.array_equal(gs["Ck"], o["Ck"]) if cfg.bf16 else close(gs["Ck"], o["Ck"], 1e-6, 1e-7)
+                assert max_rel(gs["row_norm"], o["row_norm"]) <= 1.2e-7
+                assert np.array_equal(gs["codes"], o["codes"])
+                assert np.array_equal(gs["bscale"], o["bscale"])
+                assert close(gs["logp"], o["logp"])
+                if t > 0:
+                    assert close(gs["D_i"], o["D_i"]) and close(gs["score"], o["score"])
+                    assert topk_equivalent(o["score"][0], gs["idx"][0], o["idx"][0])
+                    if np.array_equal(gs["idx"], o["idx"]):
+                        m = int(o["count"][0])
+                        assert int(gs["count"][0]) == m
+                        assert np.array_equal(gs["pos"][0, :m], o["pos"][0, :m])
+                        assert np.array_equal(gs["K_out"][0, :m], o["K_out"][0, :m])
+            else:
+                flips = lockstep_replay(P, cfg, host_data[w], prevC[w], prevCk[w], t)
+                say(f"    window {w} step {t}: assignments differ; lockstep near-tie flips: {flips}")
+                total_flips += max(flips, 1)
+            # stage-fed check of everything downstream of K-Means, then carry
+            # the GPU state forward in the oracle too
+            compare_downstream(cfg, gs, host_data[w], t, None if t == 0 else ost[w]["logp_gpu"])
+            ost[w] = dict(C=gs["C"], Ck=gs["Ck"], logp=gs["logp"], logp_gpu=gs["logp"])
+    return total_flips
+
+
+def test_tiny_planted_two_steps_exact(P):
+    cfg = synth.CONFIGS["C1"]
+    flips = run_chained(P, cfg, steps=2)
+    assert flips == 0
+
+
+def test_llada_layer_chained(P):
+    cfg = synth.CONFIGS["C2"]
+    flips = run_chained(P, cfg, steps=3)
+    say("llada layer near-tie flips:", flips)
+
+
+def test_dream_layer_chained(P):
+    cfg = synth.CONFIGS["C3"]
+    flips = run_chained(P, cfg, steps=2)
+    say("dream layer near-tie flips:", flips)
+
+
+def test_full_size_llada_batch_sampled(P):
+    """512 windows (32 layers x 16 sequences) in one launch per call, as the
+    benchmark runs them; windows 0, 301 and 511 checked against the oracle."""
+    cfg = synth.CONFIGS["C4"]
+    flips = run_chained(P, cfg, steps=2, windows=[0, 301, 511])
+    say("llada batch near-tie flips:", flips)
+
+
+def test_full_size_long_window_sampled(P):
+    """128 windows of 8192 tokens, K = 256, in one launch per call; one window
+    checked with one Lloyd iteration per step (the oracle needs minutes for
+    eight at this size: the iteration count does not change the kernels)."""
+    cfg = synth.CONFIGS["C5"].with_(iters=1)
+    flips = run_chained(P, cfg, steps=2, windows=[77])
+    say("long window near-tie flips:", flips)
+
+
+def test_step_is_deterministic(P):
+    """The same inputs twice give bit-identical outputs (no float atomics)."""
+    from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
+    cfg = synth.CONFIGS["C2"].with_(W=4)
+    spec = StepSpec(W=4, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K,
+                    k=cfg.k, iters=cfg.iters, bf16=True, softmax_scale=cfg.softmax_scale)
+    data = synth.generate(cfg)
+    ins = [dev(data[k]) for k in ("H", "Kr", "V", "Q")]
+    outs = []
+    for rep in range(2):
+        p = DriftPath(spec)
+        p.step(*ins)
+        ins[0][:, :60].mul_(-1)  # some drift for step 1
+        p.step(*ins)
+        ins[0][:, :60].mul_(-1)
+        torch.cuda.synchronize()
+        outs.append([host(x).copy() for x in (p.C, p.assign, p.Ck, p.codes, p.logp[1], p.score,
+                                              p.idx, p.pos, p.H_hat)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
