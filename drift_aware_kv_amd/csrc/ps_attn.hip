@@ -12,6 +12,10 @@ namespace {
 // proxy attention, bf16: z[k][i] = sigma * <Ck[k][g(h)], Q[i][h]> on MFMA
 // 16x16x32, one workgroup per window, one head per wave at a time.
 // Lane l holds clusters 16*mb + 4*(l/16) + r of query 16*nb + (l % 16).
+// Clusters run in groups of 16*KB; with one group the log-softmax is done in
+// registers, with several a running max and sum are kept across groups, the
+// raw logits are parked in the output row and rebased in a second pass by the
+// lane that wrote them.
 // ---------------------------------------------------------------------------
 template <int KB, int NBQ>
 __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__ Q,
@@ -19,74 +23,100 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
                                                      float* __restrict__ logp, int Hq, int Hkv, int dh,
                                                      int Nb, int K)
 {
+    constexpr int GK = 16 * KB;
     const int w = blockIdx.x;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const int G = Hq / Hkv;
+    const int ngroups = (K + GK - 1) / GK;
+    const bool vec = (K & 3) == 0;
     for (int h = wave; h < Hq; h += 4) {
         const int g = h / G;
+        float M[NBQ], S[NBQ];
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) { M[nb] = -INFINITY; S[nb] = 0.0f; }
         floatx4 acc[KB][NBQ];
+        for (int cg = 0; cg < K; cg += GK) {
 #pragma unroll
-        for (int mb = 0; mb < KB; ++mb)
+            for (int mb = 0; mb < KB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < NBQ; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (int e0 = 0; e0 < dh; e0 += 32) {
-            const int e = e0 + 8 * q;
-            uint4 bq[NBQ];
+                for (int nb = 0; nb < NBQ; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int e0 = 0; e0 < dh; e0 += 32) {
+                const int e = e0 + 8 * q;
+                uint4 bq[NBQ];
+#pragma unroll
+                for (int nb = 0; nb < NBQ; ++nb) {
+                    const int i = 16 * nb + r16;
+                    bq[nb] = (i < Nb && e < dh)
+                                 ? *reinterpret_cast<const uint4*>(Q + (((size_t)w * Nb + i) * Hq + h) * dh + e)
+                                 : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int mb = 0; mb < KB; ++mb) {
+                    const int kk = cg + 16 * mb + r16;
+                    const uint4 av = (kk < K && e < dh)
+                                         ? *reinterpret_cast<const uint4*>(Ck + (((size_t)w * K + kk) * Hkv + g) * dh + e)
+                                         : make_uint4(0, 0, 0, 0);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+                    for (int nb = 0; nb < NBQ; ++nb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bq[nb]),
+                                                                              acc[mb][nb], 0, 0, 0);
+                }
+            }
 #pragma unroll
             for (int nb = 0; nb < NBQ; ++nb) {
                 const int i = 16 * nb + r16;
-                bq[nb] = (i < Nb && e < dh)
-                             ? *reinterpret_cast<const uint4*>(Q + (((size_t)w * Nb + i) * Hq + h) * dh + e)
-                             : make_uint4(0, 0, 0, 0);
-            }
+                float zmax = -INFINITY;
 #pragma unroll
-            for (int mb = 0; mb < KB; ++mb) {
-                const int kk = 16 * mb + r16;
-                const uint4 av = (kk < K && e < dh)
-                                     ? *reinterpret_cast<const uint4*>(Ck + (((size_t)w * K + kk) * Hkv + g) * dh + e)
-                                     : make_uint4(0, 0, 0, 0);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+                for (int mb = 0; mb < KB; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < NBQ; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bq[nb]),
-                                                                          acc[mb][nb], 0, 0, 0);
+                    for (int r = 0; r < 4; ++r) {
+                        const int kk = cg + 16 * mb + 4 * q + r;
+                        const float z = acc[mb][nb][r] * sigma;
+                        acc[mb][nb][r] = z;
+                        if (kk < K) zmax = fmaxf(zmax, z);
+                    }
+                zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+                zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+                float se = 0.0f;
+#pragma unroll
+                for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int kk = cg + 16 * mb + 4 * q + r;
+                        if (kk < K) se += expf(acc[mb][nb][r] - zmax);
+                    }
+                se += __shfl_xor(se, 16, 64);
+                se += __shfl_xor(se, 32, 64);
+                const float Mn = fmaxf(M[nb], zmax);
+                S[nb] = S[nb] * expf(M[nb] - Mn) + se * expf(zmax - Mn);
+                M[nb] = Mn;
+                if (ngroups > 1 && i < Nb) {
+                    float* out = logp + (((size_t)w * Hq + h) * Nb + i) * K;
+#pragma unroll
+                    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int kk = cg + 16 * mb + 4 * q + r;
+                            if (kk < K) out[kk] = acc[mb][nb][r];
+                        }
+                }
             }
         }
 #pragma unroll
         for (int nb = 0; nb < NBQ; ++nb) {
             const int i = 16 * nb + r16;
-            float zmax = -INFINITY;
-#pragma unroll
-            for (int mb = 0; mb < KB; ++mb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int kk = 16 * mb + 4 * q + r;
-                    const float z = acc[mb][nb][r] * sigma;
-                    acc[mb][nb][r] = z;
-                    if (kk < K) zmax = fmaxf(zmax, z);
-                }
-            zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-            zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-            float se = 0.0f;
-#pragma unroll
-            for (int mb = 0; mb < KB; ++mb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int kk = 16 * mb + 4 * q + r;
-                    if (kk < K) se += expf(acc[mb][nb][r] - zmax);
-                }
-            se += __shfl_xor(se, 16, 64);
-            se += __shfl_xor(se, 32, 64);
-            const float lse = zmax + logf(se);
-            if (i < Nb) {
-                float* out = logp + (((size_t)w * Hq + h) * Nb + i) * K;
+            const float lse = M[nb] + logf(S[nb]);
+            if (i >= Nb) continue;
+            float* out = logp + (((size_t)w * Hq + h) * Nb + i) * K;
+            if (ngroups == 1) {
 #pragma unroll
                 for (int mb = 0; mb < KB; ++mb) {
                     const int k0 = 16 * mb + 4 * q;
                     const float4 v = make_float4(acc[mb][nb][0] - lse, acc[mb][nb][1] - lse,
                                                  acc[mb][nb][2] - lse, acc[mb][nb][3] - lse);
-                    if (k0 + 3 < K && (K & 3) == 0) {
+                    if (vec && k0 + 3 < K) {
                         *reinterpret_cast<float4*>(out + k0) = v;
                     } else {
                         if (k0 < K) out[k0] = v.x;
@@ -95,6 +125,15 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
                         if (k0 + 3 < K) out[k0 + 3] = v.w;
                     }
                 }
+            } else {
+                for (int cg = 0; cg < K; cg += GK)
+#pragma unroll
+                    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int kk = cg + 16 * mb + 4 * q + r;
+                            if (kk < K) out[kk] = out[kk] - lse;
+                        }
             }
         }
     }
@@ -360,8 +399,7 @@ extern "C" ps_status ps_proxy_attn(const ps_shape* s, ps_dtype dtype, const void
         else if (kb <= 2)  launch_proxy_nb<2>(s, Q, Ck, softmax_scale, logp_cur, stm);
         else if (kb <= 4)  launch_proxy_nb<4>(s, Q, Ck, softmax_scale, logp_cur, stm);
         else if (kb <= 8)  launch_proxy_nb<8>(s, Q, Ck, softmax_scale, logp_cur, stm);
-        else if (kb <= 16) launch_proxy_nb<16>(s, Q, Ck, softmax_scale, logp_cur, stm);
-        else return PS_ERR_SHAPE;
+        else               launch_proxy_nb<16>(s, Q, Ck, softmax_scale, logp_cur, stm);
     } else {
         const int pairs = s->Hq * s->Nb;
         PS_LAUNCH("k_proxy_f32", k_proxy_f32, dim3((pairs + 255) / 256, s->W), dim3(256), 0, stm, (const float*)Q,
