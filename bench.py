@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timer")
+    ap.add_argument("--no-fixed-point", action="store_true",
+                    help="skip the secondary timing with the exact fixed-point exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this path runs on one GPU; windows are independent, so more GPUs "
@@ -196,6 +198,22 @@ def main():
             roof.update({"algorithmic_bytes_per_launch": byts, "flops_per_launch": flops,
                          "avg_launch_ms": avg_s * 1e3, "launches": n})
 
+    # secondary figure: the same steps with the exact fixed-point exit (Lloyd
+    # passes after the first that moves no row are skipped per window; the
+    # results are bit-identical to running every pass)
+    fpx = None
+    if not args.no_fixed_point:
+        path.spec.kmeans_flags = P.PS_KMEANS_FIXED_POINT_EXIT
+        torch.cuda.synchronize()
+        f0 = time.perf_counter()
+        for i in range(total, total + args.steps):
+            path.step(*wl.inputs(i))
+        torch.cuda.synchronize()
+        f1 = time.perf_counter()
+        path.spec.kmeans_flags = 0
+        fpx = {"value": args.steps * cfg.W * cfg.N / (f1 - f0), "ms_per_step": 1e3 * (f1 - f0) / args.steps}
+        print(f"[bench] fixed-point exit: {fpx['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
@@ -213,6 +231,7 @@ def main():
                    "input_snapshots": n_snap, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "fixed_point_exit": fpx,
         "kernels": breakdown,
     }
     print(json.dumps(line), flush=True)

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(HERE, "libpolestar_drift.so")
 PS_F32, PS_BF16 = 0, 1
 PS_INIT_GIVEN, PS_INIT_STRIDED, PS_INIT_FARTHEST = 0, 1, 2
 PS_SCORE_KL_SHARE, PS_SCORE_KL_SHARE_ABS, PS_SCORE_ATTN_WEIGHTED = 0, 1, 2
+PS_KMEANS_DEFAULT, PS_KMEANS_FIXED_POINT_EXIT = 0, 1
 
 EXPORTS = ("ps_status_string", "ps_workspace_size", "ps_kmeans_fit", "ps_residual_nvfp4",
            "ps_proxy_attn", "ps_drift_kl", "ps_topk_clusters", "ps_refresh_gather",
@@ -66,8 +67,8 @@ def lib():
         P, I, SP = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(_CShape)
         L.ps_status_string.argtypes, L.ps_status_string.restype = [I], ctypes.c_char_p
         L.ps_workspace_size.argtypes = [SP, I, ctypes.POINTER(ctypes.c_size_t)]
-        L.ps_kmeans_fit.argtypes = [SP, I, P, P, I, ctypes.c_int32, P, P, P, P, P, P, P,
-                                    ctypes.c_size_t, P]
+        L.ps_kmeans_fit.argtypes = [SP, I, P, P, I, ctypes.c_int32, ctypes.c_uint32, P, P, P, P, P,
+                                    P, P, ctypes.c_size_t, P]
         L.ps_residual_nvfp4.argtypes = [SP, I, P, P, P, P, P, P, P, P]
         L.ps_proxy_attn.argtypes = [SP, I, P, P, ctypes.c_float, P, P, I, P, P, P, P]
         L.ps_drift_kl.argtypes = [SP, P, P, I, P, P, P, P]
@@ -165,7 +166,7 @@ def workspace(s: Shape, dtype, device=None):
 
 
 def ps_kmeans_fit(s: Shape, dtype, H, Kr, init, iters, C, assign, counts, row_norm, Ck=None,
-                  objective=None, ws=None, stream=None):
+                  objective=None, ws=None, stream=None, flags=0):
     e = _es(dtype)
     KV = s.Hkv * s.dh
     wsb = ps_workspace_size(s, dtype)
@@ -173,7 +174,7 @@ def ps_kmeans_fit(s: Shape, dtype, H, Kr, init, iters, C, assign, counts, row_no
         raise ValueError("ws is required (see workspace())")
     _check(lib().ps_kmeans_fit(
         _cs(s), dtype, _ptr(H, s.W * s.N * s.d, e, "H"),
-        _ptr(Kr, s.W * s.N * KV, e, "Kr", True), init, iters,
+        _ptr(Kr, s.W * s.N * KV, e, "Kr", True), init, iters, flags,
         _ptr(C, s.W * s.K * s.d, 4, "C"), _ptr(assign, s.W * s.N, 4, "assign"),
         _ptr(counts, s.W * s.K, 4, "counts"), _ptr(row_norm, s.W * s.N, 4, "row_norm"),
         _ptr(Ck, s.W * s.K * KV, e, "Ck", True), _ptr(objective, s.W, 8, "objective", True),

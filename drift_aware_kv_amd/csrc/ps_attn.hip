@@ -8,28 +8,52 @@ using namespace ps;
 
 namespace {
 
+// Per-cluster score term for one (head, query, cluster): the additive KL
+// share p (l - l'), its magnitude, or the attention-weighted drift p * D.
+__device__ __forceinline__ float score_term(int kind, float p, float t, float D)
+{
+    return kind == PS_SCORE_ATTN_WEIGHTED ? p * D : (kind == PS_SCORE_KL_SHARE_ABS ? fabsf(t) : t);
+}
+
 // ---------------------------------------------------------------------------
 // proxy attention, bf16: z[k][i] = sigma * <Ck[k][g(h)], Q[i][h]> on MFMA
 // 16x16x32, one workgroup per window, one head per wave at a time.
 // Lane l holds clusters 16*mb + 4*(l/16) + r of query 16*nb + (l % 16).
 // Clusters run in groups of 16*KB; with one group the log-softmax is done in
-// registers, with several a running max and sum are kept across groups, the
-// raw logits are parked in the output row and rebased in a second pass by the
-// lane that wrote them.
+// registers and, given the previous step's distribution, the drift is fused
+// into the epilogue: D_{h,i} by two lane shuffles, per-cluster scores
+// accumulated per lane over the wave's heads and queries, then combined over
+// queries (shuffles) and waves (LDS) in a fixed order.  With several groups a
+// running max and sum are kept across groups, the raw logits are parked in
+// the output row and rebased in a second pass by the lane that wrote them, and
+// the drift runs as a separate pass (fused = 0).
 // ---------------------------------------------------------------------------
 template <int KB, int NBQ>
 __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ Ck, float sigma,
-                                                     float* __restrict__ logp, int Hq, int Hkv, int dh,
-                                                     int Nb, int K)
+                                                     float* __restrict__ logp, const float* __restrict__ prev,
+                                                     int kind, int fused, float* __restrict__ D_hi,
+                                                     float* __restrict__ D_i, float* __restrict__ score,
+                                                     int Hq, int Hkv, int dh, int Nb, int K)
 {
     constexpr int GK = 16 * KB;
+    __shared__ float sred[4][GK];
+    __shared__ float dred[4][16 * NBQ];
     const int w = blockIdx.x;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const int G = Hq / Hkv;
     const int ngroups = (K + GK - 1) / GK;
     const bool vec = (K & 3) == 0;
+    float sacc[KB][4];
+    float dacc[NBQ];
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[mb][r] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) dacc[nb] = 0.0f;
+
     for (int h = wave; h < Hq; h += 4) {
         const int g = h / G;
         float M[NBQ], S[NBQ];
@@ -107,25 +131,65 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
 #pragma unroll
         for (int nb = 0; nb < NBQ; ++nb) {
             const int i = 16 * nb + r16;
+            const bool iv = i < Nb;
             const float lse = M[nb] + logf(S[nb]);
-            if (i >= Nb) continue;
-            float* out = logp + (((size_t)w * Hq + h) * Nb + i) * K;
+            const size_t row = (((size_t)w * Hq + h) * Nb + (iv ? i : 0)) * K;
+            float* out = logp + row;
             if (ngroups == 1) {
+                float lv[KB][4], pv[KB][4], tv[KB][4];
+                float tsum = 0.0f;
 #pragma unroll
                 for (int mb = 0; mb < KB; ++mb) {
                     const int k0 = 16 * mb + 4 * q;
-                    const float4 v = make_float4(acc[mb][nb][0] - lse, acc[mb][nb][1] - lse,
-                                                 acc[mb][nb][2] - lse, acc[mb][nb][3] - lse);
-                    if (vec && k0 + 3 < K) {
-                        *reinterpret_cast<float4*>(out + k0) = v;
-                    } else {
-                        if (k0 < K) out[k0] = v.x;
-                        if (k0 + 1 < K) out[k0 + 1] = v.y;
-                        if (k0 + 2 < K) out[k0 + 2] = v.z;
-                        if (k0 + 3 < K) out[k0 + 3] = v.w;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) lv[mb][r] = acc[mb][nb][r] - lse;
+                    if (iv) {
+                        if (vec && k0 + 3 < K) {
+                            *reinterpret_cast<float4*>(out + k0) = make_float4(lv[mb][0], lv[mb][1], lv[mb][2], lv[mb][3]);
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (k0 + r < K) out[k0 + r] = lv[mb][r];
+                        }
+                    }
+                    if (fused && prev) {
+                        float pp[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (iv) {
+                            const float* pr = prev + row;
+                            if (vec && k0 + 3 < K) {
+                                const float4 v = *reinterpret_cast<const float4*>(pr + k0);
+                                pp[0] = v.x; pp[1] = v.y; pp[2] = v.z; pp[3] = v.w;
+                            } else {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    if (k0 + r < K) pp[r] = pr[k0 + r];
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const bool ok = iv && k0 + r < K;
+                            pv[mb][r] = ok ? expf(lv[mb][r]) : 0.0f;
+                            tv[mb][r] = ok ? pv[mb][r] * (lv[mb][r] - pp[r]) : 0.0f;
+                            tsum += tv[mb][r];
+                        }
                     }
                 }
-            } else {
+                if (fused) {
+                    float D = 0.0f;
+                    if (prev) {
+                        D = tsum + __shfl_xor(tsum, 16, 64);
+                        D = D + __shfl_xor(D, 32, 64);
+#pragma unroll
+                        for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) sacc[mb][r] += score_term(kind, pv[mb][r], tv[mb][r], D);
+                    }
+                    if (iv) {
+                        dacc[nb] += D;
+                        if (D_hi && q == 0) D_hi[((size_t)w * Hq + h) * Nb + i] = D;
+                    }
+                }
+            } else if (iv) {
                 for (int cg = 0; cg < K; cg += GK)
 #pragma unroll
                     for (int mb = 0; mb < KB; ++mb)
@@ -137,6 +201,29 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
             }
         }
     }
+    if (!fused) return;
+    // scores: sum over the 16 query lanes, then over the four waves in order
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = sacc[mb][r];
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            v += __shfl_xor(v, 4, 64);
+            v += __shfl_xor(v, 8, 64);
+            if (r16 == 0) sred[wave][16 * mb + 4 * q + r] = v;
+        }
+    if (q == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) dred[wave][16 * nb + r16] = dacc[nb];
+    }
+    __syncthreads();
+    const float invH = 1.0f / (float)Hq;
+    for (int k = threadIdx.x; k < K; k += 256)
+        score[(size_t)w * K + k] = (((sred[0][k] + sred[1][k]) + sred[2][k]) + sred[3][k]) * invH;
+    for (int i = threadIdx.x; i < Nb; i += 256)
+        D_i[(size_t)w * Nb + i] = (((dred[0][i] + dred[1][i]) + dred[2][i]) + dred[3][i]) * invH;
 }
 
 // proxy attention, fp32 path: one thread per (h, i), three passes over K
@@ -166,29 +253,51 @@ __global__ __launch_bounds__(256) void k_proxy_f32(const float* __restrict__ Q, 
 }
 
 // ---------------------------------------------------------------------------
-// drift: D_{h,i} = sum_k p (l - l'), D_i = mean_h, per-cluster score
-// One workgroup per window; every sum in a fixed order.
+// drift from stored distributions, one workgroup per window, one pass: a wave
+// takes a (head, query) row at a time, lane l the clusters l, l+64, ...; each
+// term is computed once, D by a wave reduction, the per-cluster scores
+// accumulated per lane and combined over the waves in order.
 // ---------------------------------------------------------------------------
+template <int KM>
 __global__ __launch_bounds__(256) void k_drift_kl(const float* __restrict__ cur, const float* __restrict__ prev,
                                                    int kind, float* __restrict__ D_hi, float* __restrict__ D_i,
                                                    float* __restrict__ score, int Hq, int Nb, int K)
 {
-    extern __shared__ float dsh[];  // Hq * Nb drift values
+    extern __shared__ float dsh[];  // Hq * Nb drift values, then 4 * K score partials
+    float* sp = dsh + Hq * Nb;
     const int w = blockIdx.x, lane = lane_id(), wave = threadIdx.x >> 6;
     const size_t base = (size_t)w * Hq * Nb * K;
+    float sacc[KM];
+#pragma unroll
+    for (int m = 0; m < KM; ++m) sacc[m] = 0.0f;
     for (int pr = wave; pr < Hq * Nb; pr += 4) {
         const float* lc = cur + base + (size_t)pr * K;
         const float* lp = prev + base + (size_t)pr * K;
+        float pv[KM], tv[KM];
         float part = 0.0f;
-        for (int k = lane; k < K; k += 64) {
-            const float l = lc[k];
-            part += expf(l) * (l - lp[k]);
+#pragma unroll
+        for (int m = 0; m < KM; ++m) {
+            const int k = lane + 64 * m;
+            pv[m] = tv[m] = 0.0f;
+            if (k < K) {
+                const float l = lc[k];
+                pv[m] = expf(l);
+                tv[m] = pv[m] * (l - lp[k]);
+            }
+            part += tv[m];
         }
         const float D = wave_sum(part);
+#pragma unroll
+        for (int m = 0; m < KM; ++m) sacc[m] += score_term(kind, pv[m], tv[m], D);
         if (lane == 0) {
             dsh[pr] = D;
             if (D_hi) D_hi[(size_t)w * Hq * Nb + pr] = D;
         }
+    }
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+        const int k = lane + 64 * m;
+        if (k < K) sp[wave * K + k] = sacc[m];
     }
     __syncthreads();
     const float invH = 1.0f / (float)Hq;
@@ -197,21 +306,8 @@ __global__ __launch_bounds__(256) void k_drift_kl(const float* __restrict__ cur,
         for (int h = 0; h < Hq; ++h) s += dsh[h * Nb + i];
         D_i[(size_t)w * Nb + i] = s * invH;
     }
-    for (int k = threadIdx.x; k < K; k += 256) {
-        float s = 0.0f;
-        for (int pr = 0; pr < Hq * Nb; ++pr) {
-            const float l = cur[base + (size_t)pr * K + k];
-            const float p = expf(l);
-            float t;
-            if (kind == PS_SCORE_ATTN_WEIGHTED) t = p * dsh[pr];
-            else {
-                t = p * (l - prev[base + (size_t)pr * K + k]);
-                if (kind == PS_SCORE_KL_SHARE_ABS) t = fabsf(t);
-            }
-            s += t;
-        }
-        score[(size_t)w * K + k] = s * invH;
-    }
+    for (int k = threadIdx.x; k < K; k += 256)
+        score[(size_t)w * K + k] = (((sp[k] + sp[K + k]) + sp[2 * K + k]) + sp[3 * K + k]) * invH;
 }
 
 __global__ void k_zero(float* __restrict__ p, size_t n)
@@ -315,36 +411,50 @@ __global__ __launch_bounds__(64) void k_topk(const float* __restrict__ score, in
 }
 
 template <int KB, int NBQ>
-void launch_proxy(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, hipStream_t st)
+void launch_proxy(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, const float* prev,
+                  int kind, int fused, float* D_hi, float* D_i, float* score, hipStream_t st)
 {
     PS_LAUNCH("k_proxy_bf16<KB, NBQ>", (k_proxy_bf16<KB, NBQ>), dim3(s->W), dim3(256), 0, st, (const uint16_t*)Q,
-                       (const uint16_t*)Ck, sigma, logp, s->Hq, s->Hkv, s->dh, s->Nb, s->K);
+              (const uint16_t*)Ck, sigma, logp, prev, kind, fused, D_hi, D_i, score, s->Hq, s->Hkv, s->dh, s->Nb,
+              s->K);
 }
 
 template <int KB>
-void launch_proxy_nb(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, hipStream_t st)
+void launch_proxy_nb(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, const float* prev,
+                     int kind, int fused, float* D_hi, float* D_i, float* score, hipStream_t st)
 {
     const int nbq = (s->Nb + 15) / 16;
-    if (nbq <= 1)      launch_proxy<KB, 1>(s, Q, Ck, sigma, logp, st);
-    else if (nbq <= 2) launch_proxy<KB, 2>(s, Q, Ck, sigma, logp, st);
-    else               launch_proxy<KB, 4>(s, Q, Ck, sigma, logp, st);
+    if (nbq <= 1)      launch_proxy<KB, 1>(s, Q, Ck, sigma, logp, prev, kind, fused, D_hi, D_i, score, st);
+    else if (nbq <= 2) launch_proxy<KB, 2>(s, Q, Ck, sigma, logp, prev, kind, fused, D_hi, D_i, score, st);
+    else               launch_proxy<KB, 4>(s, Q, Ck, sigma, logp, prev, kind, fused, D_hi, D_i, score, st);
 }
 
 ps_status check_drift_shape(const ps_shape* s)
 {
     if (!s) return PS_ERR_NULL;
     if (s->W < 0 || s->Hq < 1 || s->Nb < 1 || s->K < 1 || s->K > kMaxK) return PS_ERR_SHAPE;
-    if ((int64_t)s->Hq * s->Nb > 16384) return PS_ERR_SHAPE;
+    if ((int64_t)s->Hq * s->Nb + 4 * (int64_t)s->K > 16384) return PS_ERR_SHAPE;
     return PS_OK;
 }
 
-ps_status enqueue_drift(const ps_shape* s, const float* cur, const float* prev, ps_score kind, float* D_hi,
-                        float* D_i, float* score, hipStream_t st)
+template <int KM>
+void launch_drift(const ps_shape* s, const float* cur, const float* prev, ps_score kind, float* D_hi, float* D_i,
+                  float* score, hipStream_t st)
 {
-    const size_t shm = (size_t)s->Hq * s->Nb * sizeof(float);
-    PS_LAUNCH("k_drift_kl", k_drift_kl, dim3(s->W), dim3(256), shm, st, cur, prev, (int)kind, D_hi, D_i, score,
-                       s->Hq, s->Nb, s->K);
-    return PS_OK;
+    const size_t shm = ((size_t)s->Hq * s->Nb + 4 * (size_t)s->K) * sizeof(float);
+    PS_LAUNCH("k_drift_kl<KM>", (k_drift_kl<KM>), dim3(s->W), dim3(256), shm, st, cur, prev, (int)kind, D_hi, D_i,
+              score, s->Hq, s->Nb, s->K);
+}
+
+void enqueue_drift(const ps_shape* s, const float* cur, const float* prev, ps_score kind, float* D_hi, float* D_i,
+                   float* score, hipStream_t st)
+{
+    const int km = (s->K + 63) / 64;
+    if (km <= 1)      launch_drift<1>(s, cur, prev, kind, D_hi, D_i, score, st);
+    else if (km <= 2) launch_drift<2>(s, cur, prev, kind, D_hi, D_i, score, st);
+    else if (km <= 4) launch_drift<4>(s, cur, prev, kind, D_hi, D_i, score, st);
+    else if (km <= 8) launch_drift<8>(s, cur, prev, kind, D_hi, D_i, score, st);
+    else              launch_drift<16>(s, cur, prev, kind, D_hi, D_i, score, st);
 }
 
 void enqueue_zero(float* p, size_t n, hipStream_t st)
@@ -393,24 +503,30 @@ extern "C" ps_status ps_proxy_attn(const ps_shape* s, ps_dtype dtype, const void
     if (s->W == 0) return PS_OK;
     hipStream_t stm = (hipStream_t)stream;
     (void)hipGetLastError();
+    bool fused = false;
     if (dtype == PS_BF16) {
         const int kb = (s->K + 15) / 16;
-        if (kb <= 1)       launch_proxy_nb<1>(s, Q, Ck, softmax_scale, logp_cur, stm);
-        else if (kb <= 2)  launch_proxy_nb<2>(s, Q, Ck, softmax_scale, logp_cur, stm);
-        else if (kb <= 4)  launch_proxy_nb<4>(s, Q, Ck, softmax_scale, logp_cur, stm);
-        else if (kb <= 8)  launch_proxy_nb<8>(s, Q, Ck, softmax_scale, logp_cur, stm);
-        else               launch_proxy_nb<16>(s, Q, Ck, softmax_scale, logp_cur, stm);
+        fused = kb <= 16;  // one cluster group: drift in the epilogue
+        const int f = fused ? 1 : 0;
+        const int k = (int)kind;
+        if (kb <= 1)       launch_proxy_nb<1>(s, Q, Ck, softmax_scale, logp_cur, logp_prev, k, f, D_hi, D_i, score, stm);
+        else if (kb <= 2)  launch_proxy_nb<2>(s, Q, Ck, softmax_scale, logp_cur, logp_prev, k, f, D_hi, D_i, score, stm);
+        else if (kb <= 4)  launch_proxy_nb<4>(s, Q, Ck, softmax_scale, logp_cur, logp_prev, k, f, D_hi, D_i, score, stm);
+        else if (kb <= 8)  launch_proxy_nb<8>(s, Q, Ck, softmax_scale, logp_cur, logp_prev, k, f, D_hi, D_i, score, stm);
+        else               launch_proxy_nb<16>(s, Q, Ck, softmax_scale, logp_cur, logp_prev, k, f, D_hi, D_i, score, stm);
     } else {
         const int pairs = s->Hq * s->Nb;
         PS_LAUNCH("k_proxy_f32", k_proxy_f32, dim3((pairs + 255) / 256, s->W), dim3(256), 0, stm, (const float*)Q,
-                           (const float*)Ck, softmax_scale, logp_cur, s->Hq, s->Hkv, s->dh, s->Nb, s->K);
+                  (const float*)Ck, softmax_scale, logp_cur, s->Hq, s->Hkv, s->dh, s->Nb, s->K);
     }
-    if (logp_prev) {
-        enqueue_drift(s, logp_cur, logp_prev, kind, D_hi, D_i, score, stm);
-    } else {
-        enqueue_zero(D_i, (size_t)s->W * s->Nb, stm);
-        enqueue_zero(score, (size_t)s->W * s->K, stm);
-        enqueue_zero(D_hi, (size_t)s->W * s->Hq * s->Nb, stm);
+    if (!fused) {
+        if (logp_prev) {
+            enqueue_drift(s, logp_cur, logp_prev, kind, D_hi, D_i, score, stm);
+        } else {
+            enqueue_zero(D_i, (size_t)s->W * s->Nb, stm);
+            enqueue_zero(score, (size_t)s->W * s->K, stm);
+            enqueue_zero(D_hi, (size_t)s->W * s->Hq * s->Nb, stm);
+        }
     }
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
 }

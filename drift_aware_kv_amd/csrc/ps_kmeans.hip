@@ -147,7 +147,9 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
                                                       const uint16_t* __restrict__ Cb,
                                                       int32_t* __restrict__ assign,
                                                       float* __restrict__ row_norm, int N, int d,
-                                                      int K, int tiles, int nblocks, int want_norm)
+                                                      int K, int tiles, int nblocks, int first,
+                                                      int32_t* __restrict__ dirty,
+                                                      const int32_t* __restrict__ conv)
 {
     constexpr int DK = 64;                 // d elements per LDS stage
     constexpr int ROWB = DK * 2 + 16;      // padded LDS row stride (bytes): conflict-free reads
@@ -158,6 +160,7 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
 
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int w = L / tiles, tile = L - w * tiles;
+    if (!first && conv[w]) return;  // window at a fixed point: nothing can change
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const uint16_t* Hw = H + (size_t)w * N * d;
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
     const int nchunks = (d + DK - 1) / DK;
 
     for (int cg = 0; cg < K; cg += MROWS) {
-        const bool norm_pass = want_norm && cg == 0;
+        const bool norm_pass = first && cg == 0;
         floatx4 acc[KB][2];
 #pragma unroll
         for (int mb = 0; mb < KB; ++mb)
@@ -281,11 +284,21 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
             const float ov = __shfl_xor(bestv[nb], m, 64);
             const int oi = __shfl_xor(besti[nb], m, 64);
             if (ov > bestv[nb] || (ov == bestv[nb] && oi < besti[nb])) { bestv[nb] = ov; besti[nb] = oi; }
-            if (want_norm) ss[nb] += shfl_xor_d(ss[nb], m);
+            if (first) ss[nb] += shfl_xor_d(ss[nb], m);
         }
         if (q == 0 && tv[nb]) {
-            assign[(size_t)w * N + tok[nb]] = besti[nb];
-            if (want_norm) row_norm[(size_t)w * N + tok[nb]] = (float)sqrt(ss[nb]);
+            int32_t* ap = assign + (size_t)w * N + tok[nb];
+            if (first) {
+                row_norm[(size_t)w * N + tok[nb]] = (float)sqrt(ss[nb]);
+            } else {
+                // membership changed: both clusters must be recomputed
+                const int old = *ap;
+                if (old != besti[nb]) {
+                    if (old >= 0 && old < K) dirty[(size_t)w * K + old] = 1;
+                    dirty[(size_t)w * K + besti[nb]] = 1;
+                }
+            }
+            *ap = besti[nb];
         }
     }
 }
@@ -294,11 +307,13 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
 __global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ H, const float* __restrict__ C,
                                                      int32_t* __restrict__ assign,
                                                      float* __restrict__ row_norm, int W, int N, int d,
-                                                     int K, int want_norm)
+                                                     int K, int first, int32_t* __restrict__ dirty,
+                                                     const int32_t* __restrict__ conv)
 {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (row >= (int64_t)W * N) return;
     const int w = (int)(row / N);
+    if (!first && conv[w]) return;
     const float* h = H + (size_t)row * d;
     const float* Cw = C + (size_t)w * K * d;
     float bestv = -INFINITY;
@@ -308,8 +323,15 @@ __global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ H,
         for (int e = 0; e < d; ++e) s = fmaf(h[e], Cw[(size_t)k * d + e], s);
         if (s > bestv) { bestv = s; besti = k; }
     }
+    if (!first) {
+        const int old = assign[row];
+        if (old != besti) {
+            if (old >= 0 && old < K) dirty[(size_t)w * K + old] = 1;
+            dirty[(size_t)w * K + besti] = 1;
+        }
+    }
     assign[row] = besti;
-    if (want_norm) {
+    if (first) {
         double ss = 0.0;
         for (int e = 0; e < d; ++e) ss = fma((double)h[e], (double)h[e], ss);
         row_norm[row] = (float)sqrt(ss);
@@ -317,13 +339,31 @@ __global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ H,
 }
 
 // ---------------------------------------------------------------------------
-// bucket: stable counting sort of rows by cluster, one wave per window
+// bucket: stable counting sort of rows by cluster, one wave per window.
+// After the first iteration, a window none of whose clusters changed keeps its
+// member lists (they are a function of the unchanged assignment); with the
+// fixed-point exit enabled it is also marked converged, which makes every
+// later assignment pass of that window a no-op (the iteration would reproduce
+// exactly the same centres and assignments).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_bucket(const int32_t* __restrict__ assign, int32_t* __restrict__ perm,
-                                                int32_t* __restrict__ offs, int N, int K)
+                                                int32_t* __restrict__ offs, const int32_t* __restrict__ dirty,
+                                                int32_t* __restrict__ conv, int N, int K, int first,
+                                                int fixed_point_exit)
 {
     __shared__ int cur[kMaxK];
     const int w = blockIdx.x, lane = lane_id();
+    if (first) {
+        if (lane == 0) conv[w] = 0;
+    } else {
+        if (conv[w]) return;
+        bool any = false;
+        for (int k = lane; k < K; k += 64) any |= dirty[(size_t)w * K + k] != 0;
+        if (!__ballot(any)) {
+            if (fixed_point_exit && lane == 0) conv[w] = 1;
+            return;
+        }
+    }
     const int32_t* a = assign + (size_t)w * N;
     for (int k = lane; k < K; k += 64) cur[k] = 0;
     __syncthreads();
@@ -387,12 +427,14 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
                                                  const int32_t* __restrict__ perm,
                                                  const int32_t* __restrict__ offs, float* __restrict__ C,
                                                  uint16_t* __restrict__ Cb, int32_t* __restrict__ counts,
-                                                 double* __restrict__ nrm_out, int N, int d, int K,
-                                                 int nblocks)
+                                                 double* __restrict__ nrm_out, int32_t* __restrict__ dirty,
+                                                 int N, int d, int K, int nblocks, int all)
 {
     __shared__ double red[4];
     const int Lg = xcd_remap(blockIdx.x, nblocks);
     const int w = Lg / K, k = Lg - w * K;
+    // an unchanged member set gives a bit-identical sum: keep the centre
+    if (!all && !dirty[(size_t)w * K + k]) return;
     const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
     const int32_t* pm = perm + (size_t)w * N;
     const T* Hw = H + (size_t)w * N * d;
@@ -415,6 +457,10 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
             if (e < d) {
                 load8(Hw + (size_t)j0 * d + e, v0[c]);
                 load8(Hw + (size_t)j1 * d + e, v1[c]);
+            } else {
+                // past the row: contribute exact zeros (they enter ||S||)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v0[c][i] = v1[c][i] = 0.0f;
             }
         }
         if (n0 > 0.0f) {
@@ -461,6 +507,7 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
     if (threadIdx.x == 0) {
         counts[(size_t)w * K + k] = nk;
         nrm_out[(size_t)w * K + k] = nrm;
+        dirty[(size_t)w * K + k] = 0;
     }
     if (nk > 0 && nrm > 0.0) {
         float* c_out = C + ((size_t)w * K + k) * d;
@@ -519,6 +566,8 @@ struct KmWs {
     uint16_t* Cb;
     int32_t* perm;
     int32_t* offs;
+    int32_t* dirty;
+    int32_t* conv;
     double* nrm;
     double* fm;
     float* fn;
@@ -540,6 +589,8 @@ KmWs km_layout(const ps_shape* s, int dtype, void* base)
     L.Cb = dtype == PS_BF16 ? (uint16_t*)take(W * K * d * 2) : nullptr;
     L.perm = (int32_t*)take(W * N * 4);
     L.offs = (int32_t*)take(W * (K + 1) * 4);
+    L.dirty = (int32_t*)take(W * K * 4);
+    L.conv = (int32_t*)take(W * 4);
     L.nrm = (double*)take(W * K * 8);
     L.fm = (double*)take(W * N * 8);
     L.fn = (float*)take(W * N * 4);
@@ -549,21 +600,21 @@ KmWs km_layout(const ps_shape* s, int dtype, void* base)
 
 template <typename T, int CH>
 void launch_update(const ps_shape* s, const void* H, const float* rn, const KmWs& ws, float* C,
-                   int32_t* counts, hipStream_t st)
+                   int32_t* counts, int all, hipStream_t st)
 {
     const int nblocks = s->W * s->K;
     PS_LAUNCH("k_update<T, CH>", (k_update<T, CH>), dim3(nblocks), dim3(256), 0, st, (const T*)H, rn, ws.perm,
-                       ws.offs, C, ws.Cb, counts, ws.nrm, s->N, s->d, s->K, nblocks);
+                       ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, s->N, s->d, s->K, nblocks, all);
 }
 
 template <int KB>
 void launch_assign_bf16(const ps_shape* s, const void* H, const KmWs& ws, int32_t* assign, float* rn,
-                        int want_norm, hipStream_t st)
+                        int first, hipStream_t st)
 {
     const int tiles = (s->N + 127) / 128;
     const int nblocks = s->W * tiles;
     PS_LAUNCH("k_assign_bf16<KB>", (k_assign_bf16<KB>), dim3(nblocks), dim3(256), 0, st, (const uint16_t*)H, ws.Cb,
-                       assign, rn, s->N, s->d, s->K, tiles, nblocks, want_norm);
+                       assign, rn, s->N, s->d, s->K, tiles, nblocks, first, ws.dirty, ws.conv);
 }
 
 }  // namespace
@@ -579,7 +630,7 @@ extern "C" ps_status ps_workspace_size(const ps_shape* s, ps_dtype dtype, size_t
 }
 
 extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void* H, const void* Kr,
-                                   ps_init init, int32_t iters, float* C, int32_t* assign,
+                                   ps_init init, int32_t iters, uint32_t flags, float* C, int32_t* assign,
                                    int32_t* counts, float* row_norm, void* Ck, double* objective,
                                    void* ws, size_t ws_bytes, void* stream)
 {
@@ -592,6 +643,7 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
     if (Kr && (st = check_heads(s)) != PS_OK) return st;
     if (iters < 1) return PS_ERR_RANGE;
     if (init != PS_INIT_GIVEN && init != PS_INIT_STRIDED && init != PS_INIT_FARTHEST) return PS_ERR_RANGE;
+    if (flags & ~(uint32_t)PS_KMEANS_FIXED_POINT_EXIT) return PS_ERR_RANGE;
     if (s->d > 8192) return PS_ERR_SHAPE;  // update kernel: at most 4 chunks of 2048 per thread
     if (!aligned16(H) || !aligned16(C) || !aligned16(assign) || !aligned16(counts) ||
         !aligned16(row_norm) || (Kr && (!aligned16(Kr) || !aligned16(Ck))) ||
@@ -623,33 +675,38 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
     }
     const int CH = (d + 2047) / 2048;
     const int KBn = (K + 15) / 16;
+    // Iteration 0 assigns against the incoming centres and rebuilds every
+    // cluster (the rows themselves are new).  Later iterations mark the two
+    // clusters of every row that moves; only those are rebuilt.
+    const int fpx = (flags & PS_KMEANS_FIXED_POINT_EXIT) ? 1 : 0;
     for (int it = 0; it < iters; ++it) {
-        const int want_norm = it == 0;
+        const int first = it == 0;
         if (bf) {
-            if (KBn <= 1)      launch_assign_bf16<1>(s, H, L, assign, row_norm, want_norm, stm);
-            else if (KBn <= 2) launch_assign_bf16<2>(s, H, L, assign, row_norm, want_norm, stm);
-            else if (KBn <= 4) launch_assign_bf16<4>(s, H, L, assign, row_norm, want_norm, stm);
-            else if (KBn <= 8) launch_assign_bf16<8>(s, H, L, assign, row_norm, want_norm, stm);
-            else               launch_assign_bf16<16>(s, H, L, assign, row_norm, want_norm, stm);
+            if (KBn <= 1)      launch_assign_bf16<1>(s, H, L, assign, row_norm, first, stm);
+            else if (KBn <= 2) launch_assign_bf16<2>(s, H, L, assign, row_norm, first, stm);
+            else if (KBn <= 4) launch_assign_bf16<4>(s, H, L, assign, row_norm, first, stm);
+            else if (KBn <= 8) launch_assign_bf16<8>(s, H, L, assign, row_norm, first, stm);
+            else               launch_assign_bf16<16>(s, H, L, assign, row_norm, first, stm);
         } else {
             const int64_t rows = (int64_t)W * N;
             PS_LAUNCH("k_assign_f32", k_assign_f32, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stm,
-                               (const float*)H, C, assign, row_norm, W, N, d, K, want_norm);
+                      (const float*)H, C, assign, row_norm, W, N, d, K, first, L.dirty, L.conv);
         }
-        PS_LAUNCH("k_bucket", k_bucket, dim3(W), dim3(64), 0, stm, assign, L.perm, L.offs, N, K);
+        PS_LAUNCH("k_bucket", k_bucket, dim3(W), dim3(64), 0, stm, assign, L.perm, L.offs, L.dirty, L.conv, N, K,
+                  first, fpx);
         if (bf) {
             switch (CH) {
-            case 1: launch_update<uint16_t, 1>(s, H, row_norm, L, C, counts, stm); break;
-            case 2: launch_update<uint16_t, 2>(s, H, row_norm, L, C, counts, stm); break;
-            case 3: launch_update<uint16_t, 3>(s, H, row_norm, L, C, counts, stm); break;
-            default: launch_update<uint16_t, 4>(s, H, row_norm, L, C, counts, stm); break;
+            case 1: launch_update<uint16_t, 1>(s, H, row_norm, L, C, counts, first, stm); break;
+            case 2: launch_update<uint16_t, 2>(s, H, row_norm, L, C, counts, first, stm); break;
+            case 3: launch_update<uint16_t, 3>(s, H, row_norm, L, C, counts, first, stm); break;
+            default: launch_update<uint16_t, 4>(s, H, row_norm, L, C, counts, first, stm); break;
             }
         } else {
             switch (CH) {
-            case 1: launch_update<float, 1>(s, H, row_norm, L, C, counts, stm); break;
-            case 2: launch_update<float, 2>(s, H, row_norm, L, C, counts, stm); break;
-            case 3: launch_update<float, 3>(s, H, row_norm, L, C, counts, stm); break;
-            default: launch_update<float, 4>(s, H, row_norm, L, C, counts, stm); break;
+            case 1: launch_update<float, 1>(s, H, row_norm, L, C, counts, first, stm); break;
+            case 2: launch_update<float, 2>(s, H, row_norm, L, C, counts, first, stm); break;
+            case 3: launch_update<float, 3>(s, H, row_norm, L, C, counts, first, stm); break;
+            default: launch_update<float, 4>(s, H, row_norm, L, C, counts, first, stm); break;
             }
         }
     }

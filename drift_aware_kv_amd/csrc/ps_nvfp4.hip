@@ -13,6 +13,21 @@ using namespace ps;
 
 namespace {
 
+// Correctly rounded fp32 quotient a / b from an fp64 product with the fp64
+// reciprocal of b.  For fp32 a and b, a quotient that is not an fp32 number
+// lies at least 2^-49 (relative) from every fp32 rounding midpoint: with m a
+// midpoint (25 significant bits) a - m*b is a non-zero multiple of
+// 2^(e_m + e_b - 47), since a has at most 24 significant bits.  The product
+// a * RN64(1/b) is within 2^-52 of a / b, so its fp32 rounding is the
+// correctly rounded quotient.  Below the fp32 normal range the midpoints are
+// coarser than that argument covers, so such quotients take the division.
+__device__ __forceinline__ float div_by_recip(float a, double inv_b, float b)
+{
+    const double q = (double)a * inv_b;
+    if (q != 0.0 && fabs(q) < 0x1p-125) return a / b;
+    return (float)q;
+}
+
 // One wave per row.  Lane l holds 8-element chunks l, l+64, ...; a 16-element
 // NVFP4 block is the chunk pair (2m, 2m+1), i.e. lanes l and l^1.
 template <typename T, int CPL>
@@ -26,6 +41,7 @@ __global__ __launch_bounds__(256) void k_residual(const T* __restrict__ H, const
     const int lane = lane_id();
     const int w = (int)(row / N);
     const float n = row_norm[row];
+    const double inv_n = n > 0.0f ? 1.0 / (double)n : 0.0;
     int a = assign[row];
     if (a < 0 || a >= K) a = 0;
     const float* c = C + ((size_t)w * K + a) * d;
@@ -43,7 +59,7 @@ __global__ __launch_bounds__(256) void k_residual(const T* __restrict__ H, const
             load8(c + 8 * ch, cv);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float x = n > 0.0f ? hv[t] / n : 0.0f;
+                const float x = n > 0.0f ? div_by_recip(hv[t], inv_n, n) : 0.0f;
                 r[i][t] = x - cv[t];
                 const float m = fabsf(r[i][t]);
                 if (m > A) A = m;
@@ -85,8 +101,9 @@ __global__ __launch_bounds__(256) void k_residual(const T* __restrict__ H, const
             const float eff = e4m3_decode(sb) * g;
             uint32_t word = 0;
             if (eff != 0.0f) {
+                const double inv_eff = 1.0 / (double)eff;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) word |= e2m1_encode(r[i][t] / eff) << (4 * t);
+                for (int t = 0; t < 8; ++t) word |= e2m1_encode(div_by_recip(r[i][t], inv_eff, eff)) << (4 * t);
             }
             *reinterpret_cast<uint32_t*>(cr + 4 * ch) = word;
             if (!(ch & 1)) br[ch >> 1] = (uint8_t)sb;

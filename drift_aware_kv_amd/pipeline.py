@@ -41,6 +41,7 @@ class StepSpec:
     cap: int = None
     score_kind: int = PS_SCORE_KL_SHARE
     gather_rows: bool = True
+    kmeans_flags: int = 0
 
     @property
     def shape(self) -> Shape:
@@ -101,7 +102,7 @@ class DriftPath:
         init = {"strided": PS_INIT_STRIDED, "farthest": PS_INIT_FARTHEST}[sp.init0] if first \
             else PS_INIT_GIVEN
         ps_kmeans_fit(s, dt, H, Kr, init, sp.iters, self.C, self.assign, self.counts, self.row_norm,
-                      self.Ck, self.objective, self.ws, stream)
+                      self.Ck, self.objective, self.ws, stream, flags=sp.kmeans_flags)
         ps_residual_nvfp4(s, dt, H, self.row_norm, self.C, self.assign, self.codes, self.bscale,
                           self.rscale, stream)
         ps_proxy_attn(s, dt, Q, self.Ck, self.scale, self.logp_cur, None if first else self.logp_prev,

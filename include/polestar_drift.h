@@ -71,6 +71,12 @@ typedef enum {
     PS_SCORE_ATTN_WEIGHTED = 2
 } ps_score;
 
+/* ps_kmeans_fit flags.  PS_KMEANS_FIXED_POINT_EXIT: once an iteration moves
+ * no row of a window, every later iteration would reproduce the same centres
+ * and assignments exactly, so the remaining passes of that window are skipped;
+ * results are bit-identical to running all iterations. */
+typedef enum { PS_KMEANS_DEFAULT = 0, PS_KMEANS_FIXED_POINT_EXIT = 1 } ps_kmeans_flags;
+
 typedef struct {
     int32_t W;   /* windows                                    */
     int32_t N;   /* tokens per window (prefix + block + suffix) */
@@ -97,6 +103,7 @@ ps_status ps_workspace_size(const ps_shape* shape, ps_dtype dtype, size_t* bytes
  *   H        [W][N][d]        dtype  in   hidden states of the window
  *   Kr       [W][N][Hkv][dh]  dtype  in   key rows (nullable, with Ck)
  *   init, iters                      in   seeding; Lloyd iterations (>= 1)
+ *   flags                            in   ps_kmeans_flags (others: PS_ERR_RANGE)
  *   C        [W][K][d]        f32    in/out  unit centres (input read only
  *                                     for PS_INIT_GIVEN)
  *   assign   [W][N]           int32  out  cluster of each row, last iteration
@@ -111,9 +118,12 @@ ps_status ps_workspace_size(const ps_shape* shape, ps_dtype dtype, size_t* bytes
  * fp32 path; ties to the lowest k), then S_k = sum_{a_j=k} h_j / n_j in fp64
  * and c_k = S_k / ||S_k||; empty clusters keep their centre.  The returned C
  * is the last update, so each c_k is the normalised mean of its members.
+ * Clusters whose member set did not change since the previous iteration keep
+ * their centre without being re-summed (the sum would be bit-identical).
  */
 ps_status ps_kmeans_fit(const ps_shape* shape, ps_dtype dtype, const void* H, const void* Kr,
-                        ps_init init, int32_t iters, float* C, int32_t* assign, int32_t* counts,
+                        ps_init init, int32_t iters, uint32_t flags, float* C, int32_t* assign,
+                        int32_t* counts,
                         float* row_norm, void* Ck, double* objective, void* ws, size_t ws_bytes,
                         void* stream);
 

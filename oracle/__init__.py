@@ -65,13 +65,15 @@ def lib():
         L.pso_row_norms.argtypes = [SP, I, P, P]
         L.pso_kmeans_init.argtypes = [SP, I, P, I, P]
         L.pso_kmeans_fit.argtypes = [SP, I, P, P, I, I, P, P, P, P, P, P]
+        L.pso_kmeans_update.argtypes = [SP, I, P, P, P, P, P, P]
         L.pso_residual_nvfp4.argtypes = [SP, I, P, P, P, P, P, P, P]
         L.pso_proxy_attn.argtypes = [SP, I, P, P, ctypes.c_float, P, P, I, P, P, P]
         L.pso_drift_kl.argtypes = [SP, P, P, I, P, P, P]
         L.pso_topk_clusters.argtypes = [SP, P, ctypes.c_int32, P, P]
         L.pso_refresh_gather.argtypes = [SP, I, P, P, ctypes.c_int32, ctypes.c_int32, P, P,
                                          P, P, P, P, P, P, P, P, P, P]
-        for name in ("pso_row_norms", "pso_kmeans_init", "pso_kmeans_fit", "pso_residual_nvfp4",
+        for name in ("pso_row_norms", "pso_kmeans_init", "pso_kmeans_fit", "pso_kmeans_update",
+                     "pso_residual_nvfp4",
                      "pso_proxy_attn", "pso_drift_kl", "pso_topk_clusters", "pso_refresh_gather"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -146,6 +148,17 @@ def kmeans_fit(s: Shape, dtype, H, Kr, init, iters, C, Ck=None):
     _ok(lib().pso_kmeans_fit(ctypes.byref(_cshape(s)), dtype, _p(H), _p(Kr), init, iters, _p(C),
                              _p(assign), _p(counts), _p(rn), _p(Ck), _p(obj)), "pso_kmeans_fit")
     return dict(C=C, assign=assign, counts=counts, row_norm=rn, Ck=Ck, objective=obj)
+
+
+def kmeans_update(s: Shape, dtype, H, row_norm, assign, C):
+    """The update step alone from a given assignment; C (in/out) supplies the
+    centres that empty clusters keep."""
+    C = np.array(C, np.float32, copy=True)
+    counts = np.zeros((s.W, s.K), np.int32)
+    obj = np.zeros((s.W,), np.float64)
+    _ok(lib().pso_kmeans_update(ctypes.byref(_cshape(s)), dtype, _p(H), _p(row_norm), _p(assign),
+                                _p(C), _p(counts), _p(obj)), "pso_kmeans_update")
+    return dict(C=C, counts=counts, objective=obj)
 
 
 def residual_nvfp4(s: Shape, dtype, H, row_norm, C, assign):

@@ -236,6 +236,56 @@ int pso_kmeans_init(const pso_shape* s, int dtype, const void* H, int init, floa
     return 0;
 }
 
+/* The update step of one window: for every cluster, S_k = sum of the unit
+ * rows of its members (fp64, each added as fma(h, 1/n_j, S) in ascending j),
+ * c_k = S_k / ||S_k|| rounded to fp32; an empty cluster (or ||S_k|| = 0) keeps
+ * its centre.  Returns sum_k ||S_k||.  S is scratch of d doubles. */
+static double update_window(const pso_shape* s, int dtype, const void* H, int w, const float* rn,
+                            const int32_t* aw, float* Cw, int32_t* nw, double* S)
+{
+    const int N = s->N, d = s->d, K = s->K;
+    const size_t hb = (size_t)w * N * d;
+    double obj = 0.0;
+    for (int k = 0; k < K; ++k) {
+        int cnt = 0;
+        for (int e = 0; e < d; ++e) S[e] = 0.0;
+        for (int j = 0; j < N; ++j) {
+            if (aw[j] != k) continue;
+            ++cnt;
+            if (!(rn[j] > 0.0f)) continue;
+            const double inv = 1.0 / (double)rn[j];
+            for (int e = 0; e < d; ++e)
+                S[e] = fma((double)ld(H, dtype, hb + (size_t)j * d + e), inv, S[e]);
+        }
+        nw[k] = cnt;
+        double ss = 0.0;
+        for (int e = 0; e < d; ++e) ss += S[e] * S[e];
+        double nrm = sqrt(ss);
+        obj += nrm;
+        if (cnt > 0 && nrm > 0.0)
+            for (int e = 0; e < d; ++e) Cw[(size_t)k * d + e] = (float)(S[e] / nrm);
+    }
+    return obj;
+}
+
+int pso_kmeans_update(const pso_shape* s, int dtype, const void* H, const float* row_norm,
+                      const int32_t* assign, float* C, int32_t* counts, double* objective)
+{
+    if (!s || !H || !row_norm || !assign || !C || !counts) return ERR_NULL;
+    if (!check_dtype(dtype)) return ERR_DTYPE;
+    if (!check_cluster_shape(s)) return ERR_SHAPE;
+    for (size_t i = 0; i < (size_t)s->W * s->N; ++i)
+        if (assign[i] < 0 || assign[i] >= s->K) return ERR_RANGE;
+    double* S = (double*)malloc(sizeof(double) * (size_t)s->d);
+    for (int w = 0; w < s->W; ++w) {
+        double obj = update_window(s, dtype, H, w, row_norm + (size_t)w * s->N, assign + (size_t)w * s->N,
+                                   C + (size_t)w * s->K * s->d, counts + (size_t)w * s->K, S);
+        if (objective) objective[w] = obj;
+    }
+    free(S);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* O3/O4 spherical K-Means (Dhillon & Modha 2001) on the window's hidden
  * states, then the centroid keys (Polestar 2.A/window: clustering;
@@ -300,26 +350,7 @@ int pso_kmeans_fit(const pso_shape* s, int dtype, const void* H, const void* Kr,
                 aw[j] = best;
             }
             /* update */
-            obj = 0.0;
-            for (int k = 0; k < K; ++k) {
-                int cnt = 0;
-                for (int e = 0; e < d; ++e) S[e] = 0.0;
-                for (int j = 0; j < N; ++j) {
-                    if (aw[j] != k) continue;
-                    ++cnt;
-                    if (!(rn[j] > 0.0f)) continue;
-                    const double inv = 1.0 / (double)rn[j];
-                    for (int e = 0; e < d; ++e)
-                        S[e] = fma((double)ld(H, dtype, hb + (size_t)j * d + e), inv, S[e]);
-                }
-                nw[k] = cnt;
-                double ss = 0.0;
-                for (int e = 0; e < d; ++e) ss += S[e] * S[e];
-                double nrm = sqrt(ss);
-                obj += nrm;
-                if (cnt > 0 && nrm > 0.0)
-                    for (int e = 0; e < d; ++e) Cw[(size_t)k * d + e] = (float)(S[e] / nrm);
-            }
+            obj = update_window(s, dtype, H, w, rn, aw, Cw, nw, S);
         }
         if (objective) objective[w] = obj;
 

@@ -71,6 +71,10 @@ int pso_kmeans_fit(const pso_shape* s, int dtype, const void* H, const void* Kr,
                    int iters, float* C, int32_t* assign, int32_t* counts, float* row_norm,
                    void* Ck, double* objective);
 
+/* The update step alone, from a given assignment (all values in [0, K)). */
+int pso_kmeans_update(const pso_shape* s, int dtype, const void* H, const float* row_norm,
+                      const int32_t* assign, float* C, int32_t* counts, double* objective);
+
 int pso_residual_nvfp4(const pso_shape* s, int dtype, const void* H, const float* row_norm,
                        const float* C, const int32_t* assign, uint8_t* codes, uint8_t* bscale,
                        float* rscale);

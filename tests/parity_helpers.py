@@ -59,6 +59,21 @@ def assignment_mismatches(H, C_in, bf16, got, want, row_norm):
     return ties, real
 
 
+def check_centres_from_assignment(so, dtype, H, row_norm, assign, C_gpu, counts_gpu):
+    """The GPU's centres and counts must equal the oracle's update step run on
+    the GPU's own assignment (bit for bit: same fp64 operations in the same
+    order, up to the summation order of ||S||), and every non-empty centre
+    must be a unit vector."""
+    r = O.kmeans_update(so, dtype, H, row_norm, assign, C_gpu)
+    assert np.array_equal(counts_gpu, r["counts"]), "counts from the assignment"
+    diff = C_gpu.view(np.uint32) != r["C"].view(np.uint32)
+    assert close(C_gpu, r["C"], 1e-6, 1e-7), f"centres from the assignment: {max_rel(C_gpu, r['C'])}"
+    ne = counts_gpu > 0
+    nrm = np.linalg.norm(C_gpu.astype(np.float64), axis=-1)
+    assert np.all(np.abs(nrm[ne] - 1.0) < 1e-6), "non-empty centres must be unit vectors"
+    return int(diff.sum())
+
+
 def topk_equivalent(score, got, want):
     """Top-k lists equal, or differ only where the scores swapped are within
     TIE_TOPK of each other (same score multiset up to near-ties)."""

@@ -77,9 +77,9 @@ def test_workspace_size(L):
 
 
 def _fit(L, shape, dtype=1, init=1, iters=2, H=FAKE, ws=FAKE, ws_bytes=1 << 30, C=FAKE, Kr=None,
-         Ck=None):
-    return L.ps_kmeans_fit(ctypes.byref(shape), dtype, H, Kr, init, iters, C, FAKE, FAKE, FAKE, Ck,
-                           None, ws, ws_bytes, None)
+         Ck=None, flags=0):
+    return L.ps_kmeans_fit(ctypes.byref(shape), dtype, H, Kr, init, iters, flags, C, FAKE, FAKE, FAKE,
+                           Ck, None, ws, ws_bytes, None)
 
 
 def test_kmeans_fit_argument_checks(L):
@@ -95,6 +95,7 @@ def test_kmeans_fit_argument_checks(L):
     assert _fit(L, _shape(dh=12), Kr=FAKE, Ck=FAKE) == SHAPE         # dh % 8
     assert _fit(L, s, iters=0) == RANGE
     assert _fit(L, s, init=9) == RANGE
+    assert _fit(L, s, flags=2) == RANGE                     # unknown flag bit
     assert _fit(L, s, H=MISALIGNED) == ALIGN
     assert _fit(L, s, ws=None) == WORKSPACE
     assert _fit(L, s, ws_bytes=16) == WORKSPACE

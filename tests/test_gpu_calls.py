@@ -11,8 +11,8 @@ import pytest
 import torch
 
 import oracle as O
-from parity_helpers import (assignment_mismatches, bf16f, close, dev, host, max_rel,
-                            topk_equivalent)
+from parity_helpers import (assignment_mismatches, bf16f, check_centres_from_assignment, close, dev,
+                            host, max_rel, topk_equivalent)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +46,7 @@ KM_CASES = [
     ("k300-two-groups", 1, 600, 64, 300, 1, 32, True),
     ("tiny-f32", 2, 200, 64, 8, 1, 64, False),
     ("llada-row", 1, 256, 4096, 64, 32, 128, True),
+    ("dream-rows", 1, 512, 3584, 128, 4, 128, True),   # d not a multiple of 2048
     ("k1", 2, 130, 48, 1, 1, 16, True),
 ]
 
@@ -83,6 +84,8 @@ def test_kmeans_lockstep(P, case):
         r = O.kmeans_fit(so, odt, H, Kr, init, 1, C_in.copy(), Ck_in.copy())
         ga, gC, gn, gcnt, gCk, gobj = host(a), host(C), host(rn), host(cnt), host(Ck), host(obj)
         assert max_rel(gn, r["row_norm"]) <= 1.2e-7, "row norms"
+        # the update, stage-fed from the GPU's own assignment, whatever the ties
+        check_centres_from_assignment(so, odt, H, gn, ga, gC, gcnt)
         ties_it = 0
         for w in range(W):
             ties, real = assignment_mismatches(H[w], C_in[w], bf, ga[w], r["assign"][w],
@@ -100,6 +103,51 @@ def test_kmeans_lockstep(P, case):
             assert close(gobj, r["objective"], 1e-9, 1e-9)
         # the next iteration starts both sides from the GPU's centres (lockstep)
     say("  near-ties:", ties_total)
+
+
+ITER_CASES = [("ragged-bf16", 3, 300, 80, 37, True), ("llada-rows", 2, 1024, 4096, 64, True),
+              ("f32", 2, 256, 64, 8, False)]
+
+
+@pytest.mark.parametrize("case", ITER_CASES, ids=[c[0] for c in ITER_CASES])
+def test_iteration_paths_agree(P, case):
+    """One call of n iterations (later iterations re-sum only the clusters
+    whose members changed), n calls of one iteration (every cluster re-summed
+    each time), and n iterations with the fixed-point exit must give
+    bit-identical centres, assignments, counts, keys and objective."""
+    name, W, N, d, K, bf = case
+    say("iteration paths", name)
+    rng = np.random.default_rng(21)
+    dt = P.PS_BF16 if bf else P.PS_F32
+    H = rnd_bf16(rng, (W, N, d)) if bf else rng.standard_normal((W, N, d)).astype(np.float32)
+    Kr = rnd_bf16(rng, (W, N, 2, 16)) if bf else rng.standard_normal((W, N, 2, 16)).astype(np.float32)
+    s = P.Shape(W=W, N=N, d=d, Hq=2, Hkv=2, dh=16, Nb=1, K=K)
+    Hd, Krd = dev(H), dev(Kr)
+    et = torch.bfloat16 if bf else torch.float32
+    n = 6
+
+    def fresh():
+        return dict(C=torch.zeros(W, K, d, device="cuda"),
+                    a=torch.zeros(W, N, dtype=torch.int32, device="cuda"),
+                    cnt=torch.zeros(W, K, dtype=torch.int32, device="cuda"),
+                    rn=torch.zeros(W, N, device="cuda"), Ck=torch.zeros(W, K, 2, 16, dtype=et, device="cuda"),
+                    obj=torch.zeros(W, dtype=torch.float64, device="cuda"), ws=P.workspace(s, dt))
+
+    def run(st, init, iters, flags):
+        P.ps_kmeans_fit(s, dt, Hd, Krd, init, iters, st["C"], st["a"], st["cnt"], st["rn"], st["Ck"],
+                        st["obj"], st["ws"], flags=flags)
+
+    A, B, X = fresh(), fresh(), fresh()
+    run(A, P.PS_INIT_STRIDED, n, 0)
+    run(B, P.PS_INIT_STRIDED, 1, 0)
+    for _ in range(n - 1):
+        run(B, P.PS_INIT_GIVEN, 1, 0)
+    run(X, P.PS_INIT_STRIDED, n, P.PS_KMEANS_FIXED_POINT_EXIT)
+    torch.cuda.synchronize()
+    for key in ("C", "a", "cnt", "Ck", "obj", "rn"):
+        a, b, x = host(A[key]), host(B[key]), host(X[key])
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), key
+        assert np.array_equal(a.view(np.uint8), x.view(np.uint8)), key
 
 
 def test_kmeans_chained_planted_exact(P):

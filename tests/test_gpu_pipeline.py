@@ -18,8 +18,8 @@ import torch
 
 import oracle as O
 import synth
-from parity_helpers import (assignment_mismatches, bf16f, close, dev, host, max_rel,
-                            topk_equivalent)
+from parity_helpers import (assignment_mismatches, bf16f, check_centres_from_assignment, close, dev,
+                            host, max_rel, topk_equivalent)
 
 pytestmark = pytest.mark.gpu
 
@@ -188,6 +188,11 @@ def run_chained(P, cfg, steps, windows=None, W=None):
         for w in windows:
             say(f"  {cfg.name} step {t}: oracle window {w}")
             gs = gpu_snapshot(path, w, t)
+            # centres and counts of the final iteration from the GPU's own
+            # assignment, unit norm (independent of any near-tie)
+            check_centres_from_assignment(oshape(cfg), O.BF16 if cfg.bf16 else O.F32,
+                                          host_data[w]["H"], gs["row_norm"], gs["assign"], gs["C"],
+                                          gs["counts"])
             o = oracle_step(cfg, ost[w], host_data[w], t)
             if np.array_equal(gs["assign"], o["assign"]):
                 assert np.array_equal(gs["counts"], o["counts"])

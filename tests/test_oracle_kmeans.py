@@ -253,3 +253,27 @@ def test_argument_errors():
     s = O.Shape(W=1, N=8, d=16, K=2)
     with pytest.raises(O.OracleError):
         O.kmeans_fit(s, O.F32, H, None, O.INIT_STRIDED, 0, np.zeros((1, 2, 16), np.float32))
+
+
+def test_update_step_alone_matches_fit_and_member_means():
+    """pso_kmeans_update from an assignment gives the normalised member means,
+    and one fit iteration equals update(assign of that iteration)."""
+    rng = np.random.default_rng(16)
+    N, d, K = 300, 48, 6
+    H = O.f32_to_bf16(rng.standard_normal((1, N, d)).astype(np.float32))
+    s = O.Shape(W=1, N=N, d=d, K=K)
+    C0 = O.kmeans_init(s, O.BF16, H, O.INIT_STRIDED)
+    r = O.kmeans_fit(s, O.BF16, H, None, O.INIT_GIVEN, 1, C0.copy())
+    u = O.kmeans_update(s, O.BF16, H, r["row_norm"], r["assign"], C0)
+    assert np.array_equal(u["C"], r["C"]) and np.array_equal(u["counts"], r["counts"])
+    assert u["objective"][0] == r["objective"][0]
+    # arbitrary assignment with an empty cluster
+    a = rng.integers(0, K - 1, size=(1, N)).astype(np.int32)
+    u = O.kmeans_update(s, O.BF16, H, r["row_norm"], a, C0)
+    X = _unit(_bf16_to_f32(H[0]))
+    for k in range(K - 1):
+        m = X[a[0] == k].sum(0)
+        assert np.allclose(u["C"][0, k], m / np.linalg.norm(m), atol=1e-7)
+    assert np.array_equal(u["C"][0, K - 1], C0[0, K - 1]) and u["counts"][0, K - 1] == 0
+    with pytest.raises(O.OracleError):
+        O.kmeans_update(s, O.BF16, H, r["row_norm"], np.full((1, N), K, np.int32), C0)
