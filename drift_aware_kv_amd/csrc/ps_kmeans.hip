@@ -3,20 +3,35 @@
 // clustering; sparse updates), for gfx950.
 //
 // One Lloyd iteration over all W windows is three launches:
-//   assign  bf16 MFMA (16x16x32) scores of 128-row tiles against every centre,
-//           argmax in registers; the first iteration also writes the fp64
-//           row norms.  Centres are staged through LDS in 64-wide d-chunks.
+//   assign  bf16 MFMA (16x16x32) scores of token tiles against every centre,
+//           argmax in registers.  The first iteration of a call also writes
+//           the fp64 row norms; later ones mark the clusters whose member set
+//           changed.  The operand is the bf16 copy of the centres, made once
+//           per call and then kept by the update.
 //   bucket  stable counting sort of each window's rows by cluster (wave
 //           ballots), giving every cluster its ascending member list.
 //   update  one workgroup per (window, cluster): fp64 fused multiply-add of
 //           the member rows scaled by 1/n_j in ascending order, fp64 norm,
-//           fp32 centre plus its bf16 copy for the next assignment.
+//           fp32 centre plus its bf16 copy for the next assignment; after the
+//           first iteration only clusters whose member set changed run.
 // After the last iteration the keys kernel averages the member key rows.
 #include "ps_common.h"
 
 #include <math.h>
 
 using namespace ps;
+
+// Tile shape of the assignment kernel: 16-token blocks per wave for K <= 64
+// and for larger K, and the d-width of one LDS stage (multiple of 32).
+#ifndef PS_ASSIGN_NB_SMALLK
+#define PS_ASSIGN_NB_SMALLK 4
+#endif
+#ifndef PS_ASSIGN_NB_LARGEK
+#define PS_ASSIGN_NB_LARGEK 2
+#endif
+#ifndef PS_ASSIGN_DK
+#define PS_ASSIGN_DK 64
+#endif
 
 namespace {
 
@@ -126,73 +141,87 @@ __global__ __launch_bounds__(256) void k_init_farthest(const T* __restrict__ H, 
     }
 }
 
-// bf16 copy of the centres: the operand of the assignment step
+// bf16 copy of the incoming centres (the first assignment's operand): eight
+// elements per thread, two 16-byte loads and one 16-byte store
 __global__ __launch_bounds__(256) void k_centres_to_bf16(const float* __restrict__ C,
-                                                          uint16_t* __restrict__ Cb, size_t n)
+                                                          uint16_t* __restrict__ Cb, size_t n8)
 {
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
-        Cb[i] = (uint16_t)f32_to_bf16(C[i]);
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+        float v[8];
+        load8(C + 8 * i, v);
+        store8(Cb + 8 * i, v);
+    }
 }
 
 // ---------------------------------------------------------------------------
 // assignment, bf16: scores D[cluster][token] = Cb . H^T on MFMA 16x16x32
 // ---------------------------------------------------------------------------
-// Workgroup = 4 waves = 128 tokens of one window; wave = 32 tokens (two
-// 16-token N-blocks); the M dimension runs over up to 16*KB clusters per pass
-// (more passes when K > 16*KB).  MFMA operand layout (16x16x32 bf16): lane l
-// supplies row/column (l % 16) and reduction elements 8*(l/16)..+8; the
-// result element r of lane l is D[4*(l/16) + r][l % 16].
-template <int KB>
+// Workgroup = 4 waves; a wave owns NB 16-token blocks (16*NB tokens); the M
+// dimension runs over up to 16*KB clusters per pass (more passes when
+// K > 16*KB).  MFMA operand layout (16x16x32 bf16): lane l supplies
+// row/column (l % 16) and reduction elements 8*(l/16)..+8; the result element
+// r of lane l is D[4*(l/16) + r][l % 16].  Centres are staged through LDS in
+// 64-wide d-chunks (double-buffered, padded rows: conflict-free 16-byte
+// reads); each wave streams its token rows straight into registers one chunk
+// ahead (NB*2 16-byte loads per lane per chunk, each load covering 16 rows x
+// 64 contiguous bytes).  FIRST: the first iteration of a call, which also
+// writes the fp64 row norms and marks nothing; later iterations mark the old
+// and new cluster of every row that moves and skip windows at a fixed point.
+template <int KB, int NB, bool FIRST>
 __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict__ H,
                                                       const uint16_t* __restrict__ Cb,
                                                       int32_t* __restrict__ assign,
                                                       float* __restrict__ row_norm, int N, int d,
-                                                      int K, int tiles, int nblocks, int first,
+                                                      int K, int tiles, int nblocks,
                                                       int32_t* __restrict__ dirty,
                                                       const int32_t* __restrict__ conv)
 {
-    constexpr int DK = 64;                 // d elements per LDS stage
-    constexpr int ROWB = DK * 2 + 16;      // padded LDS row stride (bytes): conflict-free reads
+    constexpr int DK = PS_ASSIGN_DK;       // d elements per LDS stage
+    constexpr int NS = DK / 32;            // MFMA k-steps per stage
+    constexpr int ROWB = DK * 2 + 16;      // padded LDS row stride (bytes)
     constexpr int MROWS = 16 * KB;
     constexpr int NPIECE = MROWS * (DK / 8);        // 16-byte pieces per stage
-    constexpr int PIECES = (NPIECE + 255) / 256;      // per thread
+    constexpr int PIECES = (NPIECE + 255) / 256;    // per thread
+    constexpr int TPW = 16 * NB;                    // tokens per wave
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][MROWS * ROWB];
 
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int w = L / tiles, tile = L - w * tiles;
-    if (!first && conv[w]) return;  // window at a fixed point: nothing can change
+    if (!FIRST && conv[w]) return;  // window at a fixed point: nothing can change
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const uint16_t* Hw = H + (size_t)w * N * d;
     const uint16_t* Cw = Cb + (size_t)w * K * d;
 
-    int tok[2];
-    bool tv[2];
+    int tok[NB];
+    bool tv[NB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        tok[nb] = tile * 128 + wave * 32 + nb * 16 + r16;
+    for (int nb = 0; nb < NB; ++nb) {
+        tok[nb] = tile * 4 * TPW + wave * TPW + nb * 16 + r16;
         tv[nb] = tok[nb] < N;
     }
-    float bestv[2] = {-INFINITY, -INFINITY};
-    int besti[2] = {0, 0};
-    double ss[2] = {0.0, 0.0};
+    float bestv[NB];
+    int besti[NB];
+    double ss[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) { bestv[nb] = -INFINITY; besti[nb] = 0; ss[nb] = 0.0; }
     const int nchunks = (d + DK - 1) / DK;
 
     for (int cg = 0; cg < K; cg += MROWS) {
-        const bool norm_pass = first && cg == 0;
-        floatx4 acc[KB][2];
+        const bool norm_pass = FIRST && cg == 0;
+        floatx4 acc[KB][NB];
 #pragma unroll
         for (int mb = 0; mb < KB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
         uint4 cpre[PIECES];
-        uint4 hcur[2][2], hnext[2][2];
+        uint4 hcur[NB][NS], hnext[NB][NS];
         auto load_c = [&](int c0) {
 #pragma unroll
             for (int p = 0; p < PIECES; ++p) {
                 const int piece = p * 256 + threadIdx.x;
-                const int row = piece >> 3, col = (piece & 7) * 8;
+                const int row = piece / (DK / 8), col = (piece % (DK / 8)) * 8;
                 const int cl = cg + row, e = c0 + col;
                 cpre[p] = (piece < NPIECE && cl < K && e < d)
                               ? *reinterpret_cast<const uint4*>(Cw + (size_t)cl * d + e)
@@ -203,15 +232,15 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
 #pragma unroll
             for (int p = 0; p < PIECES; ++p) {
                 const int piece = p * 256 + threadIdx.x;
-                const int row = piece >> 3, col = (piece & 7) * 8;
+                const int row = piece / (DK / 8), col = (piece % (DK / 8)) * 8;
                 if (piece < NPIECE) *reinterpret_cast<uint4*>(&lds[buf][row * ROWB + col * 2]) = cpre[p];
             }
         };
-        auto load_h = [&](int c0, uint4 (&hr)[2][2]) {
+        auto load_h = [&](int c0, uint4 (&hr)[NB][NS]) {
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
+                for (int s = 0; s < NS; ++s) {
                     const int e = c0 + 32 * s + 8 * q;
                     hr[nb][s] = (tv[nb] && e < d)
                                     ? *reinterpret_cast<const uint4*>(Hw + (size_t)tok[nb] * d + e)
@@ -231,11 +260,11 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
             }
             const uint8_t* buf = lds[c & 1];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+            for (int s = 0; s < NS; ++s) {
+                if (norm_pass) {
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const uint4 hv = hcur[nb][s];
-                    if (norm_pass) {
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const uint4 hv = hcur[nb][s];
                         const uint32_t wv[4] = {hv.x, hv.y, hv.z, hv.w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
@@ -245,28 +274,30 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
                             ss[nb] = fma(hi, hi, ss[nb]);
                         }
                     }
-                    const bf16x8 b = __builtin_bit_cast(bf16x8, hv);
+                }
+                // one LDS read of a centre fragment feeds NB MFMAs
 #pragma unroll
-                    for (int mb = 0; mb < KB; ++mb) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                            buf + (16 * mb + r16) * ROWB + 64 * s + 16 * q);
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mb][nb], 0, 0, 0);
-                    }
+                for (int mb = 0; mb < KB; ++mb) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(buf + (16 * mb + r16) * ROWB + 64 * s + 16 * q);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            a, __builtin_bit_cast(bf16x8, hcur[nb][s]), acc[mb][nb], 0, 0, 0);
                 }
             }
             if (more) store_c((c + 1) & 1);
             __syncthreads();
             if (more) {
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) hcur[nb][s] = hnext[nb][s];
+                    for (int s = 0; s < NS; ++s) hcur[nb][s] = hnext[nb][s];
             }
         }
         // merge this cluster group's scores into the running argmax (ascending
         // cluster order within a lane; strict > keeps the lowest index)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int mb = 0; mb < KB; ++mb)
 #pragma unroll
@@ -278,17 +309,17 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
     }
     // combine the four lanes (q = 0..3) that hold the same token
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int m = 16; m <= 32; m <<= 1) {
             const float ov = __shfl_xor(bestv[nb], m, 64);
             const int oi = __shfl_xor(besti[nb], m, 64);
             if (ov > bestv[nb] || (ov == bestv[nb] && oi < besti[nb])) { bestv[nb] = ov; besti[nb] = oi; }
-            if (first) ss[nb] += shfl_xor_d(ss[nb], m);
+            if (FIRST) ss[nb] += shfl_xor_d(ss[nb], m);
         }
         if (q == 0 && tv[nb]) {
             int32_t* ap = assign + (size_t)w * N + tok[nb];
-            if (first) {
+            if (FIRST) {
                 row_norm[(size_t)w * N + tok[nb]] = (float)sqrt(ss[nb]);
             } else {
                 // membership changed: both clusters must be recomputed
@@ -525,7 +556,8 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
     }
 }
 
-// centroid keys: mean of the member key rows, fp64, rounded to fp32 then dtype
+// centroid keys: mean of the member key rows, fp64 in ascending member order,
+// rounded to fp32 then dtype.  Four members' loads are in flight at a time.
 template <typename T>
 __global__ __launch_bounds__(256) void k_keys(const T* __restrict__ Kr, const int32_t* __restrict__ perm,
                                                const int32_t* __restrict__ offs, T* __restrict__ Ck,
@@ -539,7 +571,17 @@ __global__ __launch_bounds__(256) void k_keys(const T* __restrict__ Kr, const in
     const T* Kw = Kr + (size_t)w * N * KV;
     for (int e = threadIdx.x * 8; e < KV; e += 256 * 8) {
         double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int m = beg; m < end; ++m) {
+        int m = beg;
+        for (; m + 4 <= end; m += 4) {
+            float v[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) load8(Kw + (size_t)pm[m + u] * KV + e, v[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += (double)v[u][i];
+        }
+        for (; m < end; ++m) {
             float v[8];
             load8(Kw + (size_t)pm[m] * KV + e, v);
 #pragma unroll
@@ -607,14 +649,18 @@ void launch_update(const ps_shape* s, const void* H, const float* rn, const KmWs
                        ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, s->N, s->d, s->K, nblocks, all);
 }
 
-template <int KB>
-void launch_assign_bf16(const ps_shape* s, const void* H, const KmWs& ws, int32_t* assign, float* rn,
-                        int first, hipStream_t st)
+template <int KB, int NB>
+void launch_assign_bf16(const ps_shape* s, const void* H, const float* C, const KmWs& ws, int32_t* assign,
+                        float* rn, int first, hipStream_t st)
 {
-    const int tiles = (s->N + 127) / 128;
+    const int tiles = (s->N + 64 * NB - 1) / (64 * NB);
     const int nblocks = s->W * tiles;
-    PS_LAUNCH("k_assign_bf16<KB>", (k_assign_bf16<KB>), dim3(nblocks), dim3(256), 0, st, (const uint16_t*)H, ws.Cb,
-                       assign, rn, s->N, s->d, s->K, tiles, nblocks, first, ws.dirty, ws.conv);
+    if (first)
+        PS_LAUNCH("k_assign_bf16<KB, NB, true>", (k_assign_bf16<KB, NB, true>), dim3(nblocks), dim3(256), 0, st,
+                  (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
+    else
+        PS_LAUNCH("k_assign_bf16<KB, NB, false>", (k_assign_bf16<KB, NB, false>), dim3(nblocks), dim3(256), 0, st,
+                  (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
 }
 
 }  // namespace
@@ -669,9 +715,9 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
         else    PS_LAUNCH("k_init_farthest<float>", k_init_farthest<float>, dim3(W), dim3(256), shm, stm, (const float*)H, C, L.fm, L.fn, N, d, K);
     }
     if (bf) {
-        const size_t n = (size_t)W * K * d;
-        const int blocks = (int)std::min<size_t>((n + 255) / 256, 65536);
-        PS_LAUNCH("k_centres_to_bf16", k_centres_to_bf16, dim3(blocks), dim3(256), 0, stm, C, L.Cb, n);
+        const size_t n8 = (size_t)W * K * d / 8;
+        const int blocks = (int)std::min<size_t>((n8 + 255) / 256, 8192);
+        PS_LAUNCH("k_centres_to_bf16", k_centres_to_bf16, dim3(blocks), dim3(256), 0, stm, C, L.Cb, n8);
     }
     const int CH = (d + 2047) / 2048;
     const int KBn = (K + 15) / 16;
@@ -682,11 +728,11 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
     for (int it = 0; it < iters; ++it) {
         const int first = it == 0;
         if (bf) {
-            if (KBn <= 1)      launch_assign_bf16<1>(s, H, L, assign, row_norm, first, stm);
-            else if (KBn <= 2) launch_assign_bf16<2>(s, H, L, assign, row_norm, first, stm);
-            else if (KBn <= 4) launch_assign_bf16<4>(s, H, L, assign, row_norm, first, stm);
-            else if (KBn <= 8) launch_assign_bf16<8>(s, H, L, assign, row_norm, first, stm);
-            else               launch_assign_bf16<16>(s, H, L, assign, row_norm, first, stm);
+            if (KBn <= 1)      launch_assign_bf16<1, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
+            else if (KBn <= 2) launch_assign_bf16<2, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
+            else if (KBn <= 4) launch_assign_bf16<4, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
+            else if (KBn <= 8) launch_assign_bf16<8, PS_ASSIGN_NB_LARGEK>(s, H, C, L, assign, row_norm, first, stm);
+            else               launch_assign_bf16<16, PS_ASSIGN_NB_LARGEK>(s, H, C, L, assign, row_norm, first, stm);
         } else {
             const int64_t rows = (int64_t)W * N;
             PS_LAUNCH("k_assign_f32", k_assign_f32, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stm,

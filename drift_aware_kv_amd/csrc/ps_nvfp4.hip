@@ -4,112 +4,188 @@
 // the selected clusters (2.A, sparse updates; 2.C, only the selected clusters
 // are fetched), for gfx950.
 //
-// Both kernels are bandwidth bound: one wave per row, 16-byte coalesced
-// loads, E4M3/E2M1 rounding in integer/fp32 arithmetic (every fp32 step is one
-// correctly rounded operation, matching the stated convention bit for bit).
+// Both kernels are bandwidth bound: one workgroup per row, 16-byte coalesced
+// loads all issued before use, E4M3/E2M1 rounding in integer/fp32 arithmetic
+// (every fp32 step is one correctly rounded operation, matching the stated
+// convention bit for bit).
 #include "ps_common.h"
 
 using namespace ps;
 
 namespace {
 
-// Correctly rounded fp32 quotient a / b from an fp64 product with the fp64
-// reciprocal of b.  For fp32 a and b, a quotient that is not an fp32 number
-// lies at least 2^-49 (relative) from every fp32 rounding midpoint: with m a
-// midpoint (25 significant bits) a - m*b is a non-zero multiple of
-// 2^(e_m + e_b - 47), since a has at most 24 significant bits.  The product
-// a * RN64(1/b) is within 2^-52 of a / b, so its fp32 rounding is the
-// correctly rounded quotient.  Below the fp32 normal range the midpoints are
-// coarser than that argument covers, so such quotients take the division.
-__device__ __forceinline__ float div_by_recip(float a, double inv_b, float b)
+// Quotients on the fast path: for fp32 a and b, the fp32 rounding of
+// a * RN64(1/b) equals the correctly rounded fp32 quotient a / b whenever that
+// quotient is zero or at least 2^-125 in magnitude.  A quotient that is not an
+// fp32 number lies at least 2^-49 (relative) from every fp32 rounding
+// midpoint (with m a midpoint of 25 significant bits, a - m*b is a non-zero
+// multiple of 2^(e_m + e_b - 47), since a has at most 24 significant bits),
+// while the fp64 product is within 2^-52 of a / b.  Below the normal range the
+// midpoints are coarser than that argument covers; such a row is redone with
+// divisions (`exact`).  A quotient a / b is below 2^-125 exactly when
+// 0 < |a| < 2^-125 * b, which is what the fast path tests.
+//
+// E2M1 rounding on the fast path uses gfx950's fp32 -> fp4 conversion with
+// scale 1.0: checked exhaustively over every finite fp32 input, it returns the
+// nearest-even, saturating E2M1 code of the convention except that a negative
+// input rounding to zero comes back as -0 (nibble 0x8); `plus_zero` clears
+// those signs.  Non-finite inputs are sent to the exact path.
+__device__ __forceinline__ uint32_t plus_zero(uint32_t w)
 {
-    const double q = (double)a * inv_b;
-    if (q != 0.0 && fabs(q) < 0x1p-125) return a / b;
-    return (float)q;
+    const uint32_t m = w & 0x77777777u;                              // magnitudes
+    const uint32_t nz = (m | (m >> 1) | (m >> 2)) & 0x11111111u;     // magnitude != 0
+    return m | (w & (nz << 3));
 }
 
-// One wave per row.  Lane l holds 8-element chunks l, l+64, ...; a 16-element
-// NVFP4 block is the chunk pair (2m, 2m+1), i.e. lanes l and l^1.
-template <typename T, int CPL>
-__global__ __launch_bounds__(256) void k_residual(const T* __restrict__ H, const float* __restrict__ row_norm,
+// NVFP4 coding of one row by one workgroup of TPR threads (one or four
+// waves).  Thread i holds 8-element chunks i, i+TPR, ...; a 16-element block
+// is the chunk pair (2m, 2m+1), i.e. threads i and i^1 of one wave.  All of a
+// thread's loads are issued before any use.  With exact = false the quotients
+// are fp64 products and E2M1 uses the hardware conversion; the function
+// returns false without writing anything if any quotient of the row is tiny
+// or any value is non-finite (decided by a workgroup vote).
+template <typename T, int TPR, int CPL, bool exact>
+__device__ __forceinline__ bool residual_row(const T* __restrict__ h, const float* __restrict__ c, float n,
+                                             uint8_t* __restrict__ cr, uint8_t* __restrict__ br,
+                                             float* __restrict__ rs, int d, float* red)
+{
+    constexpr int NW = TPR / 64;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int nch = d >> 3;
+    const bool full = nch == TPR * CPL;          // every chunk of every thread is in the row
+    const bool pos_n = n > 0.0f;                 // row-uniform
+    const double inv_n = pos_n ? 1.0 / (double)n : 0.0;
+    const float t1 = n * 0x1p-125f;              // |h| below this: tiny quotient
+    bool bad = false;
+    // chunks past the row read the last chunk again (always in bounds) and
+    // are masked to zero; bf16 chunks stay packed until used
+    constexpr bool packed = sizeof(T) == 2;
+    uint4 hq[CPL][packed ? 1 : 2];
+    float r[CPL][8];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int ch = min(tid + TPR * i, nch - 1);
+        const uint4* hp = reinterpret_cast<const uint4*>(h + 8 * ch);
+        hq[i][0] = hp[0];
+        if (!packed) hq[i][packed ? 0 : 1] = hp[1];
+        load8(c + 8 * ch, r[i]);
+    }
+    float A = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const bool valid = full || tid + TPR * i < nch;
+        float hv[8];
+        if (packed) {
+            const uint32_t w4[4] = {hq[i][0].x, hq[i][0].y, hq[i][0].z, hq[i][0].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                hv[2 * t] = __uint_as_float(w4[t] << 16);
+                hv[2 * t + 1] = __uint_as_float(w4[t] & 0xffff0000u);
+            }
+        } else {
+            const uint4 a = hq[i][0], b = hq[i][packed ? 0 : 1];
+            const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) hv[t] = __uint_as_float(w8[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float x = 0.0f;
+            if (pos_n) {
+                if (exact) {
+                    x = hv[t] / n;
+                } else {
+                    x = (float)((double)hv[t] * inv_n);
+                    bad |= (fabsf(hv[t]) < t1) & (hv[t] != 0.0f);
+                }
+            }
+            r[i][t] = valid ? x - r[i][t] : 0.0f;
+            A = fmaxf(A, fabsf(r[i][t]));
+        }
+    }
+    A = wave_max(A);
+    if (NW > 1) {
+        if ((tid & 63) == 0) red[wave] = A;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NW; ++q) A = fmaxf(A, red[q]);
+    }
+    const bool zero_row = !(A > 0.0f);
+    const float g = A / 2688.0f;
+    uint32_t words[CPL], scales[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        float Ab = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) Ab = fmaxf(Ab, fabsf(r[i][t]));
+        Ab = fmaxf(Ab, __shfl_xor(Ab, 1, 64));
+        uint32_t word = 0, sb = 0;
+        if (!zero_row) {
+            sb = e4m3_encode((Ab / 6.0f) / g);
+            const float eff = e4m3_decode(sb) * g;
+            if (eff != 0.0f) {
+                if (exact) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) word |= e2m1_encode(r[i][t] / eff) << (4 * t);
+                } else {
+                    const double inv_eff = 1.0 / (double)eff;
+                    const float t2 = eff * 0x1p-125f, big = eff * 8.0f;
+                    float v[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const float a = fabsf(r[i][t]);
+                        bad |= ((a < t2) & (r[i][t] != 0.0f)) | !(a <= big);
+                        v[t] = (float)((double)r[i][t] * inv_eff);
+                    }
+                    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], 1.0f, 0);
+                    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], 1.0f, 1);
+                    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], 1.0f, 2);
+                    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], 1.0f, 3);
+                    word = plus_zero(word);
+                }
+            }
+        }
+        words[i] = word;
+        scales[i] = sb;
+    }
+    if (!exact) {
+        const bool any_bad = NW > 1 ? __syncthreads_or(bad) != 0 : __any(bad) != 0;
+        if (any_bad) return false;
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int ch = tid + TPR * i;
+        if (ch < nch) {
+            *reinterpret_cast<uint32_t*>(cr + 4 * ch) = words[i];
+            if (!(ch & 1)) br[ch >> 1] = (uint8_t)scales[i];
+        }
+    }
+    if (tid == 0) *rs = zero_row ? 0.0f : g;
+    return true;
+}
+
+// One workgroup per row; consecutive rows (one window's, sharing its centres)
+// stay on one XCD.
+template <typename T, int TPR, int CPL>
+__global__ __launch_bounds__(TPR) void k_residual(const T* __restrict__ H, const float* __restrict__ row_norm,
                                                    const float* __restrict__ C, const int32_t* __restrict__ assign,
                                                    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscale,
-                                                   float* __restrict__ rscale, int64_t rows, int N, int d, int K)
+                                                   float* __restrict__ rscale, int N, int d, int K)
 {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;  // uniform per wave
-    const int lane = lane_id();
+    __shared__ float red[TPR / 64];
+    const int64_t row = xcd_remap(blockIdx.x, gridDim.x);
     const int w = (int)(row / N);
-    const float n = row_norm[row];
-    const double inv_n = n > 0.0f ? 1.0 / (double)n : 0.0;
     int a = assign[row];
     if (a < 0 || a >= K) a = 0;
     const float* c = C + ((size_t)w * K + a) * d;
     const T* h = H + (size_t)row * d;
-    const int nch = d >> 3;
-
-    float r[CPL][8];
-    float A = 0.0f;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int ch = lane + 64 * i;
-        if (ch < nch) {
-            float hv[8], cv[8];
-            load8(h + 8 * ch, hv);
-            load8(c + 8 * ch, cv);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float x = n > 0.0f ? div_by_recip(hv[t], inv_n, n) : 0.0f;
-                r[i][t] = x - cv[t];
-                const float m = fabsf(r[i][t]);
-                if (m > A) A = m;
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) r[i][t] = 0.0f;
-        }
-    }
-    A = wave_max(A);
     uint8_t* cr = codes + (size_t)row * (d >> 1);
     uint8_t* br = bscale + (size_t)row * (d >> 4);
-    if (!(A > 0.0f)) {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int ch = lane + 64 * i;
-            if (ch < nch) {
-                *reinterpret_cast<uint32_t*>(cr + 4 * ch) = 0u;
-                if (!(ch & 1)) br[ch >> 1] = 0;
-            }
-        }
-        if (lane == 0) rscale[row] = 0.0f;
-        return;
+    const float n = row_norm[row];
+    if (!residual_row<T, TPR, CPL, false>(h, c, n, cr, br, rscale + row, d, red)) {
+        __syncthreads();  // red[] is reused
+        residual_row<T, TPR, CPL, true>(h, c, n, cr, br, rscale + row, d, red);
     }
-    const float g = A / 2688.0f;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int ch = lane + 64 * i;
-        float Ab = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float m = fabsf(r[i][t]);
-            if (m > Ab) Ab = m;
-        }
-        Ab = fmaxf(Ab, __shfl_xor(Ab, 1, 64));
-        if (ch < nch) {
-            const float t6 = Ab / 6.0f;
-            const uint32_t sb = e4m3_encode(t6 / g);
-            const float eff = e4m3_decode(sb) * g;
-            uint32_t word = 0;
-            if (eff != 0.0f) {
-                const double inv_eff = 1.0 / (double)eff;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) word |= e2m1_encode(div_by_recip(r[i][t], inv_eff, eff)) << (4 * t);
-            }
-            *reinterpret_cast<uint32_t*>(cr + 4 * ch) = word;
-            if (!(ch & 1)) br[ch >> 1] = (uint8_t)sb;
-        }
-    }
-    if (lane == 0) rscale[row] = g;
 }
 
 // stable compaction of the members of the selected clusters, one wave per window
@@ -198,25 +274,25 @@ __global__ __launch_bounds__(256) void k_gather_rows(const int32_t* __restrict__
     }
 }
 
-template <typename T, int CPL>
+template <typename T, int TPR, int CPL>
 void launch_residual(const ps_shape* s, const void* H, const float* rn, const float* C, const int32_t* a,
                      uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t st)
 {
     const int64_t rows = (int64_t)s->W * s->N;
-    PS_LAUNCH("k_residual<T, CPL>", (k_residual<T, CPL>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
-                       (const T*)H, rn, C, a, codes, bscale, rscale, rows, s->N, s->d, s->K);
+    PS_LAUNCH("k_residual<T, TPR, CPL>", (k_residual<T, TPR, CPL>), dim3((unsigned)rows), dim3(TPR), 0, st,
+              (const T*)H, rn, C, a, codes, bscale, rscale, s->N, s->d, s->K);
 }
 
+// rows of at most 512 elements: one wave per row; longer rows: four waves
 template <typename T>
 void dispatch_residual(const ps_shape* s, const void* H, const float* rn, const float* C, const int32_t* a,
                        uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t st)
 {
-    const int cpl = (s->d / 8 + 63) / 64;
-    if (cpl <= 1)      launch_residual<T, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else if (cpl <= 2) launch_residual<T, 2>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else if (cpl <= 4) launch_residual<T, 4>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else if (cpl <= 8) launch_residual<T, 8>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else               launch_residual<T, 16>(s, H, rn, C, a, codes, bscale, rscale, st);
+    const int nch = s->d / 8;
+    if (nch <= 64)        launch_residual<T, 64, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
+    else if (nch <= 256)  launch_residual<T, 256, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
+    else if (nch <= 512)  launch_residual<T, 256, 2>(s, H, rn, C, a, codes, bscale, rscale, st);
+    else                  launch_residual<T, 256, 4>(s, H, rn, C, a, codes, bscale, rscale, st);
 }
 
 }  // namespace

@@ -209,11 +209,14 @@ def test_residual_bit_exact(P, case):
     H32 = (rng.standard_normal((W, N, d)) * np.exp(rng.uniform(-4, 4, (W, N, 1)))).astype(np.float32)
     H32[0, 1] = 0.0                                   # zero row
     H32[0, 2, 16:48] *= 1e-6                          # blocks far below the row max
+    H32[0, 5] = 1e-40                                 # subnormal unit-row entries: the
+    H32[0, 5, 0] = 1.0                                # coder's exact-division path
     H = O.f32_to_bf16(H32) if bf else H32
     Hf = bf16f(H) if bf else H
     rn = np.sqrt((Hf.astype(np.float64) ** 2).sum(-1)).astype(np.float32)
     C = rng.standard_normal((W, K, d)).astype(np.float32)
     C /= np.linalg.norm(C, axis=-1, keepdims=True)
+    C[0, 1, 7] = np.nan                                 # non-finite residuals: exact path
     assign = rng.integers(0, K, (W, N)).astype(np.int32)
     assign[0, 3] = -5                                   # out of range reads cluster 0
     # a row whose residual is exactly zero: h = c * n with n = 1 exactly representable
