@@ -72,7 +72,10 @@ def lib():
         L.pso_topk_clusters.argtypes = [SP, P, ctypes.c_int32, P, P]
         L.pso_refresh_gather.argtypes = [SP, I, P, P, ctypes.c_int32, ctypes.c_int32, P, P,
                                          P, P, P, P, P, P, P, P, P, P]
-        for name in ("pso_row_norms", "pso_kmeans_init", "pso_kmeans_fit", "pso_kmeans_update",
+        F = ctypes.c_float
+        L.pso_commit_block.argtypes = [SP, P, P, ctypes.c_int32, F, F, P, P, P, P]
+        L.pso_commit_suffix.argtypes = [SP, P, P, ctypes.c_int32, ctypes.c_int32, P, F, P, P]
+        for name in ("pso_commit_block", "pso_commit_suffix", "pso_row_norms", "pso_kmeans_init", "pso_kmeans_fit", "pso_kmeans_update",
                      "pso_residual_nvfp4",
                      "pso_proxy_attn", "pso_drift_kl", "pso_topk_clusters", "pso_refresh_gather"):
             getattr(L, name).restype = ctypes.c_int
@@ -213,3 +216,26 @@ def refresh_gather(s: Shape, dtype, assign, idx, k, cap, codes=None, bscale=None
                                  _p(row_norm), _p(H_hat), _p(Kc), _p(Vc), _p(K_out), _p(V_out)),
         "pso_refresh_gather")
     return dict(pos=pos, count=count, H_hat=H_hat, K_out=K_out, V_out=V_out)
+
+
+# ---- Polestar-Commit -------------------------------------------------------
+def commit_block(s: Shape, D_i, conf, block_start, alpha, tau_s, hist_sum, hist_n):
+    """Current-block commitment.  hist_sum [W][Nb] f64 and hist_n [W] i32 are
+    advanced in place; returns commit [W][Nb] u8 (bit 0 drift rule, bit 1
+    confidence rule) and delta [W][Nb] f32."""
+    assert hist_sum.dtype == np.float64 and hist_n.dtype == np.int32
+    commit = np.zeros((s.W, s.Nb), np.uint8)
+    delta = np.zeros((s.W, s.Nb), np.float32)
+    _ok(lib().pso_commit_block(ctypes.byref(_cshape(s)), _p(D_i), _p(conf), block_start,
+                               alpha, tau_s, _p(hist_sum), _p(hist_n), _p(commit), _p(delta)),
+        "pso_commit_block")
+    return dict(commit=commit, delta=delta)
+
+
+def commit_suffix(s: Shape, assign, idx, k, block_start, conf, tau_s):
+    """Suffix-block commitment: flag [W] u8 and commit [W][N] u8."""
+    flag = np.zeros((s.W,), np.uint8)
+    commit = np.zeros((s.W, s.N), np.uint8)
+    _ok(lib().pso_commit_suffix(ctypes.byref(_cshape(s)), _p(assign), _p(idx), k, block_start,
+                                _p(conf), tau_s, _p(flag), _p(commit)), "pso_commit_suffix")
+    return dict(flag=flag, commit=commit)

@@ -642,3 +642,89 @@ int pso_refresh_gather(const pso_shape* s, int dtype, const int32_t* assign, con
     free(sel);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* O10 current-block commitment (Polestar 2.B/current).  The drift delta of a
+ * block row is its drift now minus the mean of its earlier drifts; the row is
+ * committed when that delta exceeds the confidence-conditioned threshold
+ * alpha * (tau_s - c)^2, or, as under the plain static rule, when c >= tau_s.
+ * Readings: the history mean covers the earlier steps only (not the current
+ * one), a row with no history yet cannot fire the drift rule, and a window
+ * whose count is 0 starts a fresh history (its stored sums are ignored).  Every
+ * operation on the drift is one IEEE fp64 operation in the order written.   */
+/* ------------------------------------------------------------------------- */
+int pso_commit_block(const pso_shape* s, const float* D_i, const float* conf, int32_t block_start,
+                     float alpha, float tau_s, double* hist_sum, int32_t* hist_n,
+                     uint8_t* commit, float* delta)
+{
+    if (!s || !D_i || !conf || !hist_sum || !hist_n || !commit) return ERR_NULL;
+    if (s->W < 0 || s->N < 1 || s->Nb < 0 || s->Nb > s->N) return ERR_SHAPE;
+    if (block_start < 0 || block_start > s->N - s->Nb) return ERR_RANGE;
+    if (!isfinite(alpha) || alpha < 0.0f || !isfinite(tau_s)) return ERR_RANGE;
+    const int N = s->N, Nb = s->Nb;
+    for (int w = 0; w < s->W; ++w) {
+        const int32_t n = hist_n[w] > 0 ? hist_n[w] : 0;
+        for (int i = 0; i < Nb; ++i) {
+            const size_t r = (size_t)w * Nb + i;
+            const double D = (double)D_i[r];
+            const float c = conf[(size_t)w * N + block_start + i];
+            int drift_rule = 0;
+            double dl = 0.0;
+            if (n > 0) {
+                const double mean = hist_sum[r] / (double)n;
+                const double gap = (double)tau_s - (double)c;
+                dl = D - mean;
+                drift_rule = dl > (double)alpha * (gap * gap);
+            }
+            const int conf_rule = c >= tau_s;
+            commit[r] = (uint8_t)(drift_rule | (conf_rule << 1));
+            if (delta) delta[r] = (float)dl;
+            hist_sum[r] = (n > 0 ? hist_sum[r] : 0.0) + D;
+        }
+        hist_n[w] = n + 1;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O11 suffix-block commitment (Polestar 2.B/suffix).  When the last layer's
+ * top-k drifted clusters include a suffix-window cluster, suffix rows whose
+ * confidence reaches tau_s are committed.  Reading: a cluster belongs to the
+ * suffix window when strictly more than half of its members are suffix rows
+ * (rows after the decode block); top-k entries outside [0, K) are ignored.  */
+/* ------------------------------------------------------------------------- */
+int pso_commit_suffix(const pso_shape* s, const int32_t* assign, const int32_t* idx, int32_t k,
+                      int32_t block_start, const float* conf, float tau_s, uint8_t* flag,
+                      uint8_t* commit)
+{
+    if (!s || !assign || !idx || !conf || !flag || !commit) return ERR_NULL;
+    if (s->W < 0 || s->N < 1 || s->Nb < 0 || s->Nb > s->N || s->K < 1) return ERR_SHAPE;
+    if (k < 1 || k > s->K) return ERR_RANGE;
+    if (block_start < 0 || block_start > s->N - s->Nb) return ERR_RANGE;
+    if (!isfinite(tau_s)) return ERR_RANGE;
+    const int N = s->N, K = s->K, first = block_start + s->Nb;
+    int32_t* members = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+    int32_t* in_suffix = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
+    for (int w = 0; w < s->W; ++w) {
+        for (int c = 0; c < K; ++c) members[c] = in_suffix[c] = 0;
+        for (int j = 0; j < N; ++j) {
+            const int a = assign[(size_t)w * N + j];
+            if (a < 0 || a >= K) continue;
+            members[a] += 1;
+            if (j >= first) in_suffix[a] += 1;
+        }
+        int f = 0;
+        for (int r = 0; r < k; ++r) {
+            const int c = idx[(size_t)w * k + r];
+            if (c >= 0 && c < K && 2 * in_suffix[c] > members[c]) f = 1;
+        }
+        flag[w] = (uint8_t)f;
+        for (int j = 0; j < N; ++j) {
+            const size_t r = (size_t)w * N + j;
+            commit[r] = (uint8_t)(f && j >= first && conf[r] >= tau_s);
+        }
+    }
+    free(members);
+    free(in_suffix);
+    return 0;
+}

@@ -10,10 +10,12 @@
  * Source of the method: "Polestar: Drift-Aware Cache Calibration and Token
  * Commitment for Efficient Inference of Diffusion LLMs" (Lee, Ramachandran,
  * Kundu, Krishna), as summarised on its gist.science explainer pages
- * (arXiv 2607.14107), technical summary section 2.A "Polestar-Cache".  Below,
- * "Polestar 2.A/drift" means the drift-measurement item of that section,
- * "Polestar 2.A/window" the local-window-and-clustering item, and
- * "Polestar 2.A/sparse" the sparse-updates item.
+ * (arXiv 2607.14107), technical summary section 2.A "Polestar-Cache" and
+ * section 2.B "Polestar-Commit".  Below, "Polestar 2.A/drift" means the
+ * drift-measurement item of section 2.A, "Polestar 2.A/window" the
+ * local-window-and-clustering item, "Polestar 2.A/sparse" the sparse-updates
+ * item; "Polestar 2.B/current" and "Polestar 2.B/suffix" are the current-block
+ * and suffix-block commitment items of section 2.B.
  *
  * Arithmetic: fp32 storage, fp64 accumulation of every sum and dot product,
  * rounded once to fp32 (or bf16) when stored.  bf16 inputs are widened exactly.
@@ -97,6 +99,29 @@ int pso_refresh_gather(const pso_shape* s, int dtype, const int32_t* assign, con
                        const uint8_t* codes, const uint8_t* bscale, const float* rscale,
                        const float* C, const float* row_norm, void* H_hat, const void* Kc,
                        const void* Vc, void* K_out, void* V_out);
+
+/* ---- Polestar-Commit (technical summary section 2.B) --------------------- */
+
+/* Current-block commitment.  D_i: [W][Nb] f32 drift of the block rows (the
+ * D_i that pso_drift_kl writes); conf: [W][N] f32 per-position confidence
+ * of the window, block row i at position block_start + i.  hist_sum [W][Nb]
+ * f64 and hist_n [W] i32 are the caller's running history (sum of the earlier
+ * drifts of each block row and how many there were; a negative count counts
+ * as 0); both are advanced by this call.  commit [W][Nb] u8: bit 0 = the
+ * drift rule fired, bit 1 = the confidence rule fired.  delta [W][Nb] f32
+ * (nullable) = D - history mean, 0 where there is no history. */
+int pso_commit_block(const pso_shape* s, const float* D_i, const float* conf, int32_t block_start,
+                     float alpha, float tau_s, double* hist_sum, int32_t* hist_n,
+                     uint8_t* commit, float* delta);
+
+/* Suffix-block commitment.  assign: [W][N] i32, idx: [W][k] i32 top-k
+ * clusters, conf: [W][N] f32.  Suffix rows are [block_start + Nb, N).
+ * flag [W] u8 = 1 when a top-k cluster is a suffix cluster (strictly more
+ * than half of its members are suffix rows).  commit [W][N] u8 = 1 on suffix
+ * rows with flag set and conf >= tau_s, 0 on every other row. */
+int pso_commit_suffix(const pso_shape* s, const int32_t* assign, const int32_t* idx, int32_t k,
+                      int32_t block_start, const float* conf, float tau_s, uint8_t* flag,
+                      uint8_t* commit);
 
 #ifdef __cplusplus
 }
