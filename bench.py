@@ -4,7 +4,8 @@
 A step is one pass of the whole path over one batch of W windows:
   spherical K-Means (warm start, `iters` Lloyd iterations) + centroid keys ->
   NVFP4 residuals -> proxy attention + KL drift + cluster scores ->
-  top-k clusters -> refresh gather (positions, rebuilt hidden rows, K/V rows).
+  top-k clusters -> refresh gather (positions, rebuilt hidden rows, K/V rows)
+  -> Polestar-Commit's current-block and suffix-block rules.
 Inputs are seeded synthetic tensors already resident in HBM (one snapshot per
 denoising step, generated on the device before the timed region).
 
@@ -53,6 +54,11 @@ def kernel_work(name, cfg):
         return 2 * L * 4 + W * (cfg.Hq * cfg.Nb + cfg.Nb + K) * 4, L * 4.0
     if name.startswith("k_bucket"):
         return 2 * W * N * 4 + W * (K + 1) * 4, 0.0
+    if name.startswith("k_commit_block"):
+        Nb = cfg.Nb
+        return W * Nb * (4 + 4 + 16 + 1 + 4) + W * 8, 0.0
+    if name.startswith("k_commit_suffix"):
+        return W * N * (4 + 4 + 1) + W * (cfg.k * 4 + 1), 0.0
     return None
 
 
@@ -97,7 +103,8 @@ def copy_calibration():
 
 def cpu_baseline(cfg, budget_s):
     """The oracle, unchanged, on a bounded sample: one steady-state step
-    (warm-started K-Means, residuals, proxy attention + KL, top-k, gather) of
+    (warm-started K-Means, residuals, proxy attention + KL, top-k, gather,
+    commit rules) of
     independent windows, fanned out over host threads (ctypes releases the
     GIL).  The formation step that produces each window's state is untimed."""
     import numpy as np
@@ -117,10 +124,12 @@ def cpu_baseline(cfg, budget_s):
                          np.zeros((1, cfg.K, cfg.d), np.float32))
         lp = O.proxy_attn(s, dt, data["Q"], r["Ck"], cfg.softmax_scale)["logp"]
         synth.apply_drift(cfg, data, 1, w0=w)
-        return data, r["C"], r["Ck"], lp
+        conf = synth.confidences(cfg, 1, w0=w, Wc=1)
+        return data, r["C"], r["Ck"], lp, conf
 
     def step(args):
-        data, C, Ck, lp = args
+        data, C, Ck, lp, conf = args
+        hist_sum, hist_n = np.zeros((1, cfg.Nb)), np.zeros(1, np.int32)
         t0 = time.perf_counter()
         r = O.kmeans_fit(s, dt, data["H"], data["Kr"], O.INIT_GIVEN, cfg.iters, C.copy(), Ck.copy())
         q = O.residual_nvfp4(s, dt, data["H"], r["row_norm"], r["C"], r["assign"])
@@ -128,6 +137,8 @@ def cpu_baseline(cfg, budget_s):
         tk = O.topk_clusters(s, pa["score"], cfg.k)
         O.refresh_gather(s, dt, r["assign"], tk["idx"], cfg.k, cfg.N, q["codes"], q["bscale"],
                          q["rscale"], r["C"], r["row_norm"], True, data["Kr"], data["V"])
+        O.commit_block(s, pa["D_i"], conf, cfg.block_start, 0.1, 0.9, hist_sum, hist_n)
+        O.commit_suffix(s, r["assign"], tk["idx"], cfg.k, cfg.block_start, conf, 0.9)
         return time.perf_counter() - t0
 
     # size the sample from one window timed alone: n windows, one per thread,
@@ -194,7 +205,7 @@ def main():
     wl = DeviceWorkload(cfg, n_snap)
     spec = StepSpec(W=cfg.W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb,
                     K=cfg.K, k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
-                    softmax_scale=cfg.softmax_scale, cap=cfg.N)
+                    softmax_scale=cfg.softmax_scale, cap=cfg.N, block_start=cfg.block_start)
     path = DriftPath(spec)
     torch.cuda.synchronize()
 
@@ -273,6 +284,8 @@ def main():
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.dh, "block": cfg.Nb,
                    "clusters": cfg.K, "top_k": cfg.k, "lloyd_iters": cfg.iters,
                    "drift": f"{cfg.drift} {cfg.drift_frac:.0%} rows x {cfg.drift_mag}",
+                   "commit": {"alpha": spec.alpha, "tau_s": spec.tau_s,
+                              "block_start": cfg.block_start},
                    "input_snapshots": n_snap, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

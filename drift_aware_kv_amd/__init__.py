@@ -2,7 +2,8 @@
 
 Polestar-Cache's drift-detection hot path on AMD MI355X (gfx950): spherical
 K-Means of the local window, NVFP4 residuals, proxy attention, KL drift, top-k
-drifted clusters and the refresh gather.  Every step runs in the HIP kernels of
+drifted clusters and the refresh gather; and Polestar-Commit's current-block and
+suffix-block commitment rules on that drift.  Every step runs in the HIP kernels of
 ``libpolestar_drift.so``; this module only marshals arguments (torch tensors ->
 device pointers, the current HIP stream) and checks tensor sizes against the
 shape before anything is enqueued.  There is no CPU fallback: if the library is
@@ -28,7 +29,7 @@ PS_KMEANS_DEFAULT, PS_KMEANS_FIXED_POINT_EXIT = 0, 1
 
 EXPORTS = ("ps_status_string", "ps_workspace_size", "ps_kmeans_fit", "ps_residual_nvfp4",
            "ps_proxy_attn", "ps_drift_kl", "ps_topk_clusters", "ps_refresh_gather",
-           "ps_profile_begin", "ps_profile_end", "ps_profile_summary")
+           "ps_commit_block", "ps_commit_suffix", "ps_profile_begin", "ps_profile_end", "ps_profile_summary")
 
 
 class PsError(RuntimeError):
@@ -75,6 +76,9 @@ def lib():
         L.ps_topk_clusters.argtypes = [SP, P, ctypes.c_int32, P, P, P]
         L.ps_refresh_gather.argtypes = [SP, I, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P,
                                         P, P, P, P, P, P, P, P]
+        F, I32 = ctypes.c_float, ctypes.c_int32
+        L.ps_commit_block.argtypes = [SP, P, P, I32, F, F, P, P, P, P, P]
+        L.ps_commit_suffix.argtypes = [SP, P, P, I32, I32, P, F, P, P, P]
         L.ps_profile_begin.argtypes = [ctypes.c_int32]
         L.ps_profile_end.argtypes = []
         L.ps_profile_summary.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
@@ -231,3 +235,20 @@ def ps_refresh_gather(s: Shape, dtype, assign, idx, k, cap, pos, count, codes=No
         _ptr(H_hat, s.W * cap * s.d, e, "H_hat", True), _ptr(Kc, s.W * s.N * KV, e, "Kc", True),
         _ptr(Vc, s.W * s.N * KV, e, "Vc", True), _ptr(K_out, s.W * cap * KV, e, "K_out", True),
         _ptr(V_out, s.W * cap * KV, e, "V_out", True), _stream(stream)), "ps_refresh_gather")
+
+
+def ps_commit_block(s: Shape, D_i, conf, block_start, alpha, tau_s, hist_sum, hist_n, commit,
+                    delta=None, stream=None):
+    _check(lib().ps_commit_block(
+        _cs(s), _ptr(D_i, s.W * s.Nb, 4, "D_i"), _ptr(conf, s.W * s.N, 4, "conf"),
+        int(block_start), float(alpha), float(tau_s), _ptr(hist_sum, s.W * s.Nb, 8, "hist_sum"),
+        _ptr(hist_n, s.W, 4, "hist_n"), _ptr(commit, s.W * s.Nb, 1, "commit"),
+        _ptr(delta, s.W * s.Nb, 4, "delta", True), _stream(stream)), "ps_commit_block")
+
+
+def ps_commit_suffix(s: Shape, assign, idx, k, block_start, conf, tau_s, flag, commit, stream=None):
+    _check(lib().ps_commit_suffix(
+        _cs(s), _ptr(assign, s.W * s.N, 4, "assign"), _ptr(idx, s.W * k, 4, "idx"), int(k),
+        int(block_start), _ptr(conf, s.W * s.N, 4, "conf"), float(tau_s),
+        _ptr(flag, s.W, 1, "flag"), _ptr(commit, s.W * s.N, 1, "commit"), _stream(stream)),
+        "ps_commit_suffix")

@@ -2,10 +2,11 @@
 
 ``DriftPath`` owns the cross-step state that the C ABI leaves to the caller
 (centres C, centroid keys Ck, the previous step's log-probabilities) plus the
-output buffers, all allocated once with torch on the device, and issues the six
+output buffers, all allocated once with torch on the device, and issues the
 library calls in the order of one step:
 
   kmeans_fit -> residual_nvfp4 -> proxy_attn (+ drift) -> topk -> refresh_gather
+  [-> commit_block -> commit_suffix, when per-position confidences are given]
 
 Step 0 (window formation) seeds the clusters and stores the first proxy
 distribution; there is no previous distribution, so no drift, selection or
@@ -13,14 +14,20 @@ gather happens (Polestar technical summary 2.A, schedule: a refresh follows
 formation).  Later steps warm-start K-Means from the previous centres, so
 cluster k at step t continues cluster k at step t-1 and the KL between the two
 proxy distributions is defined.
+
+Polestar-Commit (technical summary 2.B) runs on the drift of every step after
+formation: the current-block rule keeps a per-row drift history (reset when a
+window is formed), the suffix rule reads this step's top-k clusters.  The
+pages give no values for alpha and tau_s; the defaults here are placeholders
+that a caller sets.
 """
 from dataclasses import dataclass
 
 import torch
 
 from . import (PS_BF16, PS_F32, PS_INIT_FARTHEST, PS_INIT_GIVEN, PS_INIT_STRIDED,
-               PS_SCORE_KL_SHARE, Shape, ps_kmeans_fit, ps_proxy_attn, ps_refresh_gather,
-               ps_residual_nvfp4, ps_topk_clusters, workspace)
+               PS_SCORE_KL_SHARE, Shape, ps_commit_block, ps_commit_suffix, ps_kmeans_fit,
+               ps_proxy_attn, ps_refresh_gather, ps_residual_nvfp4, ps_topk_clusters, workspace)
 
 
 @dataclass
@@ -42,6 +49,9 @@ class StepSpec:
     score_kind: int = PS_SCORE_KL_SHARE
     gather_rows: bool = True
     kmeans_flags: int = 0
+    block_start: int = None      # default: the block centred in the window
+    alpha: float = 0.1
+    tau_s: float = 0.9
 
     @property
     def shape(self) -> Shape:
@@ -84,6 +94,13 @@ class DriftPath:
             self.V_out = torch.zeros(s.W, self.cap, s.Hkv, s.dh, dtype=et, device=dev)
         else:
             self.H_hat = self.K_out = self.V_out = None
+        self.block_start = (s.N - s.Nb) // 2 if spec.block_start is None else spec.block_start
+        self.hist_sum = torch.zeros(s.W, s.Nb, dtype=torch.float64, device=dev)
+        self.hist_n = torch.zeros(s.W, dtype=i32, device=dev)
+        self.commit_block = torch.zeros(s.W, s.Nb, dtype=torch.uint8, device=dev)
+        self.delta = torch.zeros(s.W, s.Nb, dtype=f32, device=dev)
+        self.suffix_flag = torch.zeros(s.W, dtype=torch.uint8, device=dev)
+        self.commit_suffix = torch.zeros(s.W, s.N, dtype=torch.uint8, device=dev)
         self.t = 0
 
     @property
@@ -94,9 +111,11 @@ class DriftPath:
     def logp_prev(self):
         return self.logp[(self.t - 1) & 1]
 
-    def step(self, H, Kr, V, Q, stream=None):
+    def step(self, H, Kr, V, Q, conf=None, stream=None):
         """Run one step on device tensors H [W][N][d], Kr/V [W][N][Hkv][dh],
-        Q [W][Nb][Hq][dh]; returns t of the step just run."""
+        Q [W][Nb][Hq][dh] and, optionally, the per-position confidences
+        conf [W][N] f32 that the commit rules read; returns t of the step just
+        run."""
         sp, s, dt = self.spec, self.shape, self.dtype
         first = self.t == 0
         init = {"strided": PS_INIT_STRIDED, "farthest": PS_INIT_FARTHEST}[sp.init0] if first \
@@ -115,6 +134,11 @@ class DriftPath:
                               self.bscale, self.rscale, self.C, self.row_norm, self.H_hat,
                               Kr if gather else None, V if gather else None, self.K_out,
                               self.V_out, stream)
+            if conf is not None:
+                ps_commit_block(s, self.D_i, conf, self.block_start, sp.alpha, sp.tau_s,
+                                self.hist_sum, self.hist_n, self.commit_block, self.delta, stream)
+                ps_commit_suffix(s, self.assign, self.idx, sp.k, self.block_start, conf, sp.tau_s,
+                                 self.suffix_flag, self.commit_suffix, stream)
         t = self.t
         self.t += 1
         return t

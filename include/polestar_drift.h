@@ -7,7 +7,9 @@
  * Krishna), as summarised on its gist.science explainer pages (arXiv
  * 2607.14107).  Citations below name that summary's section 2.A
  * ("Polestar-Cache") and its items: "drift measurement", "local window and
- * clustering", "sparse updates"; and section 2.C ("system optimisation").
+ * clustering", "sparse updates"; section 2.B ("Polestar-Commit") and its
+ * items "current-block commitment" and "suffix-block commitment"; and
+ * section 2.C ("system optimisation").
  *
  * Conventions shared by every call
  * --------------------------------
@@ -214,6 +216,57 @@ ps_status ps_refresh_gather(const ps_shape* shape, ps_dtype dtype, const int32_t
                             const float* rscale, const float* C, const float* row_norm,
                             void* H_hat, const void* Kc, const void* Vc, void* K_out,
                             void* V_out, void* stream);
+
+/*
+ * ps_commit_block -- current-block commitment (section 2.B, current-block
+ * commitment).  The drift delta of block row i is its drift now minus the
+ * mean of its drifts at the earlier steps of the window's history; the row
+ * commits when that delta exceeds the confidence-conditioned threshold
+ * alpha * (tau_s - c)^2, or when its confidence c reaches tau_s (the static
+ * rule).  With no history yet (count <= 0) only the confidence rule can fire.
+ * Every operation on the drift is one IEEE fp64 operation:
+ *   mean = hist_sum / n; gap = tau_s - c; delta = D - mean;
+ *   drift rule: delta > alpha * (gap * gap).
+ *
+ *   D_i  [W][Nb] f32 in      drift of the block rows (as ps_drift_kl writes)
+ *   conf [W][N]  f32 in      per-position confidence of the window; block row
+ *                            i sits at position block_start + i
+ *   block_start              0 <= block_start <= N - Nb
+ *   alpha >= 0, tau_s        finite (PS_ERR_RANGE otherwise)
+ *   hist_sum [W][Nb] f64 in/out  sum of each row's earlier drifts; D is added
+ *   hist_n   [W]     i32 in/out  number of earlier steps; a count <= 0 starts
+ *                            a fresh history (hist_sum is then ignored); set
+ *                            to n + 1.  Zero it when a window is re-formed.
+ *   commit [W][Nb] u8 out    bit 0: the drift rule fired; bit 1: c >= tau_s
+ *   delta  [W][Nb] f32 out   (nullable) fp32 of the delta; 0 with no history
+ * A NaN drift or confidence fires neither rule; a NaN drift makes the row's
+ * history sum NaN.
+ */
+ps_status ps_commit_block(const ps_shape* shape, const float* D_i, const float* conf,
+                          int32_t block_start, float alpha, float tau_s, double* hist_sum,
+                          int32_t* hist_n, uint8_t* commit, float* delta, void* stream);
+
+/*
+ * ps_commit_suffix -- suffix-block commitment (section 2.B, suffix-block
+ * commitment).  Pass the windows whose update packet decides (the pages use
+ * the last layer's).  A cluster belongs to the suffix window when strictly
+ * more than half of its members are suffix rows, i.e. rows at or after
+ * block_start + Nb.  When any of the window's top-k clusters is such a
+ * cluster, its suffix rows with confidence >= tau_s commit.
+ *
+ *   assign [W][N] i32 in     cluster of each row; values outside [0,K) count
+ *                            for no cluster
+ *   idx    [W][k] i32 in     top-k clusters (ps_topk_clusters); entries
+ *                            outside [0,K) are ignored; 1 <= k <= K
+ *   block_start              0 <= block_start <= N - Nb
+ *   conf   [W][N] f32 in     per-position confidence; tau_s finite
+ *   flag   [W]    u8  out    1 when a top-k cluster is a suffix cluster
+ *   commit [W][N] u8  out    1 on suffix rows of flagged windows with
+ *                            conf >= tau_s; 0 on every other row
+ */
+ps_status ps_commit_suffix(const ps_shape* shape, const int32_t* assign, const int32_t* idx,
+                           int32_t k, int32_t block_start, const float* conf, float tau_s,
+                           uint8_t* flag, uint8_t* commit, void* stream);
 
 /*
  * Kernel timer (instrumentation, not part of the method; off by default).

@@ -26,6 +26,11 @@ BASE_SEED = 20260717
 S_H, S_KR, S_V, S_Q, S_DIR, S_LAB = 1, 2, 3, 4, 5, 6
 
 
+def _conf_stream(t):
+    """Per-position token confidences at denoising step t."""
+    return 3000 + t
+
+
 def _drift_pick_stream(t):
     return 100 + t
 
@@ -112,11 +117,12 @@ def lib():
         u64, i32, i64, dbl, P = (ctypes.c_uint64, ctypes.c_int, ctypes.c_int64, ctypes.c_double,
                                  ctypes.c_void_p)
         L.synth_normal.argtypes = [u64, u64, u64, i64, dbl, i32, P]
+        L.synth_uniform.argtypes = [u64, u64, u64, i64, dbl, dbl, P]
         L.synth_planted.argtypes = [u64, i32, i32, i32, dbl, P, P]
         L.synth_pick_rows.argtypes = [u64, u64, i32, i32, i32, P]
         L.synth_add_noise_rows.argtypes = [u64, u64, i32, i32, i32, i32, i32, P, dbl, i32, i32, P]
         L.synth_rotate_rows.argtypes = [u64, u64, i32, i32, i32, i32, i32, P, dbl, i32, P]
-        for f in ("synth_normal", "synth_planted", "synth_pick_rows", "synth_add_noise_rows",
+        for f in ("synth_normal", "synth_uniform", "synth_planted", "synth_pick_rows", "synth_add_noise_rows",
                   "synth_rotate_rows"):
             getattr(L, f).restype = None
         _lib = L
@@ -133,6 +139,20 @@ def normal(shape, seed, stream, offset=0, scale=1.0, bf16=True):
     out = np.empty(shape, np.uint16 if bf16 else np.float32)
     lib().synth_normal(seed, stream, offset, out.size, scale, 1 if bf16 else 0, _ptr(out))
     return out
+
+
+def uniform(shape, seed, stream, offset=0, lo=0.0, hi=1.0):
+    """fp32 lo + (hi - lo) * U(0,1); element i = element offset+i of the stream."""
+    out = np.empty(shape, np.float32)
+    lib().synth_uniform(seed, stream, offset, out.size, lo, hi, _ptr(out))
+    return out
+
+
+def confidences(cfg: "Config", t: int, w0: int = 0, Wc: int = None, seed: int = BASE_SEED):
+    """Stand-in for the model's per-position confidence (the probability of
+    its predicted token) at step t: U(0,1), [Wc][N] fp32."""
+    Wc = cfg.W - w0 if Wc is None else Wc
+    return uniform((Wc, cfg.N), seed, _conf_stream(t), offset=w0 * cfg.N)
 
 
 def planted(N, d, M, noise, seed=BASE_SEED):

@@ -1,7 +1,8 @@
 """Device-side seeded workloads for the benchmark.
 
 Same recipe as the host generator in this package (N(0,1) hidden states, key
-and value rows and queries in bf16; per-step drift on a seeded random subset
+and value rows and queries in bf16, U(0,1) per-position confidences drawn
+afresh at every step; per-step drift on a seeded random subset
 of round(frac * N) rows per window: Gaussian noise, Student-t (nu = 3) noise,
 or a rotation by theta inside the plane of the row and a random orthogonal
 direction), drawn with torch's generator on the GPU so that multi-GiB batches
@@ -30,12 +31,16 @@ class DeviceWorkload:
             Kr=self._randn((W, N, cfg.Hkv, cfg.dh)).to(et),
             V=self._randn((W, N, cfg.Hkv, cfg.dh)).to(et),
             Q=self._randn((W, cfg.Nb, cfg.Hq, cfg.dh)).to(et),
+            conf=self._rand((W, N)),
         )
         self.snaps = [base]
         for t in range(1, n_snapshots):
             nxt = {k: v.clone() for k, v in self.snaps[-1].items()}
             self._drift(nxt)
             self.snaps.append(nxt)
+
+    def _rand(self, shape):
+        return torch.rand(shape, generator=self.g, device=self.dev, dtype=torch.float32)
 
     def _randn(self, shape):
         return torch.randn(shape, generator=self.g, device=self.dev, dtype=torch.float32)
@@ -55,6 +60,7 @@ class DeviceWorkload:
             q = s["Q"].view(W, cfg.Nb, -1)
             wq, rq = widx[inb], rows[inb] - b0
             q[wq, rq] = self._move(q[wq, rq].float()).to(q.dtype)
+        s["conf"] = self._rand((W, N))      # the model's confidences change every step
 
     def _move(self, x):
         cfg = self.cfg
@@ -78,9 +84,10 @@ class DeviceWorkload:
         S = len(self.snaps)
         i = step if step < S else 1 + (step - 1) % (S - 1) if S > 1 else 0
         s = self.snaps[i]
-        return s["H"], s["Kr"], s["V"], s["Q"]
+        return s["H"], s["Kr"], s["V"], s["Q"], s["conf"]
 
     @staticmethod
     def snapshot_bytes(cfg: Config) -> int:
         e = 2 if cfg.bf16 else 4
-        return e * cfg.W * (cfg.N * cfg.d + 2 * cfg.N * cfg.Hkv * cfg.dh + cfg.Nb * cfg.Hq * cfg.dh)
+        return (e * cfg.W * (cfg.N * cfg.d + 2 * cfg.N * cfg.Hkv * cfg.dh + cfg.Nb * cfg.Hq * cfg.dh)
+                + 4 * cfg.W * cfg.N)

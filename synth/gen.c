@@ -90,6 +90,15 @@ void synth_normal(uint64_t seed, uint64_t stream, uint64_t offset, int64_t count
         put(out, bf16, (size_t)i, scale * gauss(seed, stream, offset + (uint64_t)i));
 }
 
+/* out[i] = lo + (hi - lo) * U(0,1) as fp32, element index offset+i */
+void synth_uniform(uint64_t seed, uint64_t stream, uint64_t offset, int64_t count, double lo,
+                   double hi, float* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = (float)(lo + (hi - lo) * uni(seed, stream, offset + (uint64_t)i));
+}
+
 /* Planted directions: M unit directions u_m (normalised N(0,I) draws), labels
  * uniform in [0, M), h_j = u_{label_j} + noise * N(0,I).  fp32 output. */
 void synth_planted(uint64_t seed, int N, int d, int M, double noise, float* out, int32_t* labels)

@@ -59,19 +59,26 @@ def assignment_mismatches(H, C_in, bf16, got, want, row_norm):
     return ties, real
 
 
-def check_centres_from_assignment(so, dtype, H, row_norm, assign, C_gpu, counts_gpu):
-    """The GPU's centres and counts must equal the oracle's update step run on
-    the GPU's own assignment (bit for bit: same fp64 operations in the same
-    order, up to the summation order of ||S||), and every non-empty centre
-    must be a unit vector."""
-    r = O.kmeans_update(so, dtype, H, row_norm, assign, C_gpu)
-    assert np.array_equal(counts_gpu, r["counts"]), "counts from the assignment"
-    diff = C_gpu.view(np.uint32) != r["C"].view(np.uint32)
-    assert close(C_gpu, r["C"], 1e-6, 1e-7), f"centres from the assignment: {max_rel(C_gpu, r['C'])}"
-    ne = counts_gpu > 0
-    nrm = np.linalg.norm(C_gpu.astype(np.float64), axis=-1)
-    assert np.all(np.abs(nrm[ne] - 1.0) < 1e-6), "non-empty centres must be unit vectors"
-    return int(diff.sum())
+def check_centre_properties(H, bf16, row_norm, assign, C, counts):
+    """Properties of one window's K-Means result that hold whatever the other
+    side computed, checked with plain numpy on the device's outputs: counts
+    are the member counts of the assignment, every non-empty centre is a unit
+    vector along the sum of its members' unit rows (cosine >= 1 - 1e-6).
+    H [N][d], row_norm [N], assign [N], C [K][d], counts [K]."""
+    K = C.shape[0]
+    assert np.array_equal(counts, np.bincount(assign, minlength=K)[:K]), "counts vs assignment"
+    Hf = (bf16f(H) if bf16 else H).astype(np.float64)
+    n = row_norm.astype(np.float64)
+    X = np.where(n[:, None] > 0, Hf / np.where(n > 0, n, 1.0)[:, None], 0.0)
+    S = np.zeros((K, Hf.shape[1]))
+    np.add.at(S, assign, X)
+    Cd = C.astype(np.float64)
+    for k in np.nonzero(counts)[0]:
+        ns = np.linalg.norm(S[k])
+        if ns == 0:
+            continue
+        assert abs(np.linalg.norm(Cd[k]) - 1.0) < 1e-6, f"centre {k} is not a unit vector"
+        assert Cd[k] @ S[k] / ns >= 1.0 - 1e-6, f"centre {k} does not point along its members"
 
 
 def topk_equivalent(score, got, want):
@@ -83,3 +90,19 @@ def topk_equivalent(score, got, want):
     sw = np.sort(score[want])[::-1]
     tol = TIE_TOPK * np.maximum(1.0, np.abs(sw))
     return bool(np.all(np.abs(sg - sw) <= tol))
+
+
+def commit_block_mismatches(got, want, delta_want, conf, alpha, tau_s, d_err):
+    """Current-block commit bits that differ between the two sides, split into
+    near-threshold cases (the oracle's delta within d_err of its threshold
+    alpha*(tau_s-c)^2, where d_err bounds the difference of the two sides'
+    deltas given the drift tolerance) and real disagreements.  Bit 1 (the
+    confidence rule) reads identical inputs and must always agree."""
+    assert np.array_equal(got & 2, want & 2), "confidence rule"
+    bad = np.nonzero((got & 1) != (want & 1))
+    gap = np.float64(tau_s) - conf.astype(np.float64)
+    thr = np.float64(alpha) * (gap * gap)
+    near = np.abs(delta_want.astype(np.float64) - thr) <= d_err
+    ties = [tuple(int(x) for x in ix) for ix in zip(*bad) if near[ix]]
+    real = [tuple(int(x) for x in ix) for ix in zip(*bad) if not near[ix]]
+    return ties, real

@@ -146,3 +146,30 @@ def test_topk_and_gather_argument_checks(L):
     assert g(Hh=FAKE) == NULL                              # H_hat needs the residual inputs
     assert L.ps_refresh_gather(ctypes.byref(_shape(W=0)), 1, FAKE, FAKE, 2, 0, None, FAKE, None,
                                None, None, None, None, None, None, None, None, None, None) == OK
+
+
+def test_commit_argument_checks(L):
+    s = _shape()                                           # N=64, Nb=8, K=4
+    b = lambda s=s, b0=10, alpha=1.0, tau=0.9, D=FAKE, delta=None: L.ps_commit_block(
+        ctypes.byref(s), D, FAKE, b0, alpha, tau, FAKE, FAKE, FAKE, delta, None)
+    assert b(D=None) == NULL
+    assert b(b0=-1) == RANGE
+    assert b(b0=57) == RANGE                               # block past the window end
+    assert b(alpha=-0.5) == RANGE
+    assert b(alpha=float("nan")) == RANGE
+    assert b(tau=float("inf")) == RANGE
+    assert b(D=MISALIGNED) == ALIGN
+    assert b(delta=MISALIGNED) == ALIGN
+    assert b(s=_shape(Nb=65)) == SHAPE
+    assert b(s=_shape(W=0)) == OK
+    assert b(s=_shape(W=0), b0=56) == OK                   # last valid block start
+    u = lambda s=s, k=2, b0=10, tau=0.9, flag=FAKE: L.ps_commit_suffix(
+        ctypes.byref(s), FAKE, FAKE, k, b0, FAKE, tau, flag, FAKE, None)
+    assert u(flag=None) == NULL
+    assert u(k=0) == RANGE
+    assert u(k=5) == RANGE                                 # k > K
+    assert u(b0=60) == RANGE
+    assert u(tau=float("nan")) == RANGE
+    assert u(flag=MISALIGNED) == ALIGN
+    assert u(s=_shape(K=2000)) == SHAPE
+    assert u(s=_shape(W=0)) == OK

@@ -1,15 +1,19 @@
 """Chained end-to-end parity of whole steps (kmeans -> residual -> proxy
-attention + drift -> top-k -> gather) against the oracle run from the same
-seeded inputs, on the workloads of the benchmark: the tiny planted case, a
-LLaDA-8B layer, a Dream-7B layer (GQA), and at full size the 512-window
-LLaDA-8B batch and the 128-window long-window batch on sampled windows (every
-window is independent, so a sampled window's results depend on its own data
-only; the other windows carry random data of the same shape).
+attention + drift -> top-k -> gather -> commit rules) against the oracle run
+from the same seeded inputs, on the workloads of the benchmark: the tiny
+planted case, a LLaDA-8B layer, a Dream-7B layer (GQA), and at full size the
+512-window LLaDA-8B batch and the 128-window long-window batch on sampled
+windows (every window is independent, so a sampled window's results depend on
+its own data only; the other windows carry random data of the same shape).
 
-Where the two sides assign a row differently the test classifies the
-difference: it must be a near-tie (oracle fp64 gap <= 1e-6 on the cosine
-scale) found by replaying that step one Lloyd iteration at a time from the
-GPU's centres; everything downstream is then compared stage-fed."""
+Each side runs its own chain: the oracle never reads anything the device
+computed.  Where the two sides assign a row differently, the step is replayed
+one Lloyd iteration at a time on both sides, each from its own state, to find
+the first iteration that differs; every row that differs there must be a
+near-tie (oracle fp64 gap <= 1e-6 on the cosine scale) under the centres both
+sides started that iteration from.  That window's chains then legitimately
+part and its later steps are checked only for properties that hold on their
+own (counts, unit centres along their members)."""
 import sys
 
 import numpy as np
@@ -18,10 +22,12 @@ import torch
 
 import oracle as O
 import synth
-from parity_helpers import (assignment_mismatches, bf16f, check_centres_from_assignment, close, dev,
-                            host, max_rel, topk_equivalent)
+from parity_helpers import (ATOL, RTOL, assignment_mismatches, check_centre_properties, close,
+                            commit_block_mismatches, dev, host, max_rel, topk_equivalent)
 
 pytestmark = pytest.mark.gpu
+
+ALPHA, TAU_S = 0.02, 0.9     # commit parameters of these runs (the pages give no values)
 
 
 @pytest.fixture(scope="module")
@@ -40,8 +46,9 @@ def oshape(cfg, W=1):
     return O.Shape(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
 
 
-def oracle_step(cfg, st, data, t, iters=None):
-    """One oracle step for one window; st carries C, Ck, logp between steps."""
+def oracle_step(cfg, st, data, conf, t, iters=None):
+    """One oracle step for one window; st carries the oracle's own C, Ck,
+    logp and commit history between steps."""
     s = oshape(cfg)
     dt = O.BF16 if cfg.bf16 else O.F32
     iters = cfg.iters if iters is None else iters
@@ -49,109 +56,137 @@ def oracle_step(cfg, st, data, t, iters=None):
         init = O.INIT_FARTHEST if cfg.init0 == "farthest" else O.INIT_STRIDED
         C = np.zeros((1, cfg.K, cfg.d), np.float32)
         Ck = np.zeros((1, cfg.K, cfg.Hkv, cfg.dh), np.uint16 if cfg.bf16 else np.float32)
+        hist_sum, hist_n = np.zeros((1, cfg.Nb)), np.zeros(1, np.int32)
     else:
         init, C, Ck = O.INIT_GIVEN, st["C"].copy(), st["Ck"].copy()
+        hist_sum, hist_n = st["hist_sum"].copy(), st["hist_n"].copy()
     r = O.kmeans_fit(s, dt, data["H"], data["Kr"], init, iters, C, Ck)
     q = O.residual_nvfp4(s, dt, data["H"], r["row_norm"], r["C"], r["assign"])
     pa = O.proxy_attn(s, dt, data["Q"], r["Ck"], cfg.softmax_scale,
                       None if t == 0 else st["logp"])
     out = dict(C=r["C"], Ck=r["Ck"], assign=r["assign"], counts=r["counts"], row_norm=r["row_norm"],
                codes=q["codes"], bscale=q["bscale"], rscale=q["rscale"], logp=pa["logp"],
-               D_i=pa["D_i"], D_hi=pa["D_hi"], score=pa["score"])
+               D_i=pa["D_i"], D_hi=pa["D_hi"], score=pa["score"], hist_sum=hist_sum, hist_n=hist_n)
     if t > 0:
         tk = O.topk_clusters(s, pa["score"], cfg.k)
         g = O.refresh_gather(s, dt, r["assign"], tk["idx"], cfg.k, cfg.N, q["codes"], q["bscale"],
                              q["rscale"], r["C"], r["row_norm"], True, data["Kr"], data["V"])
         out.update(idx=tk["idx"], pos=g["pos"], count=g["count"], H_hat=g["H_hat"],
                    K_out=g["K_out"], V_out=g["V_out"])
+        cb = O.commit_block(s, pa["D_i"], conf, cfg.block_start, ALPHA, TAU_S, hist_sum, hist_n)
+        cs = O.commit_suffix(s, r["assign"], tk["idx"], cfg.k, cfg.block_start, conf, TAU_S)
+        out.update(commit_block=cb["commit"], delta=cb["delta"], suffix_flag=cs["flag"],
+                   commit_suffix=cs["commit"])
     return out
 
 
 def gpu_snapshot(path, w, t):
-    o = dict(C=host(path.C[w:w + 1]), Ck=host(path.Ck[w:w + 1]), assign=host(path.assign[w:w + 1]),
-             counts=host(path.counts[w:w + 1]), row_norm=host(path.row_norm[w:w + 1]),
-             codes=host(path.codes[w:w + 1]), bscale=host(path.bscale[w:w + 1]),
-             rscale=host(path.rscale[w:w + 1]), logp=host(path.logp[t & 1][w:w + 1]),
-             D_i=host(path.D_i[w:w + 1]), D_hi=host(path.D_hi[w:w + 1]),
-             score=host(path.score[w:w + 1]))
+    sl = slice(w, w + 1)
+    o = dict(C=host(path.C[sl]), Ck=host(path.Ck[sl]), assign=host(path.assign[sl]),
+             counts=host(path.counts[sl]), row_norm=host(path.row_norm[sl]),
+             codes=host(path.codes[sl]), bscale=host(path.bscale[sl]), rscale=host(path.rscale[sl]),
+             logp=host(path.logp[t & 1][sl]), D_i=host(path.D_i[sl]), D_hi=host(path.D_hi[sl]),
+             score=host(path.score[sl]), hist_sum=host(path.hist_sum[sl]),
+             hist_n=host(path.hist_n[sl]))
     if t > 0:
-        o.update(idx=host(path.idx[w:w + 1]), pos=host(path.pos[w:w + 1]),
-                 count=host(path.count[w:w + 1]), H_hat=host(path.H_hat[w:w + 1]),
-                 K_out=host(path.K_out[w:w + 1]), V_out=host(path.V_out[w:w + 1]))
+        o.update(idx=host(path.idx[sl]), pos=host(path.pos[sl]), count=host(path.count[sl]),
+                 H_hat=host(path.H_hat[sl]), K_out=host(path.K_out[sl]), V_out=host(path.V_out[sl]),
+                 commit_block=host(path.commit_block[sl]), delta=host(path.delta[sl]),
+                 suffix_flag=host(path.suffix_flag[sl]), commit_suffix=host(path.commit_suffix[sl]))
     return o
 
 
-def compare_downstream(cfg, g, data, t, prev_logp):
-    """Everything after K-Means, stage-fed from the GPU's own upstream."""
-    s = oshape(cfg)
-    dt = O.BF16 if cfg.bf16 else O.F32
-    q = O.residual_nvfp4(s, dt, data["H"], g["row_norm"], g["C"], g["assign"])
-    assert np.array_equal(g["codes"], q["codes"]), "codes"
-    assert np.array_equal(g["bscale"], q["bscale"]), "block scales"
-    assert np.array_equal(g["rscale"].view(np.uint32), q["rscale"].view(np.uint32)), "row scales"
-    pa = O.proxy_attn(s, dt, data["Q"], g["Ck"], cfg.softmax_scale)
-    assert close(g["logp"], pa["logp"]), f"logp {max_rel(g['logp'], pa['logp'])}"
+def compare_step(cfg, g, o, conf, t, d_hist):
+    """Both sides assigned every row alike: compare everything else."""
+    assert np.array_equal(g["counts"], o["counts"])
+    assert close(g["C"], o["C"], 1e-6, 1e-7), f"centres {max_rel(g['C'], o['C'])}"
+    assert np.array_equal(g["Ck"], o["Ck"]) if cfg.bf16 else close(g["Ck"], o["Ck"], 1e-6, 1e-7)
+    assert max_rel(g["row_norm"], o["row_norm"]) <= 1.2e-7
+    # the coder's inputs of a row are its norm and its centre: where both are
+    # bit-identical on the two sides, the codes must be too
+    a = o["assign"][0]
+    same_c = np.all(g["C"][0].view(np.uint32) == o["C"][0].view(np.uint32), axis=-1)
+    rows = same_c[a] & (g["row_norm"][0].view(np.uint32) == o["row_norm"][0].view(np.uint32))
+    assert rows.mean() >= 0.99, f"only {rows.mean():.4f} of the rows have bit-identical coder inputs"
+    assert np.array_equal(g["codes"][0][rows], o["codes"][0][rows]), "codes"
+    assert np.array_equal(g["bscale"][0][rows], o["bscale"][0][rows]), "block scales"
+    assert np.array_equal(g["rscale"][0][rows].view(np.uint32), o["rscale"][0][rows].view(np.uint32))
+    assert close(g["rscale"], o["rscale"], 1e-6, 0.0)
+    assert close(g["logp"], o["logp"]), f"logp {max_rel(g['logp'], o['logp'])}"
     if t == 0:
         assert not g["D_i"].any() and not g["score"].any()
         return
-    kl = O.drift_kl(s, g["logp"], prev_logp)
-    assert close(g["D_i"], kl["D_i"]) and close(g["score"], kl["score"]) and close(g["D_hi"], kl["D_hi"])
-    tk = O.topk_clusters(s, g["score"], cfg.k)
-    assert np.array_equal(g["idx"], tk["idx"]), "top-k on the GPU's scores"
-    ga = O.refresh_gather(s, dt, g["assign"], g["idx"], cfg.k, cfg.N, g["codes"], g["bscale"],
-                          g["rscale"], g["C"], g["row_norm"], True, data["Kr"], data["V"])
-    m = int(ga["count"][0])
+    assert close(g["D_i"], o["D_i"]) and close(g["D_hi"], o["D_hi"]) and close(g["score"], o["score"])
+    assert topk_equivalent(o["score"][0], g["idx"][0], o["idx"][0]), "top-k"
+    assert int(g["hist_n"][0]) == int(o["hist_n"][0]) == t
+    assert close(g["hist_sum"], o["hist_sum"], RTOL, ATOL * t)
+    ties, real = commit_block_mismatches(g["commit_block"][0], o["commit_block"][0], o["delta"][0],
+                                         conf[0, cfg.block_start:cfg.block_start + cfg.Nb],
+                                         ALPHA, TAU_S, d_hist)
+    assert not real, f"current-block commit: {len(real)} disagreements away from the threshold"
+    if ties:
+        say(f"    step {t}: {len(ties)} near-threshold commit rows")
+    if not np.array_equal(g["idx"], o["idx"]):
+        return                                  # equivalent near-tie selection: nothing more to compare
+    m = int(o["count"][0])
     assert int(g["count"][0]) == m
-    assert np.array_equal(g["pos"][0, :m], ga["pos"][0, :m])
-    assert np.array_equal(g["H_hat"][0, :m].view(np.uint16 if cfg.bf16 else np.uint32),
-                          ga["H_hat"][0, :m].view(np.uint16 if cfg.bf16 else np.uint32))
-    assert np.array_equal(g["K_out"][0, :m], ga["K_out"][0, :m])
-    assert np.array_equal(g["V_out"][0, :m], ga["V_out"][0, :m])
+    assert np.array_equal(g["pos"][0, :m], o["pos"][0, :m])
+    assert np.array_equal(g["K_out"][0, :m], o["K_out"][0, :m])
+    assert np.array_equal(g["V_out"][0, :m], o["V_out"][0, :m])
+    gr = rows[o["pos"][0, :m]]           # rebuilt rows whose coder inputs were bit-identical
+    view = np.uint16 if cfg.bf16 else np.uint32
+    assert np.array_equal(g["H_hat"][0, :m][gr].view(view), o["H_hat"][0, :m][gr].view(view))
+    assert np.array_equal(g["suffix_flag"], o["suffix_flag"]), "suffix flag"
+    assert np.array_equal(g["commit_suffix"], o["commit_suffix"]), "suffix commit"
 
 
-def lockstep_replay(P, cfg, data, C_start, Ck_start, t):
-    """Replay one step's K-Means one iteration at a time on the GPU from the
-    given centres, feeding each iteration's GPU centres to the oracle; return
-    the number of near-tie flips (asserting there is no real disagreement)."""
+def replay_first_difference(P, cfg, data, C_gpu, Ck_gpu, ost, t):
+    """Replay one step's K-Means one Lloyd iteration at a time on both sides,
+    the device from its own centres before the step and the oracle from its
+    own; return the near-tie rows at the first iteration whose assignments
+    differ (asserting there is no real disagreement, and that one differs)."""
     s = P.Shape(W=1, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
     dt = P.PS_BF16 if cfg.bf16 else P.PS_F32
     odt = O.BF16 if cfg.bf16 else O.F32
-    C = dev(C_start)
-    Ck = dev(Ck_start)
+    C, Ck = dev(C_gpu), dev(Ck_gpu)
     a = torch.zeros(1, cfg.N, dtype=torch.int32, device="cuda")
     cnt = torch.zeros(1, cfg.K, dtype=torch.int32, device="cuda")
     rn = torch.zeros(1, cfg.N, device="cuda")
     ws = P.workspace(s, dt)
     Hd, Krd = dev(data["H"]), dev(data["Kr"])
-    flips = 0
+    seed = O.INIT_FARTHEST if cfg.init0 == "farthest" else O.INIT_STRIDED
+    oC = np.zeros((1, cfg.K, cfg.d), np.float32) if t == 0 else ost["C"].copy()
     for it in range(cfg.iters):
-        init = P.PS_INIT_GIVEN
-        if t == 0 and it == 0:
-            init = P.PS_INIT_FARTHEST if cfg.init0 == "farthest" else P.PS_INIT_STRIDED
-            C_in = O.kmeans_init(oshape(cfg), odt, data["H"],
-                                 O.INIT_FARTHEST if cfg.init0 == "farthest" else O.INIT_STRIDED)
-        else:
-            C_in = host(C).copy()
+        first = t == 0 and it == 0
+        init = (P.PS_INIT_FARTHEST if cfg.init0 == "farthest" else P.PS_INIT_STRIDED) if first \
+            else P.PS_INIT_GIVEN
+        C_in = O.kmeans_init(oshape(cfg), odt, data["H"], seed) if first else oC.copy()
         P.ps_kmeans_fit(s, dt, Hd, Krd, init, 1, C, a, cnt, rn, Ck, None, ws)
         torch.cuda.synchronize()
-        r = O.kmeans_fit(oshape(cfg), odt, data["H"], None, O.INIT_GIVEN, 1, C_in.copy())
-        ties, real = assignment_mismatches(data["H"][0], C_in[0], cfg.bf16, host(a)[0],
-                                           r["assign"][0], r["row_norm"][0])
-        assert not real, f"step {t} iteration {it}: {len(real)} real disagreements"
-        flips += len(ties)
-    return flips
+        r = O.kmeans_fit(oshape(cfg), odt, data["H"], None, seed if first else O.INIT_GIVEN, 1,
+                         oC.copy())
+        ga = host(a)[0]
+        if not np.array_equal(ga, r["assign"][0]):
+            ties, real = assignment_mismatches(data["H"][0], C_in[0], cfg.bf16, ga, r["assign"][0],
+                                               r["row_norm"][0])
+            assert not real, f"step {t} iteration {it}: {len(real)} real disagreements"
+            return ties
+        assert close(host(C), r["C"], 1e-6, 1e-7)
+        oC = r["C"]
+    raise AssertionError(f"step {t}: the step's assignment differs but no replayed iteration does")
 
 
 def run_chained(P, cfg, steps, windows=None, W=None):
-    """GPU DriftPath over `steps` steps; for each sampled window the oracle
-    runs chained; on an assignment difference the step is replayed in
-    lockstep and the oracle re-synchronised to the GPU state."""
+    """GPU DriftPath over `steps` steps with the commit rules; the oracle runs
+    its own chain for each sampled window.  Returns the number of windows whose
+    chains parted at a near-tie."""
     from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
     W = cfg.W if W is None else W
     windows = list(range(W)) if windows is None else windows
     spec = StepSpec(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K,
                     k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
-                    softmax_scale=cfg.softmax_scale, cap=cfg.N)
+                    softmax_scale=cfg.softmax_scale, cap=cfg.N, block_start=cfg.block_start,
+                    alpha=ALPHA, tau_s=TAU_S)
     path = DriftPath(spec)
     et = torch.bfloat16 if cfg.bf16 else torch.float32
     # device inputs: sampled windows from the generator, the rest random
@@ -165,86 +200,74 @@ def run_chained(P, cfg, steps, windows=None, W=None):
     Krd = fill((W, cfg.N, cfg.Hkv, cfg.dh))
     Vd = fill((W, cfg.N, cfg.Hkv, cfg.dh))
     Qd = fill((W, cfg.Nb, cfg.Hq, cfg.dh))
+    confd = torch.rand((W, cfg.N), device="cuda", generator=g)
 
-    def upload(w):
+    def upload(w, conf):
         for key, dst in (("H", Hd), ("Kr", Krd), ("V", Vd), ("Q", Qd)):
             src = dev(host_data[w][key][0])
             dst[w].copy_(src.view(et) if cfg.bf16 else src)
+        confd[w].copy_(dev(conf[0]))
 
     ost = {w: None for w in windows}
-    total_flips = 0
+    parted = {}
+    d_max = {w: 0.0 for w in windows}
     for t in range(steps):
         if t > 0:
             for w in windows:
                 synth.apply_drift(cfg, host_data[w], t, w0=w)
             Hd.add_(fill(Hd.shape) * 0.01)  # unchecked windows drift too
+        conf = {w: synth.confidences(cfg, t, w0=w, Wc=1) for w in windows}
         for w in windows:
-            upload(w)
+            upload(w, conf[w])
         say(f"  {cfg.name} step {t}: GPU")
         prevC = {w: host(path.C[w:w + 1]).copy() for w in windows}
         prevCk = {w: host(path.Ck[w:w + 1]).copy() for w in windows}
-        path.step(Hd, Krd, Vd, Qd)
+        path.step(Hd, Krd, Vd, Qd, conf=confd)
         torch.cuda.synchronize()
         for w in windows:
-            say(f"  {cfg.name} step {t}: oracle window {w}")
             gs = gpu_snapshot(path, w, t)
-            # centres and counts of the final iteration from the GPU's own
-            # assignment, unit norm (independent of any near-tie)
-            check_centres_from_assignment(oshape(cfg), O.BF16 if cfg.bf16 else O.F32,
-                                          host_data[w]["H"], gs["row_norm"], gs["assign"], gs["C"],
-                                          gs["counts"])
-            o = oracle_step(cfg, ost[w], host_data[w], t)
-            if np.array_equal(gs["assign"], o["assign"]):
-                assert np.array_equal(gs["counts"], o["counts"])
-                assert close(gs["C"], o["C"], 1e-6, 1e-7), f"centres {max_rel(gs['C'], o['C'])}"
-                assert np.array_equal(gs["Ck"], o["Ck"]) if cfg.bf16 else close(gs["Ck"], o["Ck"], 1e-6, 1e-7)
-                assert max_rel(gs["row_norm"], o["row_norm"]) <= 1.2e-7
-                assert np.array_equal(gs["codes"], o["codes"])
-                assert np.array_equal(gs["bscale"], o["bscale"])
-                assert close(gs["logp"], o["logp"])
-                if t > 0:
-                    assert close(gs["D_i"], o["D_i"]) and close(gs["score"], o["score"])
-                    assert topk_equivalent(o["score"][0], gs["idx"][0], o["idx"][0])
-                    if np.array_equal(gs["idx"], o["idx"]):
-                        m = int(o["count"][0])
-                        assert int(gs["count"][0]) == m
-                        assert np.array_equal(gs["pos"][0, :m], o["pos"][0, :m])
-                        assert np.array_equal(gs["K_out"][0, :m], o["K_out"][0, :m])
-            else:
-                flips = lockstep_replay(P, cfg, host_data[w], prevC[w], prevCk[w], t)
-                say(f"    window {w} step {t}: assignments differ; lockstep near-tie flips: {flips}")
-                total_flips += max(flips, 1)
-            # stage-fed check of everything downstream of K-Means, then carry
-            # the GPU state forward in the oracle too
-            compare_downstream(cfg, gs, host_data[w], t, None if t == 0 else ost[w]["logp_gpu"])
-            ost[w] = dict(C=gs["C"], Ck=gs["Ck"], logp=gs["logp"], logp_gpu=gs["logp"])
-    return total_flips
+            check_centre_properties(host_data[w]["H"][0], cfg.bf16, gs["row_norm"][0],
+                                    gs["assign"][0], gs["C"][0], gs["counts"][0])
+            if w in parted:
+                continue
+            say(f"  {cfg.name} step {t}: oracle window {w}")
+            o = oracle_step(cfg, ost[w], host_data[w], conf[w], t)
+            if not np.array_equal(gs["assign"], o["assign"]):
+                ties = replay_first_difference(P, cfg, host_data[w], prevC[w], prevCk[w], ost[w], t)
+                say(f"    window {w} step {t}: chains part at {len(ties)} near-tie rows")
+                parted[w] = t
+                continue
+            if t > 0:
+                d_max[w] = max(d_max[w], float(np.abs(o["D_i"]).max()))
+            # bound on |delta_gpu - delta_oracle|: the drift tolerance on the
+            # current drift plus on the mean of the earlier ones
+            d_err = 2.0 * max(ATOL, RTOL * d_max[w])
+            compare_step(cfg, gs, o, conf[w], t, d_err)
+            ost[w] = o
+    return len(parted)
 
 
-def test_tiny_planted_two_steps_exact(P):
+def test_tiny_planted_three_steps_exact(P):
     cfg = synth.CONFIGS["C1"]
-    flips = run_chained(P, cfg, steps=2)
-    assert flips == 0
+    assert run_chained(P, cfg, steps=3) == 0
 
 
 def test_llada_layer_chained(P):
     cfg = synth.CONFIGS["C2"]
-    flips = run_chained(P, cfg, steps=3)
-    say("llada layer near-tie flips:", flips)
+    say("llada layer: windows parted at a near-tie:", run_chained(P, cfg, steps=4))
 
 
 def test_dream_layer_chained(P):
     cfg = synth.CONFIGS["C3"]
-    flips = run_chained(P, cfg, steps=2)
-    say("dream layer near-tie flips:", flips)
+    say("dream layer: windows parted at a near-tie:", run_chained(P, cfg, steps=3))
 
 
 def test_full_size_llada_batch_sampled(P):
     """512 windows (32 layers x 16 sequences) in one launch per call, as the
     benchmark runs them; windows 0, 301 and 511 checked against the oracle."""
     cfg = synth.CONFIGS["C4"]
-    flips = run_chained(P, cfg, steps=2, windows=[0, 301, 511])
-    say("llada batch near-tie flips:", flips)
+    say("llada batch: windows parted at a near-tie:",
+        run_chained(P, cfg, steps=3, windows=[0, 301, 511]))
 
 
 def test_full_size_long_window_sampled(P):
@@ -252,8 +275,7 @@ def test_full_size_long_window_sampled(P):
     checked with one Lloyd iteration per step (the oracle needs minutes for
     eight at this size: the iteration count does not change the kernels)."""
     cfg = synth.CONFIGS["C5"].with_(iters=1)
-    flips = run_chained(P, cfg, steps=2, windows=[77])
-    say("long window near-tie flips:", flips)
+    say("long window: windows parted at a near-tie:", run_chained(P, cfg, steps=2, windows=[77]))
 
 
 def test_step_is_deterministic(P):
