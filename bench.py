@@ -101,6 +101,108 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read_per_launch": 1 << 30, "copy_bytes_written_per_launch": 1 << 30}))
 
 
+class StandInForward:
+    """Stand-in for the dLLM forward pass the drift path runs beside: the
+    projection and FFN GEMMs of LLaDA-8B (hidden 4096, MHA 32 x 128, FFN
+    12288 with a gated SiLU) over `tokens` rows, for `layers` layers, bf16 on
+    hipBLASLt through torch.  One layer's weights serve every layer (436 MB,
+    larger than the last-level cache, so each layer still streams them from
+    HBM).  No attention over the cache and no model weights: it only occupies
+    the GPU the way a forward pass's GEMMs do."""
+
+    def __init__(self, tokens, layers=32, d=4096, ffn=12288, seed=5):
+        import torch
+        g = torch.Generator(device="cuda").manual_seed(seed)
+
+        def w(i, o):
+            return (torch.randn((i, o), generator=g, device="cuda") * i ** -0.5).to(torch.bfloat16)
+
+        self.layers = layers
+        self.Wqkv, self.Wo = w(d, 3 * d), w(d, d)
+        self.Wgu, self.Wd = w(d, 2 * ffn), w(ffn, d)
+        self.x0 = torch.randn((tokens, d), generator=g, device="cuda").to(torch.bfloat16)
+        self.ffn = ffn
+        self.flops = 2.0 * layers * tokens * (d * 3 * d + d * d + d * 2 * ffn + ffn * d)
+
+    def run(self):
+        import torch
+        x = self.x0
+        for _ in range(self.layers):
+            qkv = x @ self.Wqkv
+            o = qkv[:, : x.shape[1]] @ self.Wo
+            gu = x @ self.Wgu
+            h = torch.nn.functional.silu(gu[:, : self.ffn]) * gu[:, self.ffn:]
+            x = x + o + h @ self.Wd
+        return x
+
+
+def latency_hiding(path, wl, first_input, steps):
+    """Time the stand-in forward alone, the drift step alone, and both at once
+    on two streams of default priority (forward on one, drift step on the
+    other); the part of the drift step the forward hides is
+    1 - (t_both - t_forward) / t_drift."""
+    import torch
+    sequences = max(1, path.shape.W // 32)          # 32 layers per sequence
+    fwd = StandInForward(tokens=sequences * path.shape.Nb)
+    s_fwd, s_drift = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(first_input + i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def forward_only(i):
+        with torch.cuda.stream(s_fwd):
+            fwd.run()
+
+    def drift_only(i):
+        with torch.cuda.stream(s_drift):
+            path.step(*wl.inputs(i), stream=s_drift)
+
+    def both(i):
+        with torch.cuda.stream(s_fwd):
+            fwd.run()
+        with torch.cuda.stream(s_drift):
+            path.step(*wl.inputs(i), stream=s_drift)
+
+    forward_only(0)
+    torch.cuda.synchronize()
+    t_f = timed(forward_only)
+    t_d = timed(drift_only)
+    t_b = timed(both)
+    exposed = max(t_b - t_f, 0.0)
+    return {"forward": "LLaDA-8B projection + FFN GEMMs (hidden 4096, FFN 12288), 32 layers, "
+                       f"{fwd.x0.shape[0]} tokens (the decode blocks of the batch's sequences), bf16",
+            "forward_ms": t_f * 1e3, "forward_tflops": fwd.flops / t_f / 1e12,
+            "drift_ms": t_d * 1e3, "both_ms": t_b * 1e3, "exposed_drift_ms": exposed * 1e3,
+            "hidden_fraction": 1.0 - exposed / t_d, "steps": steps}
+
+
+def bandwidth():
+    """Practical HBM ceilings with torch's own streaming kernels on 4 GiB:
+    a read-only reduction and an elementwise copy (read + write)."""
+    import torch
+    n = 1 << 31
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, nbytes in (("read_sum", lambda: a.sum(dtype=torch.float32), 2 * n),
+                             ("copy_neg", lambda: torch.neg(a, out=b), 4 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_GBs"] = nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    print(json.dumps(out))
+
+
 def cpu_baseline(cfg, budget_s):
     """The oracle, unchanged, on a bounded sample: one steady-state step
     (warm-started K-Means, residuals, proxy attention + KL, top-k, gather,
@@ -167,11 +269,18 @@ def main():
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timer")
     ap.add_argument("--no-fixed-point", action="store_true",
                     help="skip the secondary timing with the exact fixed-point exit")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the latency-hiding figure (drift step beside a stand-in forward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (counter calibration) and exit")
+    ap.add_argument("--bandwidth", action="store_true",
+                    help="only measure streaming read and copy bandwidth and exit")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.bandwidth:
+        bandwidth()
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this path runs on one GPU; windows are independent, so more GPUs "
@@ -270,6 +379,12 @@ def main():
         fpx = {"value": args.steps * cfg.W * cfg.N / (f1 - f0), "ms_per_step": 1e3 * (f1 - f0) / args.steps}
         print(f"[bench] fixed-point exit: {fpx['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
 
+    hiding = None
+    if not args.no_overlap:
+        print("[bench] latency hiding beside a stand-in forward", file=sys.stderr, flush=True)
+        hiding = latency_hiding(path, wl, total + args.steps, args.steps)
+        print(f"[bench] hidden fraction {hiding['hidden_fraction']:.3f}", file=sys.stderr, flush=True)
+
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
@@ -290,6 +405,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "fixed_point_exit": fpx,
+        "latency_hiding": hiding,
         "kernels": breakdown,
     }
     print(json.dumps(line), flush=True)
