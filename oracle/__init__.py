@@ -73,9 +73,10 @@ def lib():
         L.pso_refresh_gather.argtypes = [SP, I, P, P, ctypes.c_int32, ctypes.c_int32, P, P,
                                          P, P, P, P, P, P, P, P, P, P]
         F = ctypes.c_float
+        L.pso_drift_cosine.argtypes = [SP, P, P, P]
         L.pso_commit_block.argtypes = [SP, P, P, ctypes.c_int32, F, F, P, P, P, P]
         L.pso_commit_suffix.argtypes = [SP, P, P, ctypes.c_int32, ctypes.c_int32, P, F, P, P]
-        for name in ("pso_commit_block", "pso_commit_suffix", "pso_row_norms", "pso_kmeans_init", "pso_kmeans_fit", "pso_kmeans_update",
+        for name in ("pso_drift_cosine", "pso_commit_block", "pso_commit_suffix", "pso_row_norms", "pso_kmeans_init", "pso_kmeans_fit", "pso_kmeans_update",
                      "pso_residual_nvfp4",
                      "pso_proxy_attn", "pso_drift_kl", "pso_topk_clusters", "pso_refresh_gather"):
             getattr(L, name).restype = ctypes.c_int
@@ -216,6 +217,14 @@ def refresh_gather(s: Shape, dtype, assign, idx, k, cap, codes=None, bscale=None
                                  _p(row_norm), _p(H_hat), _p(Kc), _p(Vc), _p(K_out), _p(V_out)),
         "pso_refresh_gather")
     return dict(pos=pos, count=count, H_hat=H_hat, K_out=K_out, V_out=V_out)
+
+
+def drift_cosine(s: Shape, C_cur, C_prev):
+    """Cosine-dissimilarity drift of every cluster: score [W][K] f32."""
+    score = np.zeros((s.W, s.K), np.float32)
+    _ok(lib().pso_drift_cosine(ctypes.byref(_cshape(s)), _p(C_cur), _p(C_prev), _p(score)),
+        "pso_drift_cosine")
+    return score
 
 
 # ---- Polestar-Commit -------------------------------------------------------

@@ -644,6 +644,28 @@ int pso_refresh_gather(const pso_shape* s, int dtype, const int32_t* assign, con
 }
 
 /* ------------------------------------------------------------------------- */
+/* O12 cosine-dissimilarity drift (Polestar 2.A/drift names cosine
+ * dissimilarity as the measure KL is compared against).  Reading: with
+ * warm-started spherical K-Means the cosine dissimilarity of cluster k between
+ * steps is 1 - <c_k(t), c_k(t-1)> of its unit centres, i.e. how far the
+ * centre moved; it scores clusters for the same top-k selection.            */
+/* ------------------------------------------------------------------------- */
+int pso_drift_cosine(const pso_shape* s, const float* C_cur, const float* C_prev, float* score)
+{
+    if (!s || !C_cur || !C_prev || !score) return ERR_NULL;
+    if (s->W < 0 || s->K < 1 || s->d < 1) return ERR_SHAPE;
+    const size_t K = (size_t)s->K, d = (size_t)s->d;
+    for (size_t wk = 0; wk < (size_t)s->W * K; ++wk) {
+        const float* a = C_cur + wk * d;
+        const float* b = C_prev + wk * d;
+        double dot = 0.0;
+        for (size_t e = 0; e < d; ++e) dot += (double)a[e] * (double)b[e];
+        score[wk] = (float)(1.0 - dot);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* O10 current-block commitment (Polestar 2.B/current).  The drift delta of a
  * block row is its drift now minus the mean of its earlier drifts; the row is
  * committed when that delta exceeds the confidence-conditioned threshold

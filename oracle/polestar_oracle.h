@@ -100,6 +100,12 @@ int pso_refresh_gather(const pso_shape* s, int dtype, const int32_t* assign, con
                        const float* C, const float* row_norm, void* H_hat, const void* Kc,
                        const void* Vc, void* K_out, void* V_out);
 
+/* Cosine-dissimilarity drift of each cluster between consecutive steps (the
+ * alternative the drift-measurement item compares KL against):
+ * score [W][K] f32 = fp32(1 - sum_e C_cur[k][e] * C_prev[k][e]), the sum in
+ * fp64 in ascending e.  C_cur, C_prev: [W][K][d] f32 unit centres. */
+int pso_drift_cosine(const pso_shape* s, const float* C_cur, const float* C_prev, float* score);
+
 /* ---- Polestar-Commit (technical summary section 2.B) --------------------- */
 
 /* Current-block commitment.  D_i: [W][Nb] f32 drift of the block rows (the
