@@ -54,6 +54,8 @@ def kernel_work(name, cfg):
         return 2 * L * 4 + W * (cfg.Hq * cfg.Nb + cfg.Nb + K) * 4, L * 4.0
     if name.startswith("k_bucket"):
         return 2 * W * N * 4 + W * (K + 1) * 4, 0.0
+    if name.startswith("k_drift_cosine"):
+        return 2 * W * K * d * 4 + W * K * 4, 2.0 * W * K * d
     if name.startswith("k_commit_block"):
         Nb = cfg.Nb
         return W * Nb * (4 + 4 + 16 + 1 + 4) + W * 8, 0.0
@@ -269,6 +271,9 @@ def main():
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timer")
     ap.add_argument("--no-fixed-point", action="store_true",
                     help="skip the secondary timing with the exact fixed-point exit")
+    ap.add_argument("--cluster-score", default="kl", choices=["kl", "cosine"],
+                    help="rank clusters by drift share (the method) or by centre movement "
+                         "(the cosine-dissimilarity variant)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the latency-hiding figure (drift step beside a stand-in forward)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -314,7 +319,8 @@ def main():
     wl = DeviceWorkload(cfg, n_snap)
     spec = StepSpec(W=cfg.W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb,
                     K=cfg.K, k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
-                    softmax_scale=cfg.softmax_scale, cap=cfg.N, block_start=cfg.block_start)
+                    softmax_scale=cfg.softmax_scale, cap=cfg.N, block_start=cfg.block_start,
+                    cluster_score=args.cluster_score)
     path = DriftPath(spec)
     torch.cuda.synchronize()
 
@@ -399,6 +405,7 @@ def main():
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.dh, "block": cfg.Nb,
                    "clusters": cfg.K, "top_k": cfg.k, "lloyd_iters": cfg.iters,
                    "drift": f"{cfg.drift} {cfg.drift_frac:.0%} rows x {cfg.drift_mag}",
+                   "cluster_score": args.cluster_score,
                    "commit": {"alpha": spec.alpha, "tau_s": spec.tau_s,
                               "block_start": cfg.block_start},
                    "input_snapshots": n_snap, "parallelism": "single GPU"},

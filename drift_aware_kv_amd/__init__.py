@@ -29,7 +29,7 @@ PS_KMEANS_DEFAULT, PS_KMEANS_FIXED_POINT_EXIT = 0, 1
 
 EXPORTS = ("ps_status_string", "ps_workspace_size", "ps_kmeans_fit", "ps_residual_nvfp4",
            "ps_proxy_attn", "ps_drift_kl", "ps_topk_clusters", "ps_refresh_gather",
-           "ps_commit_block", "ps_commit_suffix", "ps_profile_begin", "ps_profile_end", "ps_profile_summary")
+           "ps_drift_cosine", "ps_commit_block", "ps_commit_suffix", "ps_profile_begin", "ps_profile_end", "ps_profile_summary")
 
 
 class PsError(RuntimeError):
@@ -77,6 +77,7 @@ def lib():
         L.ps_refresh_gather.argtypes = [SP, I, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P,
                                         P, P, P, P, P, P, P, P]
         F, I32 = ctypes.c_float, ctypes.c_int32
+        L.ps_drift_cosine.argtypes = [SP, P, P, P, P]
         L.ps_commit_block.argtypes = [SP, P, P, I32, F, F, P, P, P, P, P]
         L.ps_commit_suffix.argtypes = [SP, P, P, I32, I32, P, F, P, P, P]
         L.ps_profile_begin.argtypes = [ctypes.c_int32]
@@ -235,6 +236,13 @@ def ps_refresh_gather(s: Shape, dtype, assign, idx, k, cap, pos, count, codes=No
         _ptr(H_hat, s.W * cap * s.d, e, "H_hat", True), _ptr(Kc, s.W * s.N * KV, e, "Kc", True),
         _ptr(Vc, s.W * s.N * KV, e, "Vc", True), _ptr(K_out, s.W * cap * KV, e, "K_out", True),
         _ptr(V_out, s.W * cap * KV, e, "V_out", True), _stream(stream)), "ps_refresh_gather")
+
+
+def ps_drift_cosine(s: Shape, C_cur, C_prev, score, stream=None):
+    n = s.W * s.K * s.d
+    _check(lib().ps_drift_cosine(_cs(s), _ptr(C_cur, n, 4, "C_cur"), _ptr(C_prev, n, 4, "C_prev"),
+                                 _ptr(score, s.W * s.K, 4, "score"), _stream(stream)),
+           "ps_drift_cosine")
 
 
 def ps_commit_block(s: Shape, D_i, conf, block_start, alpha, tau_s, hist_sum, hist_n, commit,

@@ -310,6 +310,31 @@ __global__ __launch_bounds__(256) void k_drift_kl(const float* __restrict__ cur,
         score[(size_t)w * K + k] = (((sp[k] + sp[K + k]) + sp[2 * K + k]) + sp[3 * K + k]) * invH;
 }
 
+// Cosine-dissimilarity drift of each cluster: one wave per (window, cluster),
+// 16-byte loads of both unit centres, products and sums in fp64 (each fp32
+// product is exact in fp64), one wave reduction, then 1 - dot rounded once.
+__global__ __launch_bounds__(256) void k_drift_cosine(const float* __restrict__ cur,
+                                                      const float* __restrict__ prev, int d,
+                                                      int64_t pairs, float* __restrict__ score)
+{
+    const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (p >= pairs) return;
+    const int lane = lane_id();
+    const float* a = cur + p * d;
+    const float* b = prev + p * d;
+    double dot = 0.0;
+    for (int e = 4 * lane; e < d; e += 256) {          // d % 16 == 0: whole float4s
+        const float4 x = *reinterpret_cast<const float4*>(a + e);
+        const float4 y = *reinterpret_cast<const float4*>(b + e);
+        dot = fma((double)x.x, (double)y.x, dot);
+        dot = fma((double)x.y, (double)y.y, dot);
+        dot = fma((double)x.z, (double)y.z, dot);
+        dot = fma((double)x.w, (double)y.w, dot);
+    }
+    dot = wave_sum_d(dot);
+    if (lane == 0) score[p] = (float)(1.0 - dot);
+}
+
 __global__ void k_zero(float* __restrict__ p, size_t n)
 {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -543,6 +568,23 @@ extern "C" ps_status ps_topk_clusters(const ps_shape* s, const float* score, int
     hipStream_t stm = (hipStream_t)stream;
     (void)hipGetLastError();
     PS_LAUNCH("k_topk", k_topk, dim3(s->W), dim3(64), 0, stm, score, s->K, k, idx, val);
+    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
+}
+
+extern "C" ps_status ps_drift_cosine(const ps_shape* s, const float* C_cur, const float* C_prev,
+                                     float* score, void* stream)
+{
+    using namespace ps_host;
+    if (!s || !C_cur || !C_prev || !score) return PS_ERR_NULL;
+    if (s->W < 0 || s->K < 1 || s->K > kMaxK || s->d < 16 || s->d % 16 != 0) return PS_ERR_SHAPE;
+    if ((int64_t)s->K * s->d >= ((int64_t)1 << 31)) return PS_ERR_SHAPE;
+    if (!aligned16(C_cur) || !aligned16(C_prev) || !aligned16(score)) return PS_ERR_ALIGN;
+    if (s->W == 0) return PS_OK;
+    const int64_t pairs = (int64_t)s->W * s->K;
+    hipStream_t stm = (hipStream_t)stream;
+    (void)hipGetLastError();
+    PS_LAUNCH("k_drift_cosine", k_drift_cosine, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stm,
+              C_cur, C_prev, s->d, pairs, score);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
 }
 

@@ -15,6 +15,11 @@ formation).  Later steps warm-start K-Means from the previous centres, so
 cluster k at step t continues cluster k at step t-1 and the KL between the two
 proxy distributions is defined.
 
+With ``cluster_score="cosine"`` the clusters are ranked instead by how far
+their centres moved during the step's K-Means (cosine dissimilarity, the
+measure the pages' drift-measurement item compares KL against); the proxy
+attention and its per-token drift still run for the commit rules.
+
 Polestar-Commit (technical summary 2.B) runs on the drift of every step after
 formation: the current-block rule keeps a per-row drift history (reset when a
 window is formed), the suffix rule reads this step's top-k clusters.  The
@@ -26,8 +31,9 @@ from dataclasses import dataclass
 import torch
 
 from . import (PS_BF16, PS_F32, PS_INIT_FARTHEST, PS_INIT_GIVEN, PS_INIT_STRIDED,
-               PS_SCORE_KL_SHARE, Shape, ps_commit_block, ps_commit_suffix, ps_kmeans_fit,
-               ps_proxy_attn, ps_refresh_gather, ps_residual_nvfp4, ps_topk_clusters, workspace)
+               PS_SCORE_KL_SHARE, Shape, ps_commit_block, ps_commit_suffix, ps_drift_cosine,
+               ps_kmeans_fit, ps_proxy_attn, ps_refresh_gather, ps_residual_nvfp4, ps_topk_clusters,
+               workspace)
 
 
 @dataclass
@@ -52,6 +58,7 @@ class StepSpec:
     block_start: int = None      # default: the block centred in the window
     alpha: float = 0.1
     tau_s: float = 0.9
+    cluster_score: str = "kl"    # "kl" (drift share) or "cosine" (centre movement)
 
     @property
     def shape(self) -> Shape:
@@ -84,6 +91,12 @@ class DriftPath:
         self.D_hi = torch.zeros(s.W, s.Hq, s.Nb, dtype=f32, device=dev)
         self.D_i = torch.zeros(s.W, s.Nb, dtype=f32, device=dev)
         self.score = torch.zeros(s.W, s.K, dtype=f32, device=dev)
+        if spec.cluster_score not in ("kl", "cosine"):
+            raise ValueError(f"cluster_score must be 'kl' or 'cosine', not {spec.cluster_score!r}")
+        self.C_prev = self.score_cos = None
+        if spec.cluster_score == "cosine":
+            self.C_prev = torch.zeros_like(self.C)
+            self.score_cos = torch.zeros(s.W, s.K, dtype=f32, device=dev)
         self.idx = torch.zeros(s.W, spec.k, dtype=i32, device=dev)
         self.val = torch.zeros(s.W, spec.k, dtype=f32, device=dev)
         self.pos = torch.full((s.W, max(self.cap, 1)), -1, dtype=i32, device=dev)
@@ -120,6 +133,10 @@ class DriftPath:
         first = self.t == 0
         init = {"strided": PS_INIT_STRIDED, "farthest": PS_INIT_FARTHEST}[sp.init0] if first \
             else PS_INIT_GIVEN
+        cosine = self.score_cos is not None and not first
+        if cosine:
+            with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+                self.C_prev.copy_(self.C)
         ps_kmeans_fit(s, dt, H, Kr, init, sp.iters, self.C, self.assign, self.counts, self.row_norm,
                       self.Ck, self.objective, self.ws, stream, flags=sp.kmeans_flags)
         ps_residual_nvfp4(s, dt, H, self.row_norm, self.C, self.assign, self.codes, self.bscale,
@@ -127,7 +144,11 @@ class DriftPath:
         ps_proxy_attn(s, dt, Q, self.Ck, self.scale, self.logp_cur, None if first else self.logp_prev,
                       sp.score_kind, self.D_hi, self.D_i, self.score, stream)
         if not first:
-            ps_topk_clusters(s, self.score, sp.k, self.idx, self.val, stream)
+            score = self.score
+            if cosine:
+                ps_drift_cosine(s, self.C, self.C_prev, self.score_cos, stream)
+                score = self.score_cos
+            ps_topk_clusters(s, score, sp.k, self.idx, self.val, stream)
             gather = self.K_out is not None
             ps_refresh_gather(s, dt, self.assign, self.idx, sp.k, self.cap,
                               self.pos if self.cap > 0 else None, self.count, self.codes,

@@ -180,6 +180,24 @@ ps_status ps_drift_kl(const ps_shape* shape, const float* logp_cur, const float*
                       ps_score score_kind, float* D_hi, float* D_i, float* score, void* stream);
 
 /*
+ * ps_drift_cosine -- cosine-dissimilarity drift of every cluster between two
+ * consecutive steps, the measure the pages' drift-measurement item (section
+ * 2.A) sets KL against, here as an alternative cluster score for the same
+ * top-k selection.  With warm-started spherical K-Means a cluster's cosine
+ * dissimilarity is 1 - <c_k(t), c_k(t-1)> of its unit centres, i.e. how far
+ * the centre moved:
+ *   score[w][k] = fp32(1 - sum_e C_cur[w][k][e] * C_prev[w][k][e]),
+ * the products and their sum in fp64 (the order of the sum may differ from
+ * a sequential one by fp64 rounding, below one fp32 ulp of the result).
+ *
+ *   C_cur, C_prev [W][K][d] f32 in (C_prev = the centres before this step's
+ *   K-Means; the call does not check that they are unit vectors)
+ *   score [W][K] f32 out
+ */
+ps_status ps_drift_cosine(const ps_shape* shape, const float* C_cur, const float* C_prev,
+                          float* score, void* stream);
+
+/*
  * ps_topk_clusters -- the k most drifted clusters of each window (section
  * 2.A, sparse updates: the top-k drifted clusters are selected).  Order:
  * score descending, then index ascending; NaN ranks after every number;

@@ -173,3 +173,12 @@ def test_commit_argument_checks(L):
     assert u(flag=MISALIGNED) == ALIGN
     assert u(s=_shape(K=2000)) == SHAPE
     assert u(s=_shape(W=0)) == OK
+
+
+def test_drift_cosine_argument_checks(L):
+    c = lambda s=_shape(), a=FAKE, sc=FAKE: L.ps_drift_cosine(ctypes.byref(s), a, FAKE, sc, None)
+    assert c(a=None) == NULL
+    assert c(s=_shape(d=24)) == SHAPE                      # d % 16 != 0
+    assert c(s=_shape(K=0)) == SHAPE
+    assert c(sc=MISALIGNED) == ALIGN
+    assert c(s=_shape(W=0)) == OK

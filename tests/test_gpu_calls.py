@@ -412,3 +412,34 @@ def test_w_zero_is_a_no_op(P):
     z = torch.zeros(16, dtype=torch.int32, device="cuda")
     P.ps_topk_clusters(s, torch.zeros(16, device="cuda"), 2, z)
     torch.cuda.synchronize()
+
+
+def cosine_close(got, want, d):
+    """fp32 roundings of 1 - (a fp64 dot product of unit vectors summed in two
+    different orders): the fp64 sums differ by at most d * 2^-53 * sum|a b|
+    <= d * 2^-53, and each side rounds once to fp32 (one fp32 ulp)."""
+    got, want = np.asarray(got, np.float32), np.asarray(want, np.float32)
+    tol = np.spacing(np.abs(want)).astype(np.float64) + d * 2.0 ** -53
+    return bool(np.all(np.abs(got.astype(np.float64) - want) <= tol))
+
+
+@pytest.mark.parametrize("W,K,d", [(3, 37, 80), (2, 64, 4096), (1, 1000, 16), (4, 1, 3584)])
+def test_drift_cosine(P, W, K, d):
+    rng = np.random.default_rng(W * 1000 + K)
+    prev = rng.standard_normal((W, K, d))
+    prev /= np.linalg.norm(prev, axis=-1, keepdims=True)
+    cur = prev + rng.uniform(0, 0.3, (W, K, 1)) * rng.standard_normal((W, K, d)) / np.sqrt(d)
+    cur /= np.linalg.norm(cur, axis=-1, keepdims=True)
+    cur, prev = cur.astype(np.float32), prev.astype(np.float32)
+    cur[0, 0] = prev[0, 0]                         # unmoved: exactly zero
+    if K > 2:
+        cur[0, 1] = -prev[0, 1]                    # reversed
+    s = P.Shape(W=W, N=K, d=d, K=K)
+    sc = torch.full((W, K), 7.0, device="cuda")
+    P.ps_drift_cosine(s, dev(cur), dev(prev), sc)
+    torch.cuda.synchronize()
+    want = O.drift_cosine(O.Shape(W=W, N=K, d=d, K=K), cur, prev)
+    got = host(sc)
+    assert cosine_close(got, want, d), f"max diff {np.abs(got - want).max()}"
+    # the unmoved centre scores 1 - ||c||^2: zero up to its fp32 normalisation
+    assert abs(got[0, 0]) < 1e-6

@@ -46,7 +46,7 @@ def oshape(cfg, W=1):
     return O.Shape(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
 
 
-def oracle_step(cfg, st, data, conf, t, iters=None):
+def oracle_step(cfg, st, data, conf, t, iters=None, cluster_score="kl"):
     """One oracle step for one window; st carries the oracle's own C, Ck,
     logp and commit history between steps."""
     s = oshape(cfg)
@@ -68,7 +68,11 @@ def oracle_step(cfg, st, data, conf, t, iters=None):
                codes=q["codes"], bscale=q["bscale"], rscale=q["rscale"], logp=pa["logp"],
                D_i=pa["D_i"], D_hi=pa["D_hi"], score=pa["score"], hist_sum=hist_sum, hist_n=hist_n)
     if t > 0:
-        tk = O.topk_clusters(s, pa["score"], cfg.k)
+        rank = pa["score"]
+        if cluster_score == "cosine":
+            rank = O.drift_cosine(s, r["C"], st["C"])
+            out.update(score_cos=rank)
+        tk = O.topk_clusters(s, rank, cfg.k)
         g = O.refresh_gather(s, dt, r["assign"], tk["idx"], cfg.k, cfg.N, q["codes"], q["bscale"],
                              q["rscale"], r["C"], r["row_norm"], True, data["Kr"], data["V"])
         out.update(idx=tk["idx"], pos=g["pos"], count=g["count"], H_hat=g["H_hat"],
@@ -88,6 +92,8 @@ def gpu_snapshot(path, w, t):
              logp=host(path.logp[t & 1][sl]), D_i=host(path.D_i[sl]), D_hi=host(path.D_hi[sl]),
              score=host(path.score[sl]), hist_sum=host(path.hist_sum[sl]),
              hist_n=host(path.hist_n[sl]))
+    if t > 0 and path.score_cos is not None:
+        o.update(score_cos=host(path.score_cos[sl]))
     if t > 0:
         o.update(idx=host(path.idx[sl]), pos=host(path.pos[sl]), count=host(path.count[sl]),
                  H_hat=host(path.H_hat[sl]), K_out=host(path.K_out[sl]), V_out=host(path.V_out[sl]),
@@ -117,7 +123,15 @@ def compare_step(cfg, g, o, conf, t, d_hist):
         assert not g["D_i"].any() and not g["score"].any()
         return
     assert close(g["D_i"], o["D_i"]) and close(g["D_hi"], o["D_hi"]) and close(g["score"], o["score"])
-    assert topk_equivalent(o["score"][0], g["idx"][0], o["idx"][0]), "top-k"
+    rank = o["score"]
+    if "score_cos" in o:
+        # fp64 dot products summed in different orders (at most d * 2^-53 apart
+        # for unit vectors), each rounded once to fp32
+        diff = np.abs(g["score_cos"].astype(np.float64) - o["score_cos"])
+        tol = np.spacing(np.abs(o["score_cos"])).astype(np.float64) + cfg.d * 2.0 ** -53
+        assert np.all(diff <= tol), "cosine scores"
+        rank = o["score_cos"]
+    assert topk_equivalent(rank[0], g["idx"][0], o["idx"][0]), "top-k"
     assert int(g["hist_n"][0]) == int(o["hist_n"][0]) == t
     assert close(g["hist_sum"], o["hist_sum"], RTOL, ATOL * t)
     ties, real = commit_block_mismatches(g["commit_block"][0], o["commit_block"][0], o["delta"][0],
@@ -176,7 +190,7 @@ def replay_first_difference(P, cfg, data, C_gpu, Ck_gpu, ost, t):
     raise AssertionError(f"step {t}: the step's assignment differs but no replayed iteration does")
 
 
-def run_chained(P, cfg, steps, windows=None, W=None):
+def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl"):
     """GPU DriftPath over `steps` steps with the commit rules; the oracle runs
     its own chain for each sampled window.  Returns the number of windows whose
     chains parted at a near-tie."""
@@ -186,7 +200,7 @@ def run_chained(P, cfg, steps, windows=None, W=None):
     spec = StepSpec(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K,
                     k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
                     softmax_scale=cfg.softmax_scale, cap=cfg.N, block_start=cfg.block_start,
-                    alpha=ALPHA, tau_s=TAU_S)
+                    alpha=ALPHA, tau_s=TAU_S, cluster_score=cluster_score)
     path = DriftPath(spec)
     et = torch.bfloat16 if cfg.bf16 else torch.float32
     # device inputs: sampled windows from the generator, the rest random
@@ -231,7 +245,7 @@ def run_chained(P, cfg, steps, windows=None, W=None):
             if w in parted:
                 continue
             say(f"  {cfg.name} step {t}: oracle window {w}")
-            o = oracle_step(cfg, ost[w], host_data[w], conf[w], t)
+            o = oracle_step(cfg, ost[w], host_data[w], conf[w], t, cluster_score=cluster_score)
             if not np.array_equal(gs["assign"], o["assign"]):
                 ties = replay_first_difference(P, cfg, host_data[w], prevC[w], prevCk[w], ost[w], t)
                 say(f"    window {w} step {t}: chains part at {len(ties)} near-tie rows")
@@ -255,6 +269,13 @@ def test_tiny_planted_three_steps_exact(P):
 def test_llada_layer_chained(P):
     cfg = synth.CONFIGS["C2"]
     say("llada layer: windows parted at a near-tie:", run_chained(P, cfg, steps=4))
+
+
+def test_llada_layer_chained_cosine_score(P):
+    """The same chain with clusters ranked by how far their centres moved."""
+    cfg = synth.CONFIGS["C2"].with_(W=4)
+    say("llada layer (cosine ranking): windows parted at a near-tie:",
+        run_chained(P, cfg, steps=3, cluster_score="cosine"))
 
 
 def test_dream_layer_chained(P):
