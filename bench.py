@@ -274,6 +274,9 @@ def main():
     ap.add_argument("--cluster-score", default="kl", choices=["kl", "cosine"],
                     help="rank clusters by drift share (the method) or by centre movement "
                          "(the cosine-dissimilarity variant)")
+    ap.add_argument("--residual-store", default="device", choices=["device", "host"],
+                    help="keep the NVFP4 residual store in HBM, or in pinned host memory as the "
+                         "pages' CPU offload (copied out each step, selected rows fetched back)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the latency-hiding figure (drift step beside a stand-in forward)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -320,7 +323,7 @@ def main():
     spec = StepSpec(W=cfg.W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb,
                     K=cfg.K, k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
                     softmax_scale=cfg.softmax_scale, cap=cfg.N, block_start=cfg.block_start,
-                    cluster_score=args.cluster_score)
+                    cluster_score=args.cluster_score, residual_store=args.residual_store)
     path = DriftPath(spec)
     torch.cuda.synchronize()
 
@@ -405,7 +408,7 @@ def main():
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.dh, "block": cfg.Nb,
                    "clusters": cfg.K, "top_k": cfg.k, "lloyd_iters": cfg.iters,
                    "drift": f"{cfg.drift} {cfg.drift_frac:.0%} rows x {cfg.drift_mag}",
-                   "cluster_score": args.cluster_score,
+                   "cluster_score": args.cluster_score, "residual_store": args.residual_store,
                    "commit": {"alpha": spec.alpha, "tau_s": spec.tau_s,
                               "block_start": cfg.block_start},
                    "input_snapshots": n_snap, "parallelism": "single GPU"},

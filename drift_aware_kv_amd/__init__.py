@@ -129,17 +129,17 @@ _ESIZE = {torch.float32: 4, torch.bfloat16: 2, torch.int16: 2, torch.uint16: 2, 
           torch.uint8: 1, torch.float64: 8}
 
 
-def _ptr(t, numel, esize, name, nullable=False):
+def _ptr(t, numel, esize, name, nullable=False, pinned_ok=False):
     """Device pointer of a contiguous tensor holding at least `numel` elements
-    of `esize` bytes."""
+    of `esize` bytes (with pinned_ok, pinned host memory is accepted too)."""
     if t is None:
         if nullable:
             return None
         raise ValueError(f"{name} is required")
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_cuda and not (pinned_ok and t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor" + (" or pinned host memory" if pinned_ok else ""))
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if _ESIZE.get(t.dtype) != esize:
@@ -229,9 +229,9 @@ def ps_refresh_gather(s: Shape, dtype, assign, idx, k, cap, pos, count, codes=No
     _check(lib().ps_refresh_gather(
         _cs(s), dtype, _ptr(assign, s.W * s.N, 4, "assign"), _ptr(idx, s.W * k, 4, "idx"), int(k),
         int(cap), _ptr(pos, s.W * cap, 4, "pos", cap == 0), _ptr(count, s.W, 4, "count"),
-        _ptr(codes, s.W * s.N * s.d // 2, 1, "codes", True),
-        _ptr(bscale, s.W * s.N * s.d // 16, 1, "bscale", True),
-        _ptr(rscale, s.W * s.N, 4, "rscale", True), _ptr(C, s.W * s.K * s.d, 4, "C", True),
+        _ptr(codes, s.W * s.N * s.d // 2, 1, "codes", True, True),
+        _ptr(bscale, s.W * s.N * s.d // 16, 1, "bscale", True, True),
+        _ptr(rscale, s.W * s.N, 4, "rscale", True, True), _ptr(C, s.W * s.K * s.d, 4, "C", True),
         _ptr(row_norm, s.W * s.N, 4, "row_norm", True),
         _ptr(H_hat, s.W * cap * s.d, e, "H_hat", True), _ptr(Kc, s.W * s.N * KV, e, "Kc", True),
         _ptr(Vc, s.W * s.N * KV, e, "Vc", True), _ptr(K_out, s.W * cap * KV, e, "K_out", True),

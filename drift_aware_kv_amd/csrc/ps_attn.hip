@@ -599,6 +599,7 @@ extern "C" const char* ps_status_string(ps_status st)
     case PS_ERR_RANGE: return "PS_ERR_RANGE: a scalar argument is out of range";
     case PS_ERR_WORKSPACE: return "PS_ERR_WORKSPACE: workspace missing or too small";
     case PS_ERR_DEVICE: return "PS_ERR_DEVICE: a HIP launch or runtime call failed";
+    case PS_ERR_MEMORY: return "PS_ERR_MEMORY: a buffer is neither device memory nor device-mapped pinned host memory";
     }
     return "unknown ps_status";
 }

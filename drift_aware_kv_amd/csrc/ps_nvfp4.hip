@@ -318,6 +318,31 @@ extern "C" ps_status ps_residual_nvfp4(const ps_shape* s, ps_dtype dtype, const 
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
 }
 
+namespace {
+
+// The address a kernel uses for a buffer it reads: device memory as it is,
+// pinned host memory through the device mapping of its allocation; anything
+// else (pageable host memory, unknown addresses) is refused before a launch.
+ps_status device_view(const void* p, const void** out)
+{
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return PS_ERR_MEMORY;
+    }
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+        *out = p;
+        return PS_OK;
+    }
+    if (a.type == hipMemoryTypeHost && a.devicePointer) {
+        *out = a.devicePointer;
+        return PS_OK;
+    }
+    return PS_ERR_MEMORY;
+}
+
+}  // namespace
+
 extern "C" ps_status ps_refresh_gather(const ps_shape* s, ps_dtype dtype, const int32_t* assign,
                                        const int32_t* idx, int32_t k, int32_t cap, int32_t* pos,
                                        int32_t* count, const uint8_t* codes, const uint8_t* bscale,
@@ -341,6 +366,15 @@ extern "C" ps_status ps_refresh_gather(const ps_shape* s, ps_dtype dtype, const 
     if ((Kc && (!aligned16(Kc) || !aligned16(K_out))) || (Vc && (!aligned16(Vc) || !aligned16(V_out))))
         return PS_ERR_ALIGN;
     if (s->W == 0) return PS_OK;
+    if (H_hat && cap > 0) {
+        const void *c = nullptr, *b = nullptr, *r = nullptr;
+        if ((st = device_view(codes, &c)) != PS_OK || (st = device_view(bscale, &b)) != PS_OK ||
+            (st = device_view(rscale, &r)) != PS_OK)
+            return st;
+        codes = (const uint8_t*)c;
+        bscale = (const uint8_t*)b;
+        rscale = (const float*)r;
+    }
     hipStream_t stm = (hipStream_t)stream;
     (void)hipGetLastError();
     PS_LAUNCH("k_gather_select", k_gather_select, dim3(s->W), dim3(64), 0, stm, assign, idx, k, cap, pos, count, s->N, s->K);

@@ -37,6 +37,13 @@ from . import (PS_BF16, PS_F32, PS_INIT_FARTHEST, PS_INIT_GIVEN, PS_INIT_STRIDED
 
 
 @dataclass
+class _Store:
+    codes: torch.Tensor
+    bscale: torch.Tensor
+    rscale: torch.Tensor
+
+
+@dataclass
 class StepSpec:
     W: int
     N: int
@@ -59,6 +66,7 @@ class StepSpec:
     alpha: float = 0.1
     tau_s: float = 0.9
     cluster_score: str = "kl"    # "kl" (drift share) or "cosine" (centre movement)
+    residual_store: str = "device"  # "device" (HBM) or "host" (pinned host memory)
 
     @property
     def shape(self) -> Shape:
@@ -87,6 +95,19 @@ class DriftPath:
         self.codes = torch.zeros(s.W, s.N, s.d // 2, dtype=torch.uint8, device=dev)
         self.bscale = torch.zeros(s.W, s.N, s.d // 16, dtype=torch.uint8, device=dev)
         self.rscale = torch.zeros(s.W, s.N, dtype=f32, device=dev)
+        if spec.residual_store not in ("device", "host"):
+            raise ValueError(f"residual_store must be 'device' or 'host', not {spec.residual_store!r}")
+        self.store = None
+        if spec.residual_store == "host":
+            # the pages' CPU offload: the quantised residual store lives in
+            # pinned host memory, written by a copy engine on its own stream
+            # while proxy attention and top-k run, and the gather fetches only
+            # the selected rows from it
+            self.store = dict(codes=torch.zeros(self.codes.shape, dtype=torch.uint8, pin_memory=True),
+                              bscale=torch.zeros(self.bscale.shape, dtype=torch.uint8, pin_memory=True),
+                              rscale=torch.zeros(self.rscale.shape, dtype=f32, pin_memory=True))
+            self.copy_stream = torch.cuda.Stream(device=dev)
+            self.coded, self.stored = torch.cuda.Event(), torch.cuda.Event()
         self.logp = [torch.zeros(s.W, s.Hq, s.Nb, s.K, dtype=f32, device=dev) for _ in range(2)]
         self.D_hi = torch.zeros(s.W, s.Hq, s.Nb, dtype=f32, device=dev)
         self.D_i = torch.zeros(s.W, s.Nb, dtype=f32, device=dev)
@@ -141,6 +162,14 @@ class DriftPath:
                       self.Ck, self.objective, self.ws, stream, flags=sp.kmeans_flags)
         ps_residual_nvfp4(s, dt, H, self.row_norm, self.C, self.assign, self.codes, self.bscale,
                           self.rscale, stream)
+        main = stream if stream is not None else torch.cuda.current_stream()
+        if self.store is not None and not first:     # formation gathers nothing
+            self.coded.record(main)
+            with torch.cuda.stream(self.copy_stream):
+                self.copy_stream.wait_event(self.coded)
+                for key in ("codes", "bscale", "rscale"):
+                    self.store[key].copy_(getattr(self, key), non_blocking=True)
+                self.stored.record(self.copy_stream)
         ps_proxy_attn(s, dt, Q, self.Ck, self.scale, self.logp_cur, None if first else self.logp_prev,
                       sp.score_kind, self.D_hi, self.D_i, self.score, stream)
         if not first:
@@ -150,9 +179,13 @@ class DriftPath:
                 score = self.score_cos
             ps_topk_clusters(s, score, sp.k, self.idx, self.val, stream)
             gather = self.K_out is not None
+            src = self
+            if self.store is not None:
+                main.wait_event(self.stored)
+                src = _Store(**self.store)
             ps_refresh_gather(s, dt, self.assign, self.idx, sp.k, self.cap,
-                              self.pos if self.cap > 0 else None, self.count, self.codes,
-                              self.bscale, self.rscale, self.C, self.row_norm, self.H_hat,
+                              self.pos if self.cap > 0 else None, self.count, src.codes,
+                              src.bscale, src.rscale, self.C, self.row_norm, self.H_hat,
                               Kr if gather else None, V if gather else None, self.K_out,
                               self.V_out, stream)
             if conf is not None:

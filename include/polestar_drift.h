@@ -53,7 +53,9 @@ typedef enum {
     PS_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned           */
     PS_ERR_RANGE = 5,     /* a scalar argument is out of range (iters, k, ...) */
     PS_ERR_WORKSPACE = 6, /* ws is NULL or smaller than ps_workspace_size      */
-    PS_ERR_DEVICE = 7     /* a HIP launch or runtime call failed               */
+    PS_ERR_DEVICE = 7,    /* a HIP launch or runtime call failed               */
+    PS_ERR_MEMORY = 8     /* a pointer the GPU must read is neither device
+                             memory nor pinned host memory mapped for it   */
 } ps_status;
 
 typedef enum { PS_F32 = 0, PS_BF16 = 1 } ps_dtype;
@@ -222,6 +224,12 @@ ps_status ps_topk_clusters(const ps_shape* shape, const float* score, int32_t k,
  *                              may be NULL when cap == 0
  *   count [W]      int32  out  true number of positions, even beyond cap
  *   codes, bscale, rscale, C, row_norm  (as ps_residual_nvfp4)        in
+ *         codes, bscale and rscale may instead sit in pinned host memory
+ *         (hipHostMalloc, mapped for the device): the pages keep the
+ *         quantised residual store in pinned CPU memory and fetch only the
+ *         selected clusters (section 2.C, CPU offloading); the kernel then
+ *         reads just the selected rows across PCIe through the allocation's
+ *         device mapping.  Other host memory gives PS_ERR_MEMORY.
  *   H_hat [W][cap][d] dtype out (nullable; needs the five inputs above):
  *         dtype((c + (e2m1 * s_b) * g_j) * n_j)
  *   Kc, Vc [W][N][Hkv][dh] dtype in (nullable) -> K_out, V_out

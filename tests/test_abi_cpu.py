@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIBPATH = os.path.join(ROOT, "drift_aware_kv_amd", "libpolestar_drift.so")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, RANGE, WORKSPACE, DEVICE = range(8)
+OK, NULL, SHAPE, DTYPE, ALIGN, RANGE, WORKSPACE, DEVICE, MEMORY = range(9)
 
 
 def declared_functions():
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_status_strings(L):
     import drift_aware_kv_amd as P
-    for st in range(8):
+    for st in range(9):
         assert P.status_string(st).startswith("PS_")
     assert "unknown" in P.status_string(99)
 
@@ -146,6 +146,12 @@ def test_topk_and_gather_argument_checks(L):
     assert g(Hh=FAKE) == NULL                              # H_hat needs the residual inputs
     assert L.ps_refresh_gather(ctypes.byref(_shape(W=0)), 1, FAKE, FAKE, 2, 0, None, FAKE, None,
                                None, None, None, None, None, None, None, None, None, None) == OK
+    # a residual store at an address that is neither device memory nor
+    # device-mapped pinned host memory is refused before any launch
+    host_buf = ctypes.create_string_buffer(1 << 12)
+    hb = ctypes.c_void_p((ctypes.addressof(host_buf) + 15) & ~15)
+    assert L.ps_refresh_gather(ctypes.byref(s), 1, FAKE, FAKE, 2, 8, FAKE, FAKE, hb, hb, hb, FAKE,
+                               FAKE, FAKE, None, None, None, None, None) == MEMORY
 
 
 def test_commit_argument_checks(L):

@@ -361,9 +361,21 @@ def test_topk_bit_exact(P, K, k):
     assert np.array_equal(host(val), r["val"], equal_nan=True)
 
 
-@pytest.mark.parametrize("bf", [True, False])
-@pytest.mark.parametrize("cap_mode", ["ample", "short", "zero"])
-def test_refresh_gather_bit_exact(P, bf, cap_mode):
+def pinned(a):
+    """A new pinned host tensor (hipHostMalloc) holding a copy of a."""
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    out = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    out.copy_(t)
+    return out
+
+
+@pytest.mark.parametrize("bf,cap_mode,store", [(True, "ample", "device"), (True, "short", "device"),
+                                               (True, "zero", "device"), (False, "ample", "device"),
+                                               (False, "short", "device"), (False, "zero", "device"),
+                                               (True, "ample", "host"), (False, "short", "host")])
+def test_refresh_gather_bit_exact(P, bf, cap_mode, store):
+    """Gather with the residual store in HBM or in pinned host memory (read
+    across PCIe through its device mapping)."""
     rng = np.random.default_rng(15)
     W, N, d, K, k, Hkv, dh = 3, 517, 96, 23, 4, 2, 16
     H32 = rng.standard_normal((W, N, d)).astype(np.float32)
@@ -389,9 +401,10 @@ def test_refresh_gather_bit_exact(P, bf, cap_mode):
     Hh = torch.zeros(W, max(cap, 1), d, dtype=et, device="cuda")
     Ko = torch.zeros(W, max(cap, 1), Hkv, dh, dtype=et, device="cuda")
     Vo = torch.zeros(W, max(cap, 1), Hkv, dh, dtype=et, device="cuda")
+    put = pinned if store == "host" else dev
     P.ps_refresh_gather(s, P.PS_BF16 if bf else P.PS_F32, dev(assign), dev(idx), k, cap,
-                        pos if cap else None, count, dev(q["codes"]), dev(q["bscale"]),
-                        dev(q["rscale"]), dev(C), dev(rn), Hh if cap else None,
+                        pos if cap else None, count, put(q["codes"]), put(q["bscale"]),
+                        put(q["rscale"]), dev(C), dev(rn), Hh if cap else None,
                         dev(Kc) if cap else None, dev(Vc) if cap else None,
                         Ko if cap else None, Vo if cap else None)
     torch.cuda.synchronize()

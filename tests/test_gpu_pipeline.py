@@ -190,7 +190,7 @@ def replay_first_difference(P, cfg, data, C_gpu, Ck_gpu, ost, t):
     raise AssertionError(f"step {t}: the step's assignment differs but no replayed iteration does")
 
 
-def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl"):
+def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl", residual_store="device"):
     """GPU DriftPath over `steps` steps with the commit rules; the oracle runs
     its own chain for each sampled window.  Returns the number of windows whose
     chains parted at a near-tie."""
@@ -200,7 +200,8 @@ def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl"):
     spec = StepSpec(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K,
                     k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
                     softmax_scale=cfg.softmax_scale, cap=cfg.N, block_start=cfg.block_start,
-                    alpha=ALPHA, tau_s=TAU_S, cluster_score=cluster_score)
+                    alpha=ALPHA, tau_s=TAU_S, cluster_score=cluster_score,
+                    residual_store=residual_store)
     path = DriftPath(spec)
     et = torch.bfloat16 if cfg.bf16 else torch.float32
     # device inputs: sampled windows from the generator, the rest random
@@ -276,6 +277,14 @@ def test_llada_layer_chained_cosine_score(P):
     cfg = synth.CONFIGS["C2"].with_(W=4)
     say("llada layer (cosine ranking): windows parted at a near-tie:",
         run_chained(P, cfg, steps=3, cluster_score="cosine"))
+
+
+def test_llada_layer_chained_host_residual_store(P):
+    """The same chain with the residual store in pinned host memory: the gather
+    fetches the selected rows across PCIe."""
+    cfg = synth.CONFIGS["C2"].with_(W=2)
+    say("llada layer (host residual store): windows parted at a near-tie:",
+        run_chained(P, cfg, steps=3, residual_store="host"))
 
 
 def test_dream_layer_chained(P):
