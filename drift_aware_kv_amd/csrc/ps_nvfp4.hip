@@ -4,10 +4,13 @@
 // the selected clusters (2.A, sparse updates; 2.C, only the selected clusters
 // are fetched), for gfx950.
 //
-// Both kernels are bandwidth bound: one workgroup per row, 16-byte coalesced
-// loads all issued before use, E4M3/E2M1 rounding in integer/fp32 arithmetic
-// (every fp32 step is one correctly rounded operation, matching the stated
-// convention bit for bit).
+// The coder gives each row four waves (one for short rows), with coalesced
+// 16-byte loads all issued before use and a single cross-wave exchange per
+// row.  Its fast path replaces divisions by reciprocal products and uses the
+// hardware E4M3/E2M1 conversions, each proven or exhaustively checked to give
+// the results of the stated convention (every fp32 step one correctly rounded
+// operation) bit for bit; rows outside the proof's conditions take the exact
+// path.  The gather is bandwidth bound: one workgroup per selected row.
 #include "ps_common.h"
 
 using namespace ps;
@@ -15,21 +18,28 @@ using namespace ps;
 namespace {
 
 // Quotients on the fast path: for fp32 a and b, the fp32 rounding of
-// a * RN64(1/b) equals the correctly rounded fp32 quotient a / b whenever that
-// quotient is zero or at least 2^-125 in magnitude.  A quotient that is not an
-// fp32 number lies at least 2^-49 (relative) from every fp32 rounding
-// midpoint (with m a midpoint of 25 significant bits, a - m*b is a non-zero
-// multiple of 2^(e_m + e_b - 47), since a has at most 24 significant bits),
-// while the fp64 product is within 2^-52 of a / b.  Below the normal range the
-// midpoints are coarser than that argument covers; such a row is redone with
-// divisions (`exact`).  A quotient a / b is below 2^-125 exactly when
-// 0 < |a| < 2^-125 * b, which is what the fast path tests.
+// a * y, with y within 2^-51 (relative) of 1/b, equals the correctly rounded
+// fp32 quotient a / b whenever that quotient is zero or at least 2^-125 in
+// magnitude.  A quotient that is not an fp32 number lies at least 2^-49
+// (relative) from every fp32 rounding midpoint (with m a midpoint of 25
+// significant bits, a - m*b is a non-zero multiple of 2^(e_m + e_b - 47),
+// since a has at most 24 significant bits), while the fp64 product is within
+// 2^-50 of a / b.  y is RN64(1/b) for the row-wide divisors (the norm n, the
+// row scale g, the constant 6) and, per block, the fp32 reciprocal estimate of
+// eff refined by three Newton steps in fp64 (relative error below 2^-52 from
+// any start better than 2^-12).  Below the normal range the midpoints are
+// coarser than that argument covers: a row with a non-zero |h| or |r| whose
+// exponent is 125 or more below its divisor's, or subnormal, is redone with
+// divisions (`residual_row_exact`); so is a row with a non-finite residual or
+// with a largest |r| below 2^-100, under which the block-scale quotients lose
+// their margin.  With max |r| >= 2^-100 a block whose Ab/6 is below 2^-125
+// has (Ab/6)/g below 2^-13, which encodes to the E4M3 zero either way.
 //
 // E2M1 rounding on the fast path uses gfx950's fp32 -> fp4 conversion with
 // scale 1.0: checked exhaustively over every finite fp32 input, it returns the
 // nearest-even, saturating E2M1 code of the convention except that a negative
 // input rounding to zero comes back as -0 (nibble 0x8); `plus_zero` clears
-// those signs.  Non-finite inputs are sent to the exact path.
+// those signs.
 __device__ __forceinline__ uint32_t plus_zero(uint32_t w)
 {
     const uint32_t m = w & 0x77777777u;                              // magnitudes
@@ -37,121 +47,73 @@ __device__ __forceinline__ uint32_t plus_zero(uint32_t w)
     return m | (w & (nz << 3));
 }
 
-// NVFP4 coding of one row by one workgroup of TPR threads (one or four
-// waves).  Thread i holds 8-element chunks i, i+TPR, ...; a 16-element block
-// is the chunk pair (2m, 2m+1), i.e. threads i and i^1 of one wave.  All of a
-// thread's loads are issued before any use.  With exact = false the quotients
-// are fp64 products and E2M1 uses the hardware conversion; the function
-// returns false without writing anything if any quotient of the row is tiny
-// or any value is non-finite (decided by a workgroup vote).
-template <typename T, int TPR, int CPL, bool exact>
-__device__ __forceinline__ bool residual_row(const T* __restrict__ h, const float* __restrict__ c, float n,
-                                             uint8_t* __restrict__ cr, uint8_t* __restrict__ br,
-                                             float* __restrict__ rs, int d, float* red)
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v)
 {
-    constexpr int NW = TPR / 64;
-    const int tid = threadIdx.x, wave = tid >> 6;
-    const int nch = d >> 3;
-    const bool full = nch == TPR * CPL;          // every chunk of every thread is in the row
-    const bool pos_n = n > 0.0f;                 // row-uniform
-    const double inv_n = pos_n ? 1.0 / (double)n : 0.0;
-    const float t1 = n * 0x1p-125f;              // |h| below this: tiny quotient
-    bool bad = false;
-    // chunks past the row read the last chunk again (always in bounds) and
-    // are masked to zero; bf16 chunks stay packed until used
-    constexpr bool packed = sizeof(T) == 2;
-    uint4 hq[CPL][packed ? 1 : 2];
-    float r[CPL][8];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, 64));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m, 64));
+    return v;
+}
+
+// a non-zero magnitude (fp32 bits) too small against a divisor (fp32 bits)
+// for the reciprocal-product argument: subnormal, or 125+ binades below
+__device__ __forceinline__ bool tiny_against(uint32_t mag, uint32_t div)
+{
+    const int e = (int)(mag >> 23);
+    return mag != 0u && (e == 0 || e + 125 <= (int)(div >> 23));
+}
+
+// One row is coded by NW waves (TPR = 64 * NW threads).  Thread i of the row
+// owns the 8-element chunks i, i + TPR, ..., so each load instruction of a wave
+// covers 64 consecutive chunks; a 16-element block is the chunk pair held by
+// threads 2m and 2m + 1 (adjacent lanes).  Chunks past the row read the last
+// chunk again (always in bounds) and are masked.
+template <typename T, int TPR, int CPL>
+__device__ __forceinline__ void load_chunks(const T* __restrict__ h, const float* __restrict__ c, int tid,
+                                            int nch, uint4 (&hq)[CPL][sizeof(T) == 2 ? 1 : 2],
+                                            float (&r)[CPL][8])
+{
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int ch = min(tid + TPR * i, nch - 1);
         const uint4* hp = reinterpret_cast<const uint4*>(h + 8 * ch);
         hq[i][0] = hp[0];
-        if (!packed) hq[i][packed ? 0 : 1] = hp[1];
-        load8(c + 8 * ch, r[i]);
+        if (sizeof(T) != 2) hq[i][sizeof(T) == 2 ? 0 : 1] = hp[1];
+        const float4* cp = reinterpret_cast<const float4*>(c + 8 * ch);
+        const float4 a = cp[0], b = cp[1];
+        r[i][0] = a.x; r[i][1] = a.y; r[i][2] = a.z; r[i][3] = a.w;
+        r[i][4] = b.x; r[i][5] = b.y; r[i][6] = b.z; r[i][7] = b.w;
     }
-    float A = 0.0f;
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack8(const uint4 (&q)[sizeof(T) == 2 ? 1 : 2], float (&hv)[8])
+{
+    if (sizeof(T) == 2) {
+        const uint32_t w[4] = {q[0].x, q[0].y, q[0].z, q[0].w};
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const bool valid = full || tid + TPR * i < nch;
-        float hv[8];
-        if (packed) {
-            const uint32_t w4[4] = {hq[i][0].x, hq[i][0].y, hq[i][0].z, hq[i][0].w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                hv[2 * t] = __uint_as_float(w4[t] << 16);
-                hv[2 * t + 1] = __uint_as_float(w4[t] & 0xffff0000u);
-            }
-        } else {
-            const uint4 a = hq[i][0], b = hq[i][packed ? 0 : 1];
-            const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) hv[t] = __uint_as_float(w8[t]);
+        for (int t = 0; t < 4; ++t) {
+            hv[2 * t] = __uint_as_float(w[t] << 16);
+            hv[2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
         }
+    } else {
+        const uint4 a = q[0], b = q[sizeof(T) == 2 ? 0 : 1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            float x = 0.0f;
-            if (pos_n) {
-                if (exact) {
-                    x = hv[t] / n;
-                } else {
-                    x = (float)((double)hv[t] * inv_n);
-                    bad |= (fabsf(hv[t]) < t1) & (hv[t] != 0.0f);
-                }
-            }
-            r[i][t] = valid ? x - r[i][t] : 0.0f;
-            A = fmaxf(A, fabsf(r[i][t]));
-        }
+        for (int t = 0; t < 8; ++t) hv[t] = __uint_as_float(w[t]);
     }
-    A = wave_max(A);
-    if (NW > 1) {
-        if ((tid & 63) == 0) red[wave] = A;
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < NW; ++q) A = fmaxf(A, red[q]);
-    }
-    const bool zero_row = !(A > 0.0f);
-    const float g = A / 2688.0f;
-    uint32_t words[CPL], scales[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        float Ab = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) Ab = fmaxf(Ab, fabsf(r[i][t]));
-        Ab = fmaxf(Ab, __shfl_xor(Ab, 1, 64));
-        uint32_t word = 0, sb = 0;
-        if (!zero_row) {
-            sb = e4m3_encode((Ab / 6.0f) / g);
-            const float eff = e4m3_decode(sb) * g;
-            if (eff != 0.0f) {
-                if (exact) {
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) word |= e2m1_encode(r[i][t] / eff) << (4 * t);
-                } else {
-                    const double inv_eff = 1.0 / (double)eff;
-                    const float t2 = eff * 0x1p-125f, big = eff * 8.0f;
-                    float v[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const float a = fabsf(r[i][t]);
-                        bad |= ((a < t2) & (r[i][t] != 0.0f)) | !(a <= big);
-                        v[t] = (float)((double)r[i][t] * inv_eff);
-                    }
-                    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], 1.0f, 0);
-                    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], 1.0f, 1);
-                    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], 1.0f, 2);
-                    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], 1.0f, 3);
-                    word = plus_zero(word);
-                }
-            }
-        }
-        words[i] = word;
-        scales[i] = sb;
-    }
-    if (!exact) {
-        const bool any_bad = NW > 1 ? __syncthreads_or(bad) != 0 : __any(bad) != 0;
-        if (any_bad) return false;
-    }
+}
+
+template <int TPR, int CPL>
+__device__ __forceinline__ void store_chunks(const uint32_t (&words)[CPL], const uint32_t (&scales)[CPL],
+                                             int tid, int nch, uint8_t* __restrict__ cr, uint8_t* __restrict__ br)
+{
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int ch = tid + TPR * i;
@@ -160,21 +122,215 @@ __device__ __forceinline__ bool residual_row(const T* __restrict__ h, const floa
             if (!(ch & 1)) br[ch >> 1] = (uint8_t)scales[i];
         }
     }
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// the partner lane's value within a lane pair (DPP quad permutation 1,0,3,2)
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ u16x2 wave_min_u16x2(u16x2 v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v = __builtin_elementwise_min(v, __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, v), m, 64)));
+    return v;
+}
+
+// Fast NVFP4 coding of one row: reciprocal products instead of divisions, the
+// hardware E4M3 and E2M1 conversions (checked exhaustively against the
+// software rounding: E4M3 over every fp32 in [0, 464), which holds every block
+// scale quotient, E2M1 over every finite fp32), and the checks folded into
+// integer max/min over magnitude bit patterns (which also catch NaN and
+// infinity).  The row's largest |r| and smallest non-zero |h| are combined in
+// one exchange; from them every thread takes the same decision whether the
+// row needs the exact path, before any block is coded.  Quotients r/eff below
+// 2^-125 need no check: they encode to the E2M1 zero however they round.
+// Returns false without writing anything when the exact path is needed.
+template <typename T, int NW, int CPL, bool FULL>
+__device__ __forceinline__ bool residual_row_fast(const T* __restrict__ h, const float* __restrict__ c, float n,
+                                                  uint8_t* __restrict__ cr, uint8_t* __restrict__ br,
+                                                  float* __restrict__ rs, int d, uint32_t (*red)[3])
+{
+    constexpr int TPR = 64 * NW;
+    constexpr bool packed = sizeof(T) == 2;
+    if (!(n > 0.0f) || n == INFINITY) return false;   // row-uniform: zero, negative or non-finite norm
+    const int tid = (int)(threadIdx.x % TPR), wave = tid >> 6;
+    const int nch = d >> 3;
+    const double inv_n = 1.0 / (double)n;
+    uint4 hq[CPL][packed ? 1 : 2];
+    float r[CPL][8];
+    load_chunks<T, TPR, CPL>(h, c, tid, nch, hq, r);
+    uint32_t cmax[CPL];
+    u16x2 hmin2 = {0xffff, 0xffff};              // bf16: smallest non-zero |h|, minus one, per half
+    uint32_t hmin = ~0u;                         // fp32: the same over fp32 bit patterns
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const bool valid = FULL || tid + TPR * i < nch;
+        if (packed) {
+            const uint32_t w4[4] = {hq[i][0].x, hq[i][0].y, hq[i][0].z, hq[i][0].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                hmin2 = __builtin_elementwise_min(
+                    hmin2, __builtin_bit_cast(u16x2, w4[t] & 0x7fff7fffu) - (u16x2){1, 1});
+        }
+        float hv[8];
+        unpack8<T>(hq[i], hv);
+        float m = 0.0f;                          // NaN-propagating max of |r|
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (!packed) hmin = min(hmin, (__float_as_uint(hv[t]) & 0x7fffffffu) - 1u);
+            float rv = (float)((double)hv[t] * inv_n) - r[i][t];
+            if (!FULL) rv = valid ? rv : 0.0f;
+            r[i][t] = rv;
+            m = __builtin_elementwise_maximum(m, fabsf(rv));
+        }
+        cmax[i] = __float_as_uint(m);            // non-negative: bit order is value order, NaN on top
+    }
+    uint32_t Am = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) Am = max(Am, cmax[i]);
+    Am = wave_max_u(Am);
+    uint32_t hm;                                 // smallest non-zero |h| minus one, fp32-bit order
+    if (packed) {
+        hmin2 = wave_min_u16x2(hmin2);
+        const uint32_t m16 = min((uint32_t)hmin2.x, (uint32_t)hmin2.y);
+        hm = m16 == 0xffffu ? ~0u : ((m16 + 1u) << 16) - 1u;
+    } else {
+        hm = wave_min_u(hmin);
+    }
+    if (NW > 1) {
+        if ((tid & 63) == 0) {
+            red[wave][0] = Am;
+            red[wave][1] = hm;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+            Am = max(Am, red[q][0]);
+            hm = min(hm, red[q][1]);
+        }
+    }
+    // row-uniform decision
+    if (Am >= 0x7f800000u) return false;                 // a NaN or infinite residual
+    const bool zero_row = Am == 0u;
+    if (!zero_row && Am < 0x0d800000u) return false;     // max |r| below 2^-100
+    if (tiny_against(hm + 1u, __float_as_uint(n))) return false;
+    const float g = __uint_as_float(Am) / 2688.0f;
+    const double inv_g = zero_row ? 0.0 : 1.0 / (double)g;
+    uint32_t words[CPL], scales[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const uint32_t bm = max(cmax[i], pair_swap(cmax[i]));   // the block's max
+        uint32_t word = 0, sb = 0;
+        if (!zero_row) {
+            const float q1 = (float)((double)__uint_as_float(bm) * (1.0 / 6.0));
+            const float q2 = (float)((double)q1 * inv_g);
+            sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q2, 0, false) & 0xffu;
+            const float eff = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
+            if (eff != 0.0f) {
+                const double e64 = (double)eff;
+                double y = (double)__builtin_amdgcn_rcpf(eff);
+#pragma unroll
+                for (int it = 0; it < 3; ++it) y = fma(y, fma(-e64, y, 1.0), y);
+                float v[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] = (float)((double)r[i][t] * y);
+                word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], 1.0f, 0);
+                word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], 1.0f, 1);
+                word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], 1.0f, 2);
+                word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], 1.0f, 3);
+                word = plus_zero(word);
+            }
+        }
+        words[i] = word;
+        scales[i] = sb;
+    }
+    store_chunks<TPR, CPL>(words, scales, tid, nch, cr, br);
     if (tid == 0) *rs = zero_row ? 0.0f : g;
     return true;
 }
 
-// One workgroup per row; consecutive rows (one window's, sharing its centres)
-// stay on one XCD.
-template <typename T, int TPR, int CPL>
-__global__ __launch_bounds__(TPR) void k_residual(const T* __restrict__ H, const float* __restrict__ row_norm,
+// Exact NVFP4 coding of one row: every quotient a correctly rounded fp32
+// division, E2M1 by threshold comparison (the rows the fast path declines).
+template <typename T, int NW, int CPL>
+__device__ __forceinline__ void residual_row_exact(const T* __restrict__ h, const float* __restrict__ c, float n,
+                                                   uint8_t* __restrict__ cr, uint8_t* __restrict__ br,
+                                                   float* __restrict__ rs, int d, uint32_t (*red)[3])
+{
+    constexpr int TPR = 64 * NW;
+    const int tid = (int)(threadIdx.x % TPR), wave = tid >> 6;
+    const int nch = d >> 3;
+    const bool full = nch == TPR * CPL;
+    const bool pos_n = n > 0.0f;
+    uint4 hq[CPL][sizeof(T) == 2 ? 1 : 2];
+    float r[CPL][8];
+    load_chunks<T, TPR, CPL>(h, c, tid, nch, hq, r);
+    float cmax[CPL];
+    float A = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const bool valid = full || tid + TPR * i < nch;
+        float hv[8];
+        unpack8<T>(hq[i], hv);
+        float m = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float x = pos_n ? hv[t] / n : 0.0f;
+            r[i][t] = valid ? x - r[i][t] : 0.0f;
+            m = fmaxf(m, fabsf(r[i][t]));
+        }
+        cmax[i] = m;
+        A = fmaxf(A, m);
+    }
+    A = wave_max(A);
+    if (NW > 1) {
+        if ((tid & 63) == 0) red[wave][0] = __float_as_uint(A);
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NW; ++q) A = fmaxf(A, __uint_as_float(red[q][0]));
+    }
+    const bool zero_row = !(A > 0.0f);
+    const float g = A / 2688.0f;
+    uint32_t words[CPL], scales[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const float Ab = fmaxf(cmax[i], __shfl_xor(cmax[i], 1, 64));
+        uint32_t word = 0, sb = 0;
+        if (!zero_row) {
+            sb = e4m3_encode((Ab / 6.0f) / g);
+            const float eff = e4m3_decode(sb) * g;
+            if (eff != 0.0f) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) word |= e2m1_encode(r[i][t] / eff) << (4 * t);
+            }
+        }
+        words[i] = word;
+        scales[i] = sb;
+    }
+    store_chunks<TPR, CPL>(words, scales, tid, nch, cr, br);
+    if (tid == 0) *rs = zero_row ? 0.0f : g;
+}
+
+// NW waves per row, 4 / NW rows per 256-thread workgroup; one exchange (and
+// with one wave per row, none) per row.  Consecutive rows (one window's,
+// sharing its centres) stay on one XCD.
+template <typename T, int NW, int CPL, bool FULL>
+__global__ __launch_bounds__(256) void k_residual(const T* __restrict__ H, const float* __restrict__ row_norm,
                                                    const float* __restrict__ C, const int32_t* __restrict__ assign,
                                                    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscale,
-                                                   float* __restrict__ rscale, int N, int d, int K)
+                                                   float* __restrict__ rscale, int64_t rows, int N, int d, int K)
 {
-    __shared__ float red[TPR / 64];
-    const int64_t row = xcd_remap(blockIdx.x, gridDim.x);
-    const int w = (int)(row / N);
+    constexpr int RPB = 4 / NW;                  // rows per workgroup
+    __shared__ uint32_t red[4][3];
+    const int64_t row = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * RPB + (RPB > 1 ? (int)(threadIdx.x / (64 * NW)) : 0);
+    // with one row per workgroup every thread has the same row; with several,
+    // a whole wave leaves together and no barrier follows on this path
+    if (row >= rows) return;
+    const int w = rows < ((int64_t)1 << 32) ? (int)((uint32_t)row / (uint32_t)N) : (int)(row / N);
     int a = assign[row];
     if (a < 0 || a >= K) a = 0;
     const float* c = C + ((size_t)w * K + a) * d;
@@ -182,9 +338,9 @@ __global__ __launch_bounds__(TPR) void k_residual(const T* __restrict__ H, const
     uint8_t* cr = codes + (size_t)row * (d >> 1);
     uint8_t* br = bscale + (size_t)row * (d >> 4);
     const float n = row_norm[row];
-    if (!residual_row<T, TPR, CPL, false>(h, c, n, cr, br, rscale + row, d, red)) {
-        __syncthreads();  // red[] is reused
-        residual_row<T, TPR, CPL, true>(h, c, n, cr, br, rscale + row, d, red);
+    if (!residual_row_fast<T, NW, CPL, FULL>(h, c, n, cr, br, rscale + row, d, red)) {
+        if (NW > 1) __syncthreads();  // red[] is reused
+        residual_row_exact<T, NW, CPL>(h, c, n, cr, br, rscale + row, d, red);
     }
 }
 
@@ -274,25 +430,32 @@ __global__ __launch_bounds__(256) void k_gather_rows(const int32_t* __restrict__
     }
 }
 
-template <typename T, int TPR, int CPL>
+template <typename T, int NW, int CPL>
 void launch_residual(const ps_shape* s, const void* H, const float* rn, const float* C, const int32_t* a,
                      uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t st)
 {
     const int64_t rows = (int64_t)s->W * s->N;
-    PS_LAUNCH("k_residual<T, TPR, CPL>", (k_residual<T, TPR, CPL>), dim3((unsigned)rows), dim3(TPR), 0, st,
-              (const T*)H, rn, C, a, codes, bscale, rscale, s->N, s->d, s->K);
+    const int rpb = 4 / NW;
+    const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+    if (s->d / 8 == 64 * NW * CPL)
+        PS_LAUNCH("k_residual<T, NW, CPL, FULL>", (k_residual<T, NW, CPL, true>), grid, dim3(256), 0, st,
+                  (const T*)H, rn, C, a, codes, bscale, rscale, rows, s->N, s->d, s->K);
+    else
+        PS_LAUNCH("k_residual<T, NW, CPL, FULL>", (k_residual<T, NW, CPL, false>), grid, dim3(256), 0, st,
+                  (const T*)H, rn, C, a, codes, bscale, rscale, rows, s->N, s->d, s->K);
 }
 
-// rows of at most 512 elements: one wave per row; longer rows: four waves
+// rows of up to 512 elements: one wave per row; longer rows (up to 8192
+// elements): four waves, 1 to 4 chunks of 8 elements per thread
 template <typename T>
 void dispatch_residual(const ps_shape* s, const void* H, const float* rn, const float* C, const int32_t* a,
                        uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t st)
 {
     const int nch = s->d / 8;
-    if (nch <= 64)        launch_residual<T, 64, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else if (nch <= 256)  launch_residual<T, 256, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else if (nch <= 512)  launch_residual<T, 256, 2>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else                  launch_residual<T, 256, 4>(s, H, rn, C, a, codes, bscale, rscale, st);
+    if (nch <= 64)        launch_residual<T, 1, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
+    else if (nch <= 256)  launch_residual<T, 4, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
+    else if (nch <= 512)  launch_residual<T, 4, 2>(s, H, rn, C, a, codes, bscale, rscale, st);
+    else                  launch_residual<T, 4, 4>(s, H, rn, C, a, codes, bscale, rscale, st);
 }
 
 }  // namespace
