@@ -334,6 +334,195 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
     }
 }
 
+// ---------------------------------------------------------------------------
+// assignment, bf16, K > 128: a 512-thread workgroup owns 256 tokens and runs
+// over the clusters 256 at a time.  Wave v (0..7) computes clusters
+// [64 * (v & 3), +64) of the group against tokens [128 * (v >> 2), +128) of
+// the tile: 4 x 8 MFMA blocks of 16x16.  Both operands are staged through
+// LDS in 64-wide d-chunks, each chunk loaded once for the eight waves
+// (double-buffered, padded 144-byte rows); per chunk a wave reads 8 KB of
+// centre and 16 KB of token fragments for 64 MFMAs, so neither LDS nor the
+// centre traffic per token limits the MFMA rate.  Each score accumulates over
+// d in the same ascending order as in the smaller kernel, so the scores, and
+// the argmax, are identical.
+// ---------------------------------------------------------------------------
+constexpr int kWideTok = 256;                  // tokens per workgroup
+constexpr int kWideCl = 256;                   // clusters per pass
+constexpr int kWideDK = 64;                    // d elements per chunk
+constexpr int kWideRowB = kWideDK * 2 + 16;    // padded LDS row (bytes)
+constexpr int kWideTile = 256 * kWideRowB;     // one operand tile
+constexpr size_t kWideLds = 4 * (size_t)kWideTile;  // centre and token tiles, two buffers
+
+template <bool FIRST>
+__global__ __launch_bounds__(512) void k_assign_wide(const uint16_t* __restrict__ H,
+                                                      const uint16_t* __restrict__ Cb,
+                                                      int32_t* __restrict__ assign,
+                                                      float* __restrict__ row_norm, int N, int d, int K,
+                                                      int tiles, int nblocks, int32_t* __restrict__ dirty,
+                                                      const int32_t* __restrict__ conv)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t wlds[];
+    constexpr int NS = kWideDK / 32;
+    const int L = xcd_remap(blockIdx.x, nblocks);
+    const int w = L / tiles, tile = L - w * tiles;
+    if (!FIRST && conv[w]) return;  // window at a fixed point: nothing can change
+    const int tid = threadIdx.x, lane = lane_id(), v = tid >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int cq = v & 3, th = v >> 2;
+    const int tok0 = tile * kWideTok;
+    const uint16_t* Hw = H + (size_t)w * N * d;
+    const uint16_t* Cw = Cb + (size_t)w * K * d;
+    const int nchunks = (d + kWideDK - 1) / kWideDK;
+
+    // staging: thread t moves the 16-byte pieces t + 512 u (u < 4) of each
+    // 256-row tile: row (t >> 3) + 64 u, columns 8 (t & 7) .. + 8
+    const int srow = tid >> 3, scol = (tid & 7) * 8;
+    double ss[4] = {0.0, 0.0, 0.0, 0.0};  // first pass: sums of squares of the 4 token rows
+
+    float bestv[8];
+    int besti[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) { bestv[nt] = -INFINITY; besti[nt] = 0; }
+
+    for (int cg = 0; cg < K; cg += kWideCl) {
+        const bool norm_pass = FIRST && cg == 0;
+        floatx4 acc[4][8];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) acc[mb][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        uint4 cpre[4], hpre[4];
+        auto load = [&](int c0) {
+            const int e = c0 + scol;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int row = srow + 64 * u;
+                const int cl = cg + row, tk = tok0 + row;
+                cpre[u] = (cl < K && e < d) ? *reinterpret_cast<const uint4*>(Cw + (size_t)cl * d + e)
+                                            : make_uint4(0, 0, 0, 0);
+                hpre[u] = (tk < N && e < d) ? *reinterpret_cast<const uint4*>(Hw + (size_t)tk * d + e)
+                                            : make_uint4(0, 0, 0, 0);
+            }
+        };
+        auto store = [&](int buf) {
+            uint8_t* cbuf = wlds + (size_t)buf * 2 * kWideTile;
+            uint8_t* hbuf = cbuf + kWideTile;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int off = (srow + 64 * u) * kWideRowB + scol * 2;
+                *reinterpret_cast<uint4*>(cbuf + off) = cpre[u];
+                *reinterpret_cast<uint4*>(hbuf + off) = hpre[u];
+                if (norm_pass) {
+                    const uint32_t wv[4] = {hpre[u].x, hpre[u].y, hpre[u].z, hpre[u].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const double lo = (double)__uint_as_float(wv[i] << 16);
+                        const double hi = (double)__uint_as_float(wv[i] & 0xffff0000u);
+                        ss[u] = fma(lo, lo, ss[u]);
+                        ss[u] = fma(hi, hi, ss[u]);
+                    }
+                }
+            }
+        };
+        load(0);
+        store(0);
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            const bool more = c + 1 < nchunks;
+            if (more) load((c + 1) * kWideDK);
+            const uint8_t* cbuf = wlds + (size_t)(c & 1) * 2 * kWideTile;
+            const uint8_t* hbuf = cbuf + kWideTile;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                bf16x8 a[4];
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+                    a[mb] = *reinterpret_cast<const bf16x8*>(cbuf + (64 * cq + 16 * mb + r16) * kWideRowB +
+                                                              64 * s + 16 * q);
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) {
+                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(
+                        hbuf + (128 * th + 16 * nt + r16) * kWideRowB + 64 * s + 16 * q);
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+                        acc[mb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[mb][nt], 0, 0, 0);
+                }
+            }
+            if (more) store((c + 1) & 1);
+            __syncthreads();
+        }
+        // merge this group's scores (ascending cluster order within a lane;
+        // strict > keeps the lowest index)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int cl = cg + 64 * cq + 16 * mb + 4 * q + r;
+                    const float sv = acc[mb][nt][r];
+                    if (cl < K && sv > bestv[nt]) { bestv[nt] = sv; besti[nt] = cl; }
+                }
+    }
+    // the four lanes (q) of a token, then the four cluster quarters (waves)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int m = 16; m <= 32; m <<= 1) {
+            const float ov = __shfl_xor(bestv[nt], m, 64);
+            const int oi = __shfl_xor(besti[nt], m, 64);
+            if (ov > bestv[nt] || (ov == bestv[nt] && oi < besti[nt])) { bestv[nt] = ov; besti[nt] = oi; }
+        }
+    float* bv = reinterpret_cast<float*>(wlds);             // [2][4][128]; the tiles are free now
+    int* bi = reinterpret_cast<int*>(wlds + 4096);
+    if (q == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const int t = (th * 4 + cq) * 128 + 16 * nt + r16;
+            bv[t] = bestv[nt];
+            bi[t] = besti[nt];
+        }
+    }
+    if (FIRST) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int m = 1; m <= 4; m <<= 1) ss[u] += shfl_xor_d(ss[u], m);
+    }
+    __syncthreads();
+    if (FIRST && (tid & 7) == 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int tk = tok0 + srow + 64 * u;
+            if (tk < N) row_norm[(size_t)w * N + tk] = (float)sqrt(ss[u]);
+        }
+    }
+    if (tid < kWideTok) {
+        const int tk = tok0 + tid;
+        if (tk < N) {
+            const int h2 = tid >> 7, tt = tid & 127;
+            float best = bv[(h2 * 4) * 128 + tt];
+            int bidx = bi[(h2 * 4) * 128 + tt];
+#pragma unroll
+            for (int cqq = 1; cqq < 4; ++cqq) {
+                const float ov = bv[(h2 * 4 + cqq) * 128 + tt];
+                const int oi = bi[(h2 * 4 + cqq) * 128 + tt];
+                if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+            }
+            int32_t* ap = assign + (size_t)w * N + tk;
+            if (!FIRST) {
+                // membership changed: both clusters must be recomputed
+                const int old = *ap;
+                if (old != bidx) {
+                    if (old >= 0 && old < K) dirty[(size_t)w * K + old] = 1;
+                    dirty[(size_t)w * K + bidx] = 1;
+                }
+            }
+            *ap = bidx;
+        }
+    }
+}
+
 // assignment, fp32 path (exact centres): one thread per row
 __global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ H, const float* __restrict__ C,
                                                      int32_t* __restrict__ assign,
@@ -649,6 +838,19 @@ void launch_update(const ps_shape* s, const void* H, const float* rn, const KmWs
                        ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, s->N, s->d, s->K, nblocks, all);
 }
 
+template <bool FIRST>
+void launch_assign_wide(const ps_shape* s, const void* H, const KmWs& ws, int32_t* assign, float* rn,
+                        hipStream_t st)
+{
+    const int tiles = (s->N + kWideTok - 1) / kWideTok;
+    const int nblocks = s->W * tiles;
+    (void)hipFuncSetAttribute((const void*)k_assign_wide<FIRST>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kWideLds);
+    PS_LAUNCH(FIRST ? "k_assign_wide<true>" : "k_assign_wide<false>", k_assign_wide<FIRST>, dim3(nblocks),
+              dim3(512), kWideLds, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks,
+              ws.dirty, ws.conv);
+}
+
 template <int KB, int NB>
 void launch_assign_bf16(const ps_shape* s, const void* H, const float* C, const KmWs& ws, int32_t* assign,
                         float* rn, int first, hipStream_t st)
@@ -732,7 +934,8 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
             else if (KBn <= 2) launch_assign_bf16<2, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
             else if (KBn <= 4) launch_assign_bf16<4, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
             else if (KBn <= 8) launch_assign_bf16<8, PS_ASSIGN_NB_LARGEK>(s, H, C, L, assign, row_norm, first, stm);
-            else               launch_assign_bf16<16, PS_ASSIGN_NB_LARGEK>(s, H, C, L, assign, row_norm, first, stm);
+            else if (first)    launch_assign_wide<true>(s, H, L, assign, row_norm, stm);
+            else               launch_assign_wide<false>(s, H, L, assign, row_norm, stm);
         } else {
             const int64_t rows = (int64_t)W * N;
             PS_LAUNCH("k_assign_f32", k_assign_f32, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stm,
