@@ -277,3 +277,51 @@ def test_update_step_alone_matches_fit_and_member_means():
     assert np.array_equal(u["C"][0, K - 1], C0[0, K - 1]) and u["counts"][0, K - 1] == 0
     with pytest.raises(O.OracleError):
         O.kmeans_update(s, O.BF16, H, r["row_norm"], np.full((1, N), K, np.int32), C0)
+
+
+def test_assignment_ties_go_to_lowest_index():
+    """Exactly equal scores (a duplicated centre, a row equidistant from two
+    centres) go to the lowest cluster index."""
+    d = 16
+    e = np.eye(d, dtype=np.float32)
+    H = np.stack([e[1], e[1] + e[0], e[2], e[0]])[None].astype(np.float32)      # [1][4][16]
+    C = np.stack([e[0], e[1], e[1], e[2]])[None].astype(np.float32)             # centres 1 and 2 identical
+    s = O.Shape(W=1, N=4, d=d, K=4)
+    r = O.kmeans_fit(s, O.F32, H, None, O.INIT_GIVEN, 1, C.copy())
+    # row 0 = e1: ties between centres 1 and 2 -> 1; row 1 = e0 + e1: ties
+    # between 0 (score 1) and 1, 2 (score 1) -> 0; row 2 = e2 -> 3; row 3 = e0 -> 0
+    assert r["assign"][0].tolist() == [1, 0, 3, 0]
+
+
+def test_assignment_uses_bf16_rounded_centres():
+    """On the bf16 path the scores use the centres rounded to bf16: two centres
+    whose first components 1.00389 and 1.0039 both round to 1.0 tie, so the
+    lower index wins, although the unrounded second centre scores higher."""
+    d = 16
+    H32 = np.zeros((1, 2, d), np.float32)
+    H32[0, :, 0] = 1.0
+    H = O.f32_to_bf16(H32)
+    C = np.zeros((1, 2, d), np.float32)
+    C[0, 0, 0] = np.float32(1.00389)
+    C[0, 1, 0] = np.float32(1.0039)
+    assert O.bf16_to_f32(O.f32_to_bf16(C[0, :, 0])).tolist() == [1.0, 1.0]
+    s = O.Shape(W=1, N=2, d=d, K=2)
+    r = O.kmeans_fit(s, O.BF16, H, None, O.INIT_GIVEN, 1, C.copy())
+    assert r["assign"][0].tolist() == [0, 0]
+    rf = O.kmeans_fit(s, O.F32, H32, None, O.INIT_GIVEN, 1, C.copy())
+    assert rf["assign"][0].tolist() == [1, 1]            # fp32 path: no rounding, the larger wins
+
+
+def test_singleton_cluster_centre_is_its_row():
+    """A cluster with one member moves to that member's unit row, whatever
+    centre it started from."""
+    d = 16
+    e = np.eye(d, dtype=np.float32)
+    H = np.stack([e[0] + 0.25 * e[2], e[1] - 0.5 * e[3]])[None].astype(np.float32)
+    C = np.stack([e[0], e[1]])[None].astype(np.float32)
+    s = O.Shape(W=1, N=2, d=d, K=2)
+    r = O.kmeans_fit(s, O.F32, H, None, O.INIT_GIVEN, 1, C.copy())
+    assert r["assign"][0].tolist() == [0, 1]
+    want = _unit(H[0]).astype(np.float32)
+    assert np.allclose(r["C"][0], want, rtol=0, atol=1e-7)
+    assert r["counts"][0].tolist() == [1, 1]

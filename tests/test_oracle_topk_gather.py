@@ -109,3 +109,34 @@ def test_gather_bf16_rows_are_byte_copies():
     t = np.arange(2, N, K)
     assert r["count"][0] == t.size
     assert np.array_equal(r["K_out"][0, : t.size], Kc[0, t])
+
+
+def test_gather_rebuilds_representable_rows_exactly():
+    """Rows built from NVFP4-representable residuals (centre 0, every block
+    holding a +-6, power-of-two row scale) times a power-of-two norm n are
+    rebuilt exactly: h_hat = (c + rhat) * n == h, bit for bit."""
+    rng = np.random.default_rng(8)
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    N, d, K = 24, 64, 2
+    nb = d // 16
+    nib = rng.integers(0, 16, size=(N, d)).astype(np.uint8)
+    nib[nib == 8] = 0
+    for j in range(N):
+        for b in range(nb):
+            nib[j, 16 * b + rng.integers(0, 16)] = 7 | (8 * rng.integers(0, 2))
+    sc = rng.integers(0x08, 0x7E, size=(N, nb)).astype(np.uint8)
+    sc[np.arange(N), rng.integers(0, nb, size=N)] = 0x7E
+    g = np.ldexp(1.0, rng.integers(-20, -6, size=N))
+    sval = np.array([[O.e4m3_decode(c) for c in row] for row in sc])
+    x = np.where(nib & 8, -1.0, 1.0) * mags[nib & 7] * np.repeat(sval, 16, axis=1) * g[:, None]
+    n = np.ldexp(1.0, rng.integers(-3, 9, size=N)).astype(np.float32)     # powers of two, not 1
+    H = (x * n[:, None]).astype(np.float32)[None]
+    s = O.Shape(W=1, N=N, d=d, K=K)
+    C = np.zeros((1, K, d), np.float32)
+    assign = np.zeros((1, N), np.int32)
+    rn = n[None].copy()
+    q = O.residual_nvfp4(s, O.F32, H, rn, C, assign)
+    idx = np.array([[0, 1]], np.int32)
+    r = O.refresh_gather(s, O.F32, assign, idx, 2, N, q["codes"], q["bscale"], q["rscale"], C, rn, True)
+    assert int(r["count"][0]) == N
+    assert np.array_equal(r["H_hat"][0].view(np.uint32), H[0].view(np.uint32))
