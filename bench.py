@@ -277,6 +277,8 @@ def main():
     ap.add_argument("--residual-store", default="device", choices=["device", "host"],
                     help="keep the NVFP4 residual store in HBM, or in pinned host memory as the "
                          "pages' CPU offload (copied out each step, selected rows fetched back)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the secondary timing of the same steps replayed from HIP graphs")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the latency-hiding figure (drift step beside a stand-in forward)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -388,6 +390,24 @@ def main():
         fpx = {"value": args.steps * cfg.W * cfg.N / (f1 - f0), "ms_per_step": 1e3 * (f1 - f0) / args.steps}
         print(f"[bench] fixed-point exit: {fpx['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # secondary figure: the same steps replayed from HIP graphs (one graph per
+    # input snapshot and step parity, captured in two untimed passes)
+    graphed = None
+    if not args.no_graph and args.residual_store == "device":
+        ins = [wl.inputs(i) for i in range(args.warmup, total)]
+        for _ in range(2):
+            for x in ins:
+                path.step_graphed(*x)
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for x in ins:
+            path.step_graphed(*x)
+        torch.cuda.synchronize()
+        g1 = time.perf_counter()
+        graphed = {"value": args.steps * cfg.W * cfg.N / (g1 - g0), "ms_per_step": 1e3 * (g1 - g0) / args.steps,
+                   "graphs": len(path._graphs)}
+        print(f"[bench] graph replay: {graphed['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+
     hiding = None
     if not args.no_overlap:
         print("[bench] latency hiding beside a stand-in forward", file=sys.stderr, flush=True)
@@ -415,6 +435,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "fixed_point_exit": fpx,
+        "graph_replay": graphed,
         "latency_hiding": hiding,
         "kernels": breakdown,
     }

@@ -844,8 +844,14 @@ void launch_assign_wide(const ps_shape* s, const void* H, const KmWs& ws, int32_
 {
     const int tiles = (s->N + kWideTok - 1) / kWideTok;
     const int nblocks = s->W * tiles;
-    (void)hipFuncSetAttribute((const void*)k_assign_wide<FIRST>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)kWideLds);
+    // the LDS limit is raised once per device (outside any stream capture
+    // that a caller may run later); a failure shows up as a launch error
+    static bool raised[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !raised[dev]) {
+        raised[dev] = hipFuncSetAttribute((const void*)k_assign_wide<FIRST>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds) == hipSuccess;
+    }
     PS_LAUNCH(FIRST ? "k_assign_wide<true>" : "k_assign_wide<false>", k_assign_wide<FIRST>, dim3(nblocks),
               dim3(512), kWideLds, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks,
               ws.dirty, ws.conv);

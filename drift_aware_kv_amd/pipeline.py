@@ -136,6 +136,7 @@ class DriftPath:
         self.suffix_flag = torch.zeros(s.W, dtype=torch.uint8, device=dev)
         self.commit_suffix = torch.zeros(s.W, s.N, dtype=torch.uint8, device=dev)
         self.t = 0
+        self._graphs = {}
 
     @property
     def logp_cur(self):
@@ -193,6 +194,35 @@ class DriftPath:
                                 self.hist_sum, self.hist_n, self.commit_block, self.delta, stream)
                 ps_commit_suffix(s, self.assign, self.idx, sp.k, self.block_start, conf, sp.tau_s,
                                  self.suffix_flag, self.commit_suffix, stream)
+        t = self.t
+        self.t += 1
+        return t
+
+    def step_graphed(self, H, Kr, V, Q, conf=None):
+        """The same step as step(), replayed from a HIP graph.
+
+        Steps after window formation launch the same kernels with the same
+        arguments whenever the input buffers and the parity of t (which of the
+        two log-probability buffers is current) repeat, so one graph per such
+        key is captured on first use and replayed after that: one submission
+        instead of one launch per kernel.  Formation runs eagerly.  Inputs must
+        stay at their addresses; the residual store must be on the device; the
+        kernel timer must be off.  Runs on the current stream."""
+        if self.t == 0:
+            return self.step(H, Kr, V, Q, conf)
+        if self.store is not None:
+            raise ValueError("step_graphed needs the residual store on the device")
+        key = (H.data_ptr(), Kr.data_ptr(), V.data_ptr(), Q.data_ptr(),
+               conf.data_ptr() if conf is not None else 0, self.t & 1)
+        g = self._graphs.get(key)
+        if g is None:
+            g = torch.cuda.CUDAGraph()
+            t = self.t
+            with torch.cuda.graph(g):
+                self.step(H, Kr, V, Q, conf)      # recorded, not run
+            self.t = t
+            self._graphs[key] = g
+        g.replay()
         t = self.t
         self.t += 1
         return t
