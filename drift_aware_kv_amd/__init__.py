@@ -70,7 +70,7 @@ def lib():
         L.ps_workspace_size.argtypes = [SP, I, ctypes.POINTER(ctypes.c_size_t)]
         L.ps_kmeans_fit.argtypes = [SP, I, P, P, I, ctypes.c_int32, ctypes.c_uint32, P, P, P, P, P,
                                     P, P, ctypes.c_size_t, P]
-        L.ps_residual_nvfp4.argtypes = [SP, I, P, P, P, P, P, P, P, P]
+        L.ps_residual_nvfp4.argtypes = [SP, I, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.ps_proxy_attn.argtypes = [SP, I, P, P, ctypes.c_float, P, P, I, P, P, P, P]
         L.ps_drift_kl.argtypes = [SP, P, P, I, P, P, P, P]
         L.ps_topk_clusters.argtypes = [SP, P, ctypes.c_int32, P, P, P]
@@ -166,7 +166,8 @@ def ps_workspace_size(s: Shape, dtype) -> int:
 
 
 def workspace(s: Shape, dtype, device=None):
-    """Allocate a workspace tensor for ps_kmeans_fit (caller-owned)."""
+    """Allocate a workspace tensor for ps_kmeans_fit and ps_residual_nvfp4
+    (caller-owned)."""
     return torch.empty(max(ps_workspace_size(s, dtype), 16), dtype=torch.uint8, device=device or "cuda")
 
 
@@ -186,13 +187,17 @@ def ps_kmeans_fit(s: Shape, dtype, H, Kr, init, iters, C, assign, counts, row_no
         _ptr(ws, wsb, 1, "ws"), ws.numel(), _stream(stream)), "ps_kmeans_fit")
 
 
-def ps_residual_nvfp4(s: Shape, dtype, H, row_norm, C, assign, codes, bscale, rscale, stream=None):
+def ps_residual_nvfp4(s: Shape, dtype, H, row_norm, C, assign, codes, bscale, rscale, ws=None,
+                      stream=None):
+    """ws: optional uint8 scratch tensor of at least 8*W*N + 16 bytes (workspace()
+    is always enough): with it, rows are coded grouped by cluster."""
     e = _es(dtype)
     _check(lib().ps_residual_nvfp4(
         _cs(s), dtype, _ptr(H, s.W * s.N * s.d, e, "H"), _ptr(row_norm, s.W * s.N, 4, "row_norm"),
         _ptr(C, s.W * s.K * s.d, 4, "C"), _ptr(assign, s.W * s.N, 4, "assign"),
         _ptr(codes, s.W * s.N * s.d // 2, 1, "codes"), _ptr(bscale, s.W * s.N * s.d // 16, 1, "bscale"),
-        _ptr(rscale, s.W * s.N, 4, "rscale"), _stream(stream)), "ps_residual_nvfp4")
+        _ptr(rscale, s.W * s.N, 4, "rscale"), _ptr(ws, 8 * s.W * s.N + 16, 1, "ws", True),
+        ws.numel() if ws is not None else 0, _stream(stream)), "ps_residual_nvfp4")
 
 
 def ps_proxy_attn(s: Shape, dtype, Q, Ck, softmax_scale, logp_cur, logp_prev, score_kind, D_hi, D_i,

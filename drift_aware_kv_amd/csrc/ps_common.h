@@ -180,6 +180,13 @@ inline ps_status check_window(const ps_shape* s)
     return PS_OK;
 }
 
+// scratch of the grouped NVFP4 coder: the grouped row order, the list of rows
+// for the exact path and its count (int32 each)
+inline size_t residual_ws_bytes(const ps_shape* s)
+{
+    return 8 * (size_t)s->W * (size_t)s->N + 16;
+}
+
 inline ps_status check_clusters(const ps_shape* s)
 {
     ps_status st = check_window(s);

@@ -879,7 +879,7 @@ extern "C" ps_status ps_workspace_size(const ps_shape* s, ps_dtype dtype, size_t
     if (!ps_host::dtype_ok(dtype)) return PS_ERR_DTYPE;
     ps_status st = ps_host::check_clusters(s);
     if (st != PS_OK) return st;
-    *bytes = km_layout(s, dtype, nullptr).bytes;
+    *bytes = std::max(km_layout(s, dtype, nullptr).bytes, ps_host::residual_ws_bytes(s));
     return PS_OK;
 }
 

@@ -4,13 +4,13 @@
 // the selected clusters (2.A, sparse updates; 2.C, only the selected clusters
 // are fetched), for gfx950.
 //
-// The coder gives each row four waves (one for short rows), with coalesced
-// 16-byte loads all issued before use and a single cross-wave exchange per
-// row.  Its fast path replaces divisions by reciprocal products and uses the
-// hardware E4M3/E2M1 conversions, each proven or exhaustively checked to give
-// the results of the stated convention (every fp32 step one correctly rounded
-// operation) bit for bit; rows outside the proof's conditions take the exact
-// path.  The gather is bandwidth bound: one workgroup per selected row.
+// The coder gives each row one wave (four for rows longer than 4096), each
+// thread owning whole 16-element blocks, with 16-byte loads all issued before
+// use and at most one cross-wave exchange per row.  Its fast path replaces
+// divisions by reciprocal products and uses the hardware E4M3/E2M1
+// conversions, each proven or exhaustively checked to give the results of the
+// stated convention (every fp32 step one correctly rounded operation) bit for
+// bit; rows outside the proof's conditions take the exact path.  The gather is bandwidth bound: one workgroup per selected row.
 #include "ps_common.h"
 
 using namespace ps;
@@ -24,15 +24,17 @@ namespace {
 // (relative) from every fp32 rounding midpoint (with m a midpoint of 25
 // significant bits, a - m*b is a non-zero multiple of 2^(e_m + e_b - 47),
 // since a has at most 24 significant bits), while the fp64 product is within
-// 2^-50 of a / b.  y is RN64(1/b) for the row-wide divisors (the norm n, the
-// row scale g, the constant 6) and, per block, the fp32 reciprocal estimate of
-// eff refined by three Newton steps in fp64 (relative error below 2^-52 from
-// any start better than 2^-12).  Below the normal range the midpoints are
-// coarser than that argument covers: a row with a non-zero |h| or |r| whose
-// exponent is 125 or more below its divisor's, or subnormal, is redone with
-// divisions (`residual_row_exact`); so is a row with a non-finite residual or
-// with a largest |r| below 2^-100, under which the block-scale quotients lose
-// their margin.  With max |r| >= 2^-100 a block whose Ab/6 is below 2^-125
+// 2^-50 of a / b.  y is RN64(1/b) for the norm n and the constants 6 and
+// 2688; for the row scale g and each block's eff, both normal fp32 numbers in
+// [2^-126, 2^126) on this path, it is the fp32 reciprocal estimate refined by
+// two Newton steps in fp64 (`recip_nr`: the relative error e of the start
+// becomes e^4 plus fp64 rounding; checked exhaustively over that range, below
+// 2^-53).  Below the normal
+// range the midpoints are coarser than that argument covers: a row with a
+// non-zero |h| or |r| whose exponent is 125 or more below its divisor's, or
+// subnormal, is redone with divisions (`residual_row_exact`); so is a row with
+// a non-finite residual or with a largest |r| below 2^-100, under which the
+// block-scale quotients lose their margin.  With max |r| >= 2^-100 a block whose Ab/6 is below 2^-125
 // has (Ab/6)/g below 2^-13, which encodes to the E4M3 zero either way.
 //
 // E2M1 rounding on the fast path uses gfx950's fp32 -> fp4 conversion with
@@ -45,6 +47,16 @@ __device__ __forceinline__ uint32_t plus_zero(uint32_t w)
     const uint32_t m = w & 0x77777777u;                              // magnitudes
     const uint32_t nz = (m | (m >> 1) | (m >> 2)) & 0x11111111u;     // magnitude != 0
     return m | (w & (nz << 3));
+}
+
+// 1/b within 2^-52 (relative) for a normal fp32 b in [2^-126, 2^126)
+__device__ __forceinline__ double recip_nr(float b)
+{
+    const double b64 = (double)b;
+    double y = (double)__builtin_amdgcn_rcpf(b);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) y = fma(y, fma(-b64, y, 1.0), y);
+    return y;
 }
 
 __device__ __forceinline__ uint32_t wave_max_u(uint32_t v)
@@ -126,12 +138,6 @@ __device__ __forceinline__ void store_chunks(const uint32_t (&words)[CPL], const
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// the partner lane's value within a lane pair (DPP quad permutation 1,0,3,2)
-__device__ __forceinline__ uint32_t pair_swap(uint32_t v)
-{
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
-}
-
 __device__ __forceinline__ u16x2 wave_min_u16x2(u16x2 v)
 {
 #pragma unroll
@@ -140,18 +146,51 @@ __device__ __forceinline__ u16x2 wave_min_u16x2(u16x2 v)
     return v;
 }
 
+// Block layout of the fast path: thread i of the row owns the 16-element
+// blocks i, i + TPR, ..., so every block scale is computed once, by the thread
+// that codes the block.  Blocks past the row read the last block again (always
+// in bounds) and are masked.
+template <typename T, int TPR, int BPL>
+__device__ __forceinline__ void load_hblocks(const T* __restrict__ h, int tid, int nb,
+                                             uint4 (&hq)[BPL][sizeof(T) == 2 ? 2 : 4])
+{
+    constexpr int HW = sizeof(T) == 2 ? 2 : 4;
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+        const uint4* hp = reinterpret_cast<const uint4*>(h + 16 * min(tid + TPR * b, nb - 1));
+#pragma unroll
+        for (int q = 0; q < HW; ++q) hq[b][q] = hp[q];
+    }
+}
+
+template <int TPR, int BPL>
+__device__ __forceinline__ void load_cblocks(const float* __restrict__ c, int tid, int nb, float (&cv)[BPL][16])
+{
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+        const float4* cp = reinterpret_cast<const float4*>(c + 16 * min(tid + TPR * b, nb - 1));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = cp[q];
+            cv[b][4 * q] = v.x; cv[b][4 * q + 1] = v.y; cv[b][4 * q + 2] = v.z; cv[b][4 * q + 3] = v.w;
+        }
+    }
+}
+
 // Fast NVFP4 coding of one row: reciprocal products instead of divisions, the
 // hardware E4M3 and E2M1 conversions (checked exhaustively against the
 // software rounding: E4M3 over every fp32 in [0, 464), which holds every block
 // scale quotient, E2M1 over every finite fp32), and the checks folded into
 // integer max/min over magnitude bit patterns (which also catch NaN and
 // infinity).  The row's largest |r| and smallest non-zero |h| are combined in
-// one exchange; from them every thread takes the same decision whether the
+// one reduction; from them every thread takes the same decision whether the
 // row needs the exact path, before any block is coded.  Quotients r/eff below
 // 2^-125 need no check: they encode to the E2M1 zero however they round.
 // Returns false without writing anything when the exact path is needed.
-template <typename T, int NW, int CPL, bool FULL>
-__device__ __forceinline__ bool residual_row_fast(const T* __restrict__ h, const float* __restrict__ c, float n,
+// The row's h and centre blocks arrive loaded (load_hblocks, load_cblocks).
+template <typename T, int NW, int BPL, bool FULL>
+__device__ __forceinline__ bool residual_row_fast(const uint4 (&hq)[BPL][sizeof(T) == 2 ? 2 : 4],
+                                                  const float (&cv)[BPL][16], float n,
                                                   uint8_t* __restrict__ cr, uint8_t* __restrict__ br,
                                                   float* __restrict__ rs, int d, uint32_t (*red)[3])
 {
@@ -159,46 +198,60 @@ __device__ __forceinline__ bool residual_row_fast(const T* __restrict__ h, const
     constexpr bool packed = sizeof(T) == 2;
     if (!(n > 0.0f) || n == INFINITY) return false;   // row-uniform: zero, negative or non-finite norm
     const int tid = (int)(threadIdx.x % TPR), wave = tid >> 6;
-    const int nch = d >> 3;
+    const int nb = d >> 4;
     const double inv_n = 1.0 / (double)n;
-    uint4 hq[CPL][packed ? 1 : 2];
-    float r[CPL][8];
-    load_chunks<T, TPR, CPL>(h, c, tid, nch, hq, r);
-    uint32_t cmax[CPL];
-    u16x2 hmin2 = {0xffff, 0xffff};              // bf16: smallest non-zero |h|, minus one, per half
-    uint32_t hmin = ~0u;                         // fp32: the same over fp32 bit patterns
+    float r[BPL][16];
+    uint32_t bmax[BPL];
+    // bf16: per half, 2|h| - 2 (mod 2^16): the sign drops out, zero maps to
+    // 0xfffe above every non-zero magnitude; fp32: |h| - 1 over the bit patterns
+    u16x2 hkey = {0xffff, 0xffff};
+    uint32_t hmin = ~0u;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const bool valid = FULL || tid + TPR * i < nch;
+    for (int b = 0; b < BPL; ++b) {
+        const bool valid = FULL || tid + TPR * b < nb;
+        float hv[16];
         if (packed) {
-            const uint32_t w4[4] = {hq[i][0].x, hq[i][0].y, hq[i][0].z, hq[i][0].w};
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                hmin2 = __builtin_elementwise_min(
-                    hmin2, __builtin_bit_cast(u16x2, w4[t] & 0x7fff7fffu) - (u16x2){1, 1});
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t w4[4] = {hq[b][q].x, hq[b][q].y, hq[b][q].z, hq[b][q].w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const u16x2 x = __builtin_bit_cast(u16x2, w4[t]);
+                    hkey = __builtin_elementwise_min(hkey, x * (u16x2){2, 2} + (u16x2){0xfffe, 0xfffe});
+                    hv[8 * q + 2 * t] = __uint_as_float(w4[t] << 16);
+                    hv[8 * q + 2 * t + 1] = __uint_as_float(w4[t] & 0xffff0000u);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w4[4] = {hq[b][q].x, hq[b][q].y, hq[b][q].z, hq[b][q].w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    hmin = min(hmin, (w4[t] & 0x7fffffffu) - 1u);
+                    hv[4 * q + t] = __uint_as_float(w4[t]);
+                }
+            }
         }
-        float hv[8];
-        unpack8<T>(hq[i], hv);
         float m = 0.0f;                          // NaN-propagating max of |r|
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (!packed) hmin = min(hmin, (__float_as_uint(hv[t]) & 0x7fffffffu) - 1u);
-            float rv = (float)((double)hv[t] * inv_n) - r[i][t];
+        for (int t = 0; t < 16; ++t) {
+            float rv = (float)((double)hv[t] * inv_n) - cv[b][t];
             if (!FULL) rv = valid ? rv : 0.0f;
-            r[i][t] = rv;
+            r[b][t] = rv;
             m = __builtin_elementwise_maximum(m, fabsf(rv));
         }
-        cmax[i] = __float_as_uint(m);            // non-negative: bit order is value order, NaN on top
+        bmax[b] = __float_as_uint(m);            // non-negative: bit order is value order, NaN on top
     }
     uint32_t Am = 0;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) Am = max(Am, cmax[i]);
+    for (int b = 0; b < BPL; ++b) Am = max(Am, bmax[b]);
     Am = wave_max_u(Am);
     uint32_t hm;                                 // smallest non-zero |h| minus one, fp32-bit order
     if (packed) {
-        hmin2 = wave_min_u16x2(hmin2);
-        const uint32_t m16 = min((uint32_t)hmin2.x, (uint32_t)hmin2.y);
-        hm = m16 == 0xffffu ? ~0u : ((m16 + 1u) << 16) - 1u;
+        hkey = wave_min_u16x2(hkey);
+        const uint32_t k16 = min((uint32_t)hkey.x, (uint32_t)hkey.y);
+        hm = k16 >= 0xfffeu ? ~0u : ((((k16 + 2u) >> 1)) << 16) - 1u;
     } else {
         hm = wave_min_u(hmin);
     }
@@ -219,37 +272,39 @@ __device__ __forceinline__ bool residual_row_fast(const T* __restrict__ h, const
     const bool zero_row = Am == 0u;
     if (!zero_row && Am < 0x0d800000u) return false;     // max |r| below 2^-100
     if (tiny_against(hm + 1u, __float_as_uint(n))) return false;
-    const float g = __uint_as_float(Am) / 2688.0f;
-    const double inv_g = zero_row ? 0.0 : 1.0 / (double)g;
-    uint32_t words[CPL], scales[CPL];
+    const float g = (float)((double)__uint_as_float(Am) * (1.0 / 2688.0));   // >= 2^-112 unless zero
+    const double inv_g = zero_row ? 0.0 : recip_nr(g);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const uint32_t bm = max(cmax[i], pair_swap(cmax[i]));   // the block's max
-        uint32_t word = 0, sb = 0;
+    for (int b = 0; b < BPL; ++b) {
+        uint32_t w0 = 0, w1 = 0, sb = 0;
         if (!zero_row) {
-            const float q1 = (float)((double)__uint_as_float(bm) * (1.0 / 6.0));
+            const float q1 = (float)((double)__uint_as_float(bmax[b]) * (1.0 / 6.0));
             const float q2 = (float)((double)q1 * inv_g);
             sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q2, 0, false) & 0xffu;
             const float eff = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
             if (eff != 0.0f) {
-                const double e64 = (double)eff;
-                double y = (double)__builtin_amdgcn_rcpf(eff);
+                const double y = recip_nr(eff);
+                float v[16];
 #pragma unroll
-                for (int it = 0; it < 3; ++it) y = fma(y, fma(-e64, y, 1.0), y);
-                float v[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) v[t] = (float)((double)r[i][t] * y);
-                word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], 1.0f, 0);
-                word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], 1.0f, 1);
-                word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], 1.0f, 2);
-                word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], 1.0f, 3);
-                word = plus_zero(word);
+                for (int t = 0; t < 16; ++t) v[t] = (float)((double)r[b][t] * y);
+                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[0], v[1], 1.0f, 0);
+                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[2], v[3], 1.0f, 1);
+                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[4], v[5], 1.0f, 2);
+                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[6], v[7], 1.0f, 3);
+                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[8], v[9], 1.0f, 0);
+                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[10], v[11], 1.0f, 1);
+                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[12], v[13], 1.0f, 2);
+                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[14], v[15], 1.0f, 3);
+                w0 = plus_zero(w0);
+                w1 = plus_zero(w1);
             }
         }
-        words[i] = word;
-        scales[i] = sb;
+        const int blk = tid + TPR * b;
+        if (FULL || blk < nb) {
+            *reinterpret_cast<uint2*>(cr + 8 * blk) = make_uint2(w0, w1);
+            br[blk] = (uint8_t)sb;
+        }
     }
-    store_chunks<TPR, CPL>(words, scales, tid, nch, cr, br);
     if (tid == 0) *rs = zero_row ? 0.0f : g;
     return true;
 }
@@ -315,16 +370,18 @@ __device__ __forceinline__ void residual_row_exact(const T* __restrict__ h, cons
     if (tid == 0) *rs = zero_row ? 0.0f : g;
 }
 
-// NW waves per row, 4 / NW rows per 256-thread workgroup; one exchange (and
-// with one wave per row, none) per row.  Consecutive rows (one window's,
-// sharing its centres) stay on one XCD.
-template <typename T, int NW, int CPL, bool FULL>
+// NW waves per row: four one-wave rows per workgroup, or one row of NW waves
+// per workgroup (64 * NW threads); one exchange (and with one wave per row,
+// none) per row.  Consecutive rows (one window's,
+// sharing its centres) stay on one XCD.  BPL blocks of 16 per thread on the
+// fast path; the exact path holds the same elements as 2 * BPL chunks of 8.
+template <typename T, int NW, int BPL, bool FULL>
 __global__ __launch_bounds__(256) void k_residual(const T* __restrict__ H, const float* __restrict__ row_norm,
                                                    const float* __restrict__ C, const int32_t* __restrict__ assign,
                                                    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscale,
                                                    float* __restrict__ rscale, int64_t rows, int N, int d, int K)
 {
-    constexpr int RPB = 4 / NW;                  // rows per workgroup
+    constexpr int RPB = NW == 1 ? 4 : 1;         // rows per workgroup
     __shared__ uint32_t red[4][3];
     const int64_t row = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * RPB + (RPB > 1 ? (int)(threadIdx.x / (64 * NW)) : 0);
     // with one row per workgroup every thread has the same row; with several,
@@ -338,9 +395,153 @@ __global__ __launch_bounds__(256) void k_residual(const T* __restrict__ H, const
     uint8_t* cr = codes + (size_t)row * (d >> 1);
     uint8_t* br = bscale + (size_t)row * (d >> 4);
     const float n = row_norm[row];
-    if (!residual_row_fast<T, NW, CPL, FULL>(h, c, n, cr, br, rscale + row, d, red)) {
+    constexpr int TPR = 64 * NW;
+    uint4 hq[BPL][sizeof(T) == 2 ? 2 : 4];
+    float cv[BPL][16];
+    load_hblocks<T, TPR, BPL>(h, (int)(threadIdx.x % TPR), d >> 4, hq);
+    load_cblocks<TPR, BPL>(c, (int)(threadIdx.x % TPR), d >> 4, cv);
+    if (!residual_row_fast<T, NW, BPL, FULL>(hq, cv, n, cr, br, rscale + row, d, red)) {
         if (NW > 1) __syncthreads();  // red[] is reused
-        residual_row_exact<T, NW, CPL>(h, c, n, cr, br, rscale + row, d, red);
+        residual_row_exact<T, NW, 2 * BPL>(h, c, n, cr, br, rscale + row, d, red);
+    }
+}
+
+// Rows of each window grouped by cluster: perm[w][.] lists the window's rows
+// with each cluster's members contiguous, clusters in ascending order (the
+// order within a cluster is unspecified: no result depends on it).
+// Assignments outside [0, K) count as cluster 0, as the coder reads them.
+// One workgroup per window; the first also clears the count of listed rows.
+__global__ __launch_bounds__(256) void k_group_rows(const int32_t* __restrict__ assign,
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ listed,
+                                                     int N, int K)
+{
+    __shared__ int base[kMaxK];
+    __shared__ int wsum[4];
+    const int w = blockIdx.x, t = threadIdx.x;
+    if (w == 0 && t == 0) *listed = 0;
+    for (int c = t; c < K; c += 256) base[c] = 0;
+    __syncthreads();
+    const int32_t* a = assign + (size_t)w * N;
+    for (int j = t; j < N; j += 256) {
+        const int c = a[j];
+        atomicAdd(&base[(unsigned)c < (unsigned)K ? c : 0], 1);
+    }
+    __syncthreads();
+    // exclusive prefix sum of the counts; thread t owns clusters 4t .. 4t + 3
+    int v[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = 4 * t + i;
+        v[i] = c < K ? base[c] : 0;
+        sum += v[i];
+    }
+    int x = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if ((t & 63) >= o) x += y;
+    }
+    if ((t & 63) == 63) wsum[t >> 6] = x;
+    __syncthreads();
+    int off = x - sum;
+    for (int q = 0; q < (t >> 6); ++q) off += wsum[q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = 4 * t + i;
+        if (c < K) base[c] = off;
+        off += v[i];
+    }
+    __syncthreads();
+    for (int j = t; j < N; j += 256) {
+        const int c = a[j];
+        const int p = atomicAdd(&base[(unsigned)c < (unsigned)K ? c : 0], 1);
+        perm[(size_t)w * N + p] = j;
+    }
+}
+
+// The coder over grouped rows: each wave codes kGroupRows consecutive entries
+// of its window's perm, one row at a time, and keeps the current cluster's
+// centre blocks in registers, reloading them only when the cluster changes, so
+// each centre is read about once per wave instead of once per row.  The next
+// row's h is requested before the current row is coded.  Rows the fast path
+// declines are appended to a list for k_residual_listed.  One wave per row
+// (rows of up to 4096 elements); the workgroups of a window stay on one XCD.
+constexpr int kGroupRows = 16;
+
+template <typename T, int BPL, bool FULL>
+__global__ __launch_bounds__(256) void k_residual_grouped(const T* __restrict__ H, const float* __restrict__ row_norm,
+                                                           const float* __restrict__ C,
+                                                           const int32_t* __restrict__ assign,
+                                                           const int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ list, int32_t* __restrict__ listed,
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ bscale,
+                                                           float* __restrict__ rscale, int N, int d, int K, int tiles,
+                                                           int nblocks)
+{
+    constexpr int HW = sizeof(T) == 2 ? 2 : 4;
+    const int tile = xcd_remap(blockIdx.x, nblocks);
+    const int w = tile / tiles;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int p0 = (tile - w * tiles) * (4 * kGroupRows) + wave * kGroupRows;
+    const int p1 = min(p0 + kGroupRows, N);
+    if (p0 >= p1) return;
+    const int lane = (int)(threadIdx.x & 63), nb = d >> 4;
+    const size_t wrow = (size_t)w * N;
+    const int32_t* pw = perm + wrow;
+    // perm holds a permutation of 0 .. N-1; the clamp only keeps reads in bounds
+    int j = min(max(pw[p0], 0), N - 1);
+    uint4 hq[BPL][HW];
+    load_hblocks<T, 64, BPL>(H + (wrow + j) * d, lane, nb, hq);
+    float cv[BPL][16];
+    int cur = -1;
+    for (int p = p0; p < p1; ++p) {
+        const size_t row = wrow + j;
+        int a = assign[row];
+        if (a < 0 || a >= K) a = 0;
+        const float n = row_norm[row];
+        const bool more = p + 1 < p1;
+        const int jn = more ? min(max(pw[p + 1], 0), N - 1) : j;
+        uint4 hn[BPL][HW];
+        if (more) load_hblocks<T, 64, BPL>(H + (wrow + jn) * d, lane, nb, hn);
+        if (a != cur) {
+            load_cblocks<64, BPL>(C + ((size_t)w * K + a) * d, lane, nb, cv);
+            cur = a;
+        }
+        if (!residual_row_fast<T, 1, BPL, FULL>(hq, cv, n, codes + row * (size_t)(d >> 1),
+                                                bscale + row * (size_t)(d >> 4), rscale + row, d, nullptr)) {
+            if (lane == 0) list[atomicAdd(listed, 1)] = (int32_t)row;
+        }
+        if (more) {
+#pragma unroll
+            for (int b = 0; b < BPL; ++b)
+#pragma unroll
+                for (int q = 0; q < HW; ++q) hq[b][q] = hn[b][q];
+        }
+        j = jn;
+    }
+}
+
+// The exact coder over the listed rows, one wave per row; every wave reads the
+// count and strides over the list.
+template <typename T, int CPL>
+__global__ __launch_bounds__(256) void k_residual_listed(const T* __restrict__ H, const float* __restrict__ row_norm,
+                                                          const float* __restrict__ C,
+                                                          const int32_t* __restrict__ assign,
+                                                          const int32_t* __restrict__ list,
+                                                          const int32_t* __restrict__ listed,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ bscale,
+                                                          float* __restrict__ rscale, int N, int d, int K)
+{
+    const int total = *listed;
+    const int stride = (int)gridDim.x * 4;
+    for (int i = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6); i < total; i += stride) {
+        const size_t row = (size_t)list[i];
+        const int w = (int)(row / (size_t)N);
+        int a = assign[row];
+        if (a < 0 || a >= K) a = 0;
+        residual_row_exact<T, 1, CPL>(H + row * d, C + ((size_t)w * K + a) * d, row_norm[row],
+                                      codes + row * (size_t)(d >> 1), bscale + row * (size_t)(d >> 4),
+                                      rscale + row, d, nullptr);
     }
 }
 
@@ -430,39 +631,71 @@ __global__ __launch_bounds__(256) void k_gather_rows(const int32_t* __restrict__
     }
 }
 
-template <typename T, int NW, int CPL>
+template <typename T, int NW, int BPL>
 void launch_residual(const ps_shape* s, const void* H, const float* rn, const float* C, const int32_t* a,
                      uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t st)
 {
     const int64_t rows = (int64_t)s->W * s->N;
-    const int rpb = 4 / NW;
-    const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-    if (s->d / 8 == 64 * NW * CPL)
-        PS_LAUNCH("k_residual<T, NW, CPL, FULL>", (k_residual<T, NW, CPL, true>), grid, dim3(256), 0, st,
+    const int rpb = NW == 1 ? 4 : 1;
+    const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(64 * NW * rpb);
+    if (s->d / 16 == 64 * NW * BPL)
+        PS_LAUNCH("k_residual<T, NW, BPL, FULL>", (k_residual<T, NW, BPL, true>), grid, block, 0, st,
                   (const T*)H, rn, C, a, codes, bscale, rscale, rows, s->N, s->d, s->K);
     else
-        PS_LAUNCH("k_residual<T, NW, CPL, FULL>", (k_residual<T, NW, CPL, false>), grid, dim3(256), 0, st,
+        PS_LAUNCH("k_residual<T, NW, BPL, FULL>", (k_residual<T, NW, BPL, false>), grid, block, 0, st,
                   (const T*)H, rn, C, a, codes, bscale, rscale, rows, s->N, s->d, s->K);
 }
 
-// rows of up to 512 elements: one wave per row; longer rows (up to 8192
-// elements): four waves, 1 to 4 chunks of 8 elements per thread
+template <typename T, int BPL>
+void launch_residual_grouped(const ps_shape* s, const void* H, const float* rn, const float* C, const int32_t* a,
+                             int32_t* ws, uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t st)
+{
+    const size_t rows = (size_t)s->W * s->N;
+    int32_t* perm = ws;
+    int32_t* list = ws + rows;
+    int32_t* listed = ws + 2 * rows;
+    PS_LAUNCH("k_group_rows", k_group_rows, dim3(s->W), dim3(256), 0, st, a, perm, listed, s->N, s->K);
+    const int tiles = (s->N + 4 * kGroupRows - 1) / (4 * kGroupRows);
+    const int nblocks = s->W * tiles;
+    if (s->d / 16 == 64 * BPL)
+        PS_LAUNCH("k_residual_grouped<T, BPL, FULL>", (k_residual_grouped<T, BPL, true>), dim3(nblocks), dim3(256),
+                  0, st, (const T*)H, rn, C, a, perm, list, listed, codes, bscale, rscale, s->N, s->d, s->K, tiles,
+                  nblocks);
+    else
+        PS_LAUNCH("k_residual_grouped<T, BPL, FULL>", (k_residual_grouped<T, BPL, false>), dim3(nblocks), dim3(256),
+                  0, st, (const T*)H, rn, C, a, perm, list, listed, codes, bscale, rscale, s->N, s->d, s->K, tiles,
+                  nblocks);
+    const unsigned lb = (unsigned)std::min<size_t>((rows + 3) / 4, 1024);
+    PS_LAUNCH("k_residual_listed<T, CPL>", (k_residual_listed<T, 2 * BPL>), dim3(lb), dim3(256), 0, st,
+              (const T*)H, rn, C, a, list, listed, codes, bscale, rscale, s->N, s->d, s->K);
+}
+
+// rows of up to 4096 elements: one wave per row, 1, 2 or 4 blocks of 16 per
+// thread, over rows grouped by cluster when scratch is given; longer rows (up
+// to 8192): four waves, 2 blocks per thread, in row order
 template <typename T>
 void dispatch_residual(const ps_shape* s, const void* H, const float* rn, const float* C, const int32_t* a,
-                       uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t st)
+                       int32_t* perm, uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t st)
 {
-    const int nch = s->d / 8;
-    if (nch <= 64)        launch_residual<T, 1, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else if (nch <= 256)  launch_residual<T, 4, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else if (nch <= 512)  launch_residual<T, 4, 2>(s, H, rn, C, a, codes, bscale, rscale, st);
-    else                  launch_residual<T, 4, 4>(s, H, rn, C, a, codes, bscale, rscale, st);
+    const int nb = s->d / 16;
+    if (perm && nb <= 256 && (int64_t)s->W * s->N < ((int64_t)1 << 31)) {
+        if (nb <= 64)       launch_residual_grouped<T, 1>(s, H, rn, C, a, perm, codes, bscale, rscale, st);
+        else if (nb <= 128) launch_residual_grouped<T, 2>(s, H, rn, C, a, perm, codes, bscale, rscale, st);
+        else                launch_residual_grouped<T, 4>(s, H, rn, C, a, perm, codes, bscale, rscale, st);
+        return;
+    }
+    if (nb <= 64)        launch_residual<T, 1, 1>(s, H, rn, C, a, codes, bscale, rscale, st);
+    else if (nb <= 128)  launch_residual<T, 1, 2>(s, H, rn, C, a, codes, bscale, rscale, st);
+    else if (nb <= 256)  launch_residual<T, 1, 4>(s, H, rn, C, a, codes, bscale, rscale, st);
+    else                 launch_residual<T, 4, 2>(s, H, rn, C, a, codes, bscale, rscale, st);
 }
 
 }  // namespace
 
 extern "C" ps_status ps_residual_nvfp4(const ps_shape* s, ps_dtype dtype, const void* H,
                                        const float* row_norm, const float* C, const int32_t* assign,
-                                       uint8_t* codes, uint8_t* bscale, float* rscale, void* stream)
+                                       uint8_t* codes, uint8_t* bscale, float* rscale, void* ws,
+                                       size_t ws_bytes, void* stream)
 {
     using namespace ps_host;
     if (!s || !H || !row_norm || !C || !assign || !codes || !bscale || !rscale) return PS_ERR_NULL;
@@ -471,13 +704,15 @@ extern "C" ps_status ps_residual_nvfp4(const ps_shape* s, ps_dtype dtype, const 
     if (st != PS_OK) return st;
     if (s->d > 8192) return PS_ERR_SHAPE;
     if (!aligned16(H) || !aligned16(row_norm) || !aligned16(C) || !aligned16(assign) || !aligned16(codes) ||
-        !aligned16(bscale) || !aligned16(rscale))
+        !aligned16(bscale) || !aligned16(rscale) || (ws && !aligned16(ws)))
         return PS_ERR_ALIGN;
+    if (ws && ws_bytes < residual_ws_bytes(s)) return PS_ERR_WORKSPACE;
     if (s->W == 0) return PS_OK;
     hipStream_t stm = (hipStream_t)stream;
+    int32_t* perm = (int32_t*)ws;
     (void)hipGetLastError();
-    if (dtype == PS_BF16) dispatch_residual<uint16_t>(s, H, row_norm, C, assign, codes, bscale, rscale, stm);
-    else                  dispatch_residual<float>(s, H, row_norm, C, assign, codes, bscale, rscale, stm);
+    if (dtype == PS_BF16) dispatch_residual<uint16_t>(s, H, row_norm, C, assign, perm, codes, bscale, rscale, stm);
+    else                  dispatch_residual<float>(s, H, row_norm, C, assign, perm, codes, bscale, rscale, stm);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
 }
 

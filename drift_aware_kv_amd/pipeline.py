@@ -162,7 +162,7 @@ class DriftPath:
         ps_kmeans_fit(s, dt, H, Kr, init, sp.iters, self.C, self.assign, self.counts, self.row_norm,
                       self.Ck, self.objective, self.ws, stream, flags=sp.kmeans_flags)
         ps_residual_nvfp4(s, dt, H, self.row_norm, self.C, self.assign, self.codes, self.bscale,
-                          self.rscale, stream)
+                          self.rscale, self.ws, stream)
         main = stream if stream is not None else torch.cuda.current_stream()
         if self.store is not None and not first:     # formation gathers nothing
             self.coded.record(main)

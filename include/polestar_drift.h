@@ -95,7 +95,8 @@ typedef struct {
 /* Human-readable name of a status code (static storage). */
 const char* ps_status_string(ps_status status);
 
-/* Bytes of scratch that ps_kmeans_fit needs for this shape and dtype. */
+/* Bytes of scratch that ps_kmeans_fit (and ps_residual_nvfp4) need for this
+ * shape and dtype. */
 ps_status ps_workspace_size(const ps_shape* shape, ps_dtype dtype, size_t* bytes);
 
 /*
@@ -146,10 +147,20 @@ ps_status ps_kmeans_fit(const ps_shape* shape, ps_dtype dtype, const void* H, co
  *                                 nibble = sign<<3 | E2M1 magnitude index
  *   bscale [W][N][d/16] u8   out  E4M3 (bias 7, 0x7e = 448)
  *   rscale [W][N]       f32  out  g_j
+ *   ws, ws_bytes                     scratch, or NULL: with at least
+ *                                    8*W*N + 16 bytes (ps_workspace_size is
+ *                                    always enough; the contents are
+ *                                    overwritten), rows of up to 4096
+ *                                    elements are coded grouped by cluster,
+ *                                    each centre read about once per 16
+ *                                    member rows; results are identical
+ *                                    either way.  A smaller non-NULL ws:
+ *                                    PS_ERR_WORKSPACE.
  */
 ps_status ps_residual_nvfp4(const ps_shape* shape, ps_dtype dtype, const void* H,
                             const float* row_norm, const float* C, const int32_t* assign,
-                            uint8_t* codes, uint8_t* bscale, float* rscale, void* stream);
+                            uint8_t* codes, uint8_t* bscale, float* rscale, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /*
  * ps_proxy_attn -- attention of the decode block's queries against the

@@ -105,13 +105,16 @@ def test_kmeans_fit_argument_checks(L):
 
 def test_residual_argument_checks(L):
     s = _shape()
-    f = lambda s=s, dt=1, H=FAKE: L.ps_residual_nvfp4(ctypes.byref(s), dt, H, FAKE, FAKE, FAKE, FAKE,
-                                                      FAKE, FAKE, None)
+    f = lambda s=s, dt=1, H=FAKE, ws=None, wsb=0: L.ps_residual_nvfp4(
+        ctypes.byref(s), dt, H, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
     assert f(H=None) == NULL
     assert f(dt=5) == DTYPE
     assert f(s=_shape(d=8)) == SHAPE
     assert f(H=MISALIGNED) == ALIGN
+    assert f(ws=MISALIGNED, wsb=1 << 20) == ALIGN
+    assert f(ws=FAKE, wsb=8 * 2 * 64 + 15) == WORKSPACE    # needs 8 * W * N + 16 bytes
     assert f(s=_shape(W=0)) == OK
+    assert f(s=_shape(W=0), ws=FAKE, wsb=16) == OK
 
 
 def test_proxy_and_drift_argument_checks(L):

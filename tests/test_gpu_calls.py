@@ -202,14 +202,20 @@ def test_farthest_seeding_matches(P, bf):
     assert close(host(C), r["C"], 1e-6, 1e-7)
 
 
+# hidden sizes covering every thread layout of the coder, full and ragged:
+# one wave with 1, 2 or 4 blocks of 16 per thread, four waves with 2
 RES_CASES = [("bf16-4096", 2, 97, 4096, 5, True), ("bf16-80", 3, 50, 80, 4, True),
-             ("f32-64", 2, 64, 64, 3, False), ("bf16-8192", 1, 9, 8192, 2, True)]
+             ("f32-64", 2, 64, 64, 3, False), ("bf16-8192", 1, 9, 8192, 2, True),
+             ("bf16-3584", 2, 40, 3584, 4, True), ("f32-2048", 1, 33, 2048, 3, False),
+             ("bf16-1040", 2, 21, 1040, 3, True), ("bf16-6160", 1, 7, 6160, 2, True),
+             ("f32-4096", 1, 20, 4096, 3, False)]
 
 
+@pytest.mark.parametrize("grouped", [False, True], ids=["row-order", "grouped"])
 @pytest.mark.parametrize("case", RES_CASES, ids=[c[0] for c in RES_CASES])
-def test_residual_bit_exact(P, case):
+def test_residual_bit_exact(P, case, grouped):
     name, W, N, d, K, bf = case
-    say("residual", name)
+    say("residual", name, "grouped" if grouped else "row order")
     rng = np.random.default_rng(11)
     H32 = (rng.standard_normal((W, N, d)) * np.exp(rng.uniform(-4, 4, (W, N, 1)))).astype(np.float32)
     H32[0, 1] = 0.0                                   # zero row
@@ -237,7 +243,8 @@ def test_residual_bit_exact(P, case):
     codes = torch.zeros(W, N, d // 2, dtype=torch.uint8, device="cuda")
     bsc = torch.zeros(W, N, d // 16, dtype=torch.uint8, device="cuda")
     rsc = torch.zeros(W, N, device="cuda")
-    P.ps_residual_nvfp4(s, dt, dev(H), dev(rn), dev(C), dev(assign), codes, bsc, rsc)
+    ws = torch.empty(8 * W * N + 16, dtype=torch.uint8, device="cuda") if grouped else None  # the minimum
+    P.ps_residual_nvfp4(s, dt, dev(H), dev(rn), dev(C), dev(assign), codes, bsc, rsc, ws)
     torch.cuda.synchronize()
     r = O.residual_nvfp4(O.Shape(W=W, N=N, d=d, K=K), O.BF16 if bf else O.F32, H, rn, C, assign)
     assert np.array_equal(host(rsc).view(np.uint32), r["rscale"].view(np.uint32))
@@ -270,7 +277,8 @@ def test_residual_ties_and_saturation(P):
     codes = torch.zeros(1, N, d // 2, dtype=torch.uint8, device="cuda")
     bsc = torch.zeros(1, N, d // 16, dtype=torch.uint8, device="cuda")
     rsc = torch.zeros(1, N, device="cuda")
-    P.ps_residual_nvfp4(s, P.PS_F32, dev(H), dev(rn), dev(C), dev(a), codes, bsc, rsc)
+    P.ps_residual_nvfp4(s, P.PS_F32, dev(H), dev(rn), dev(C), dev(a), codes, bsc, rsc,
+                        torch.empty(8 * N + 16, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     r = O.residual_nvfp4(O.Shape(W=1, N=N, d=d, K=1), O.F32, H, rn, C, a)
     assert np.array_equal(host(rsc).view(np.uint32), r["rscale"].view(np.uint32))
