@@ -640,6 +640,90 @@ __global__ __launch_bounds__(64) void k_bucket(const int32_t* __restrict__ assig
 }
 
 // ---------------------------------------------------------------------------
+// ordered member sums (update and keys): a batch of up to 256 members of one
+// cluster is staged in LDS (row ids and weights, in ascending member order),
+// then every thread sums its 8 * CH elements [e0 + 8 (t + 256 c), + 8) over
+// the batch in that order, in fp64.  Two members' rows are requested while
+// the previous two are added; every load is issued unconditionally (past the
+// batch: the last member again, past the row: its last 8 elements, neither
+// added), so each wait covers exactly the rows it needs.
+// ---------------------------------------------------------------------------
+template <typename T, int CH, bool WEIGHTED>
+__device__ __forceinline__ void member_sums(const T* __restrict__ rows, int rowlen, int e0,
+                                            const int* mid, const double* mw, int nv, double (&acc)[CH][8])
+{
+    if (nv <= 0) return;
+    int off[CH];
+    bool in_row[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int e = e0 + (int)(threadIdx.x + 256 * c) * 8;
+        in_row[c] = e < rowlen;
+        off[c] = min(e, rowlen - 8);
+    }
+    float A[2][CH][8], B[2][CH][8];
+    auto load = [&](int m, float (&X)[2][CH][8]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const T* r = rows + (size_t)mid[min(m + u, nv - 1)] * rowlen;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) load8(r + off[c], X[u][c]);
+        }
+    };
+    auto add = [&](int m, const float (&X)[2][CH][8]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (m + u >= nv) break;
+            const double wt = WEIGHTED ? mw[m + u] : 1.0;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                if (!in_row[c]) continue;   // past the row: the sums stay exact zeros
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[c][i] = WEIGHTED ? fma((double)X[u][c][i], wt, acc[c][i]) : acc[c][i] + (double)X[u][c][i];
+            }
+        }
+    };
+    load(0, A);
+    for (int m = 0; m < nv; m += 4) {
+        load(m + 2, B);
+        add(m, A);
+        load(m + 4, A);
+        add(m + 2, B);
+    }
+}
+
+// Stage members [b0, b0 + 256) of the ascending list pm[beg .. end) into LDS,
+// keeping those `keep` accepts, in order; returns how many were kept.  The
+// caller's previous batch must no longer be read (a barrier comes first).
+template <typename Keep>
+__device__ __forceinline__ int stage_members(const int32_t* __restrict__ pm, int b0, int end, int* mid,
+                                             double* mw, int* wcnt, Keep keep)
+{
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    int j = 0;
+    double wt = 0.0;
+    bool ok = false;
+    if (b0 + t < end) {
+        j = pm[b0 + t];
+        ok = keep(j, wt);
+    }
+    const uint64_t bal = __ballot(ok);
+    __syncthreads();
+    if (lane == 0) wcnt[wv] = __popcll(bal);
+    __syncthreads();
+    int pos = __popcll(bal & ((1ull << lane) - 1ull));
+    for (int q = 0; q < wv; ++q) pos += wcnt[q];
+    if (ok) {
+        mid[pos] = j;
+        mw[pos] = wt;
+    }
+    const int nv = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    __syncthreads();
+    return nv;
+}
+
+// ---------------------------------------------------------------------------
 // update: one workgroup per (window, cluster)
 // ---------------------------------------------------------------------------
 template <typename T, int CH>
@@ -660,59 +744,23 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
     const T* Hw = H + (size_t)w * N * d;
     const float* rn = row_norm + (size_t)w * N;
 
+    __shared__ int mid[256];
+    __shared__ double mw[256];
+    __shared__ int wcnt[4];
     double acc[CH][8];
 #pragma unroll
     for (int c = 0; c < CH; ++c)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[c][i] = 0.0;
-
-    int m = beg;
-    for (; m + 2 <= end; m += 2) {
-        const int j0 = pm[m], j1 = pm[m + 1];
-        const float n0 = rn[j0], n1 = rn[j1];
-        float v0[CH][8], v1[CH][8];
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int e = (threadIdx.x + 256 * c) * 8;
-            if (e < d) {
-                load8(Hw + (size_t)j0 * d + e, v0[c]);
-                load8(Hw + (size_t)j1 * d + e, v1[c]);
-            } else {
-                // past the row: contribute exact zeros (they enter ||S||)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v0[c][i] = v1[c][i] = 0.0f;
-            }
-        }
-        if (n0 > 0.0f) {
-            const double inv = 1.0 / (double)n0;
-#pragma unroll
-            for (int c = 0; c < CH; ++c)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[c][i] = fma((double)v0[c][i], inv, acc[c][i]);
-        }
-        if (n1 > 0.0f) {
-            const double inv = 1.0 / (double)n1;
-#pragma unroll
-            for (int c = 0; c < CH; ++c)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[c][i] = fma((double)v1[c][i], inv, acc[c][i]);
-        }
-    }
-    for (; m < end; ++m) {
-        const int j0 = pm[m];
-        const float n0 = rn[j0];
-        if (!(n0 > 0.0f)) continue;
-        const double inv = 1.0 / (double)n0;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int e = (threadIdx.x + 256 * c) * 8;
-            if (e < d) {
-                float v0[8];
-                load8(Hw + (size_t)j0 * d + e, v0);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[c][i] = fma((double)v0[i], inv, acc[c][i]);
-            }
-        }
+    // members whose norm is not positive (zero, or a non-finite row) add nothing
+    for (int b0 = beg; b0 < end; b0 += 256) {
+        const int nv = stage_members(pm, b0, end, mid, mw, wcnt, [&](int j, double& wt) {
+            const float n = rn[j];
+            if (!(n > 0.0f)) return false;
+            wt = 1.0 / (double)n;
+            return true;
+        });
+        member_sums<T, CH, true>(Hw, d, 0, mid, mw, nv, acc);
     }
     double ss = 0.0;
 #pragma unroll
@@ -746,40 +794,43 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
 }
 
 // centroid keys: mean of the member key rows, fp64 in ascending member order,
-// rounded to fp32 then dtype.  Four members' loads are in flight at a time.
+// rounded to fp32 then dtype; each thread owns 16 elements of a 4096-element
+// block of the key row, blocks in turn
 template <typename T>
 __global__ __launch_bounds__(256) void k_keys(const T* __restrict__ Kr, const int32_t* __restrict__ perm,
                                                const int32_t* __restrict__ offs, T* __restrict__ Ck,
                                                int N, int KV, int K, int nblocks)
 {
+    constexpr int CH = 2;
     const int Lg = xcd_remap(blockIdx.x, nblocks);
     const int w = Lg / K, k = Lg - w * K;
     const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
     if (end == beg) return;
     const int32_t* pm = perm + (size_t)w * N;
     const T* Kw = Kr + (size_t)w * N * KV;
-    for (int e = threadIdx.x * 8; e < KV; e += 256 * 8) {
-        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        int m = beg;
-        for (; m + 4 <= end; m += 4) {
-            float v[4][8];
+    __shared__ int mid[256];
+    __shared__ double mw[256];
+    __shared__ int wcnt[4];
+    for (int e0 = 0; e0 < KV; e0 += 256 * 8 * CH) {
+        double acc[CH][8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) load8(Kw + (size_t)pm[m + u] * KV + e, v[u]);
+        for (int c = 0; c < CH; ++c)
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += (double)v[u][i];
+            for (int i = 0; i < 8; ++i) acc[c][i] = 0.0;
+        for (int b0 = beg; b0 < end; b0 += 256) {
+            const int nv = stage_members(pm, b0, end, mid, mw, wcnt, [](int, double&) { return true; });
+            member_sums<T, CH, false>(Kw, KV, e0, mid, mw, nv, acc);
         }
-        for (; m < end; ++m) {
-            float v[8];
-            load8(Kw + (size_t)pm[m] * KV + e, v);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += (double)v[i];
+        for (int c = 0; c < CH; ++c) {
+            const int e = e0 + (int)(threadIdx.x + 256 * c) * 8;
+            if (e < KV) {
+                float o[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = (float)(acc[c][i] / (double)(end - beg));
+                store8(Ck + ((size_t)w * K + k) * KV + e, o);
+            }
         }
-        float o[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = (float)(acc[i] / (double)(end - beg));
-        store8(Ck + ((size_t)w * K + k) * KV + e, o);
     }
 }
 
