@@ -277,6 +277,8 @@ def main():
     ap.add_argument("--residual-store", default="device", choices=["device", "host"],
                     help="keep the NVFP4 residual store in HBM, or in pinned host memory as the "
                          "pages' CPU offload (copied out each step, selected rows fetched back)")
+    ap.add_argument("--no-scoring-only", action="store_true",
+                    help="skip the secondary timing of the scoring half of the step on fixed clusters")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the secondary timing of the same steps replayed from HIP graphs")
     ap.add_argument("--no-overlap", action="store_true",
@@ -336,12 +338,16 @@ def main():
 
     if not args.no_profile:
         P.profile_begin(64 * args.steps * (cfg.iters + 8))
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    marks[0].record()
     for i in range(args.warmup, total):
         path.step(*wl.inputs(i))
+        marks[i - args.warmup + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     prof = {}
     if not args.no_profile:
         P.profile_end()
@@ -408,6 +414,21 @@ def main():
                    "graphs": len(path._graphs)}
         print(f"[bench] graph replay: {graphed['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # secondary figure: the scoring half only (proxy attention and drift,
+    # top-k, gather, commit rules) on the clusters of the last clustered step
+    scoring = None
+    if not args.no_scoring_only and args.cluster_score == "kl":
+        ins = [wl.inputs(i) for i in range(args.warmup, total)]
+        path.step(*ins[0], recluster=False)
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        for x in ins:
+            path.step(*x, recluster=False)
+        torch.cuda.synchronize()
+        s1 = time.perf_counter()
+        scoring = {"value": args.steps * cfg.W * cfg.N / (s1 - s0), "ms_per_step": 1e3 * (s1 - s0) / args.steps}
+        print(f"[bench] scoring only: {scoring['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+
     hiding = None
     if not args.no_overlap:
         print("[bench] latency hiding beside a stand-in forward", file=sys.stderr, flush=True)
@@ -436,6 +457,8 @@ def main():
         "cpu_baseline": cpu,
         "fixed_point_exit": fpx,
         "graph_replay": graphed,
+        "scoring_only": scoring,
+        "step_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1]},
         "latency_hiding": hiding,
         "kernels": breakdown,
     }

@@ -146,23 +146,29 @@ class DriftPath:
     def logp_prev(self):
         return self.logp[(self.t - 1) & 1]
 
-    def step(self, H, Kr, V, Q, conf=None, stream=None):
+    def step(self, H, Kr, V, Q, conf=None, stream=None, recluster=True):
         """Run one step on device tensors H [W][N][d], Kr/V [W][N][Hkv][dh],
         Q [W][Nb][Hq][dh] and, optionally, the per-position confidences
         conf [W][N] f32 that the commit rules read; returns t of the step just
-        run."""
+        run.  recluster=False keeps the clusters, centroid keys and residual
+        codes of the last clustered step and runs only the scoring half
+        (proxy attention and drift, top-k, gather, commit rules): the reading
+        in which clustering happens at window formation only."""
         sp, s, dt = self.spec, self.shape, self.dtype
         first = self.t == 0
+        if not recluster and (first or self.score_cos is not None):
+            raise ValueError("recluster=False needs a formed window and the KL cluster score")
         init = {"strided": PS_INIT_STRIDED, "farthest": PS_INIT_FARTHEST}[sp.init0] if first \
             else PS_INIT_GIVEN
         cosine = self.score_cos is not None and not first
         if cosine:
             with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
                 self.C_prev.copy_(self.C)
-        ps_kmeans_fit(s, dt, H, Kr, init, sp.iters, self.C, self.assign, self.counts, self.row_norm,
-                      self.Ck, self.objective, self.ws, stream, flags=sp.kmeans_flags)
-        ps_residual_nvfp4(s, dt, H, self.row_norm, self.C, self.assign, self.codes, self.bscale,
-                          self.rscale, self.ws, stream)
+        if recluster:
+            ps_kmeans_fit(s, dt, H, Kr, init, sp.iters, self.C, self.assign, self.counts, self.row_norm,
+                          self.Ck, self.objective, self.ws, stream, flags=sp.kmeans_flags)
+            ps_residual_nvfp4(s, dt, H, self.row_norm, self.C, self.assign, self.codes, self.bscale,
+                              self.rscale, self.ws, stream)
         main = stream if stream is not None else torch.cuda.current_stream()
         if self.store is not None and not first:     # formation gathers nothing
             self.coded.record(main)

@@ -46,9 +46,10 @@ def oshape(cfg, W=1):
     return O.Shape(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
 
 
-def oracle_step(cfg, st, data, conf, t, iters=None, cluster_score="kl"):
+def oracle_step(cfg, st, data, conf, t, iters=None, cluster_score="kl", recluster=True):
     """One oracle step for one window; st carries the oracle's own C, Ck,
-    logp and commit history between steps."""
+    logp and commit history between steps.  recluster=False keeps the last
+    step's clusters, keys and residual codes and runs only the scoring half."""
     s = oshape(cfg)
     dt = O.BF16 if cfg.bf16 else O.F32
     iters = cfg.iters if iters is None else iters
@@ -60,8 +61,12 @@ def oracle_step(cfg, st, data, conf, t, iters=None, cluster_score="kl"):
     else:
         init, C, Ck = O.INIT_GIVEN, st["C"].copy(), st["Ck"].copy()
         hist_sum, hist_n = st["hist_sum"].copy(), st["hist_n"].copy()
-    r = O.kmeans_fit(s, dt, data["H"], data["Kr"], init, iters, C, Ck)
-    q = O.residual_nvfp4(s, dt, data["H"], r["row_norm"], r["C"], r["assign"])
+    if recluster:
+        r = O.kmeans_fit(s, dt, data["H"], data["Kr"], init, iters, C, Ck)
+        q = O.residual_nvfp4(s, dt, data["H"], r["row_norm"], r["C"], r["assign"])
+    else:
+        r = {key: st[key] for key in ("C", "Ck", "assign", "counts", "row_norm")}
+        q = {key: st[key] for key in ("codes", "bscale", "rscale")}
     pa = O.proxy_attn(s, dt, data["Q"], r["Ck"], cfg.softmax_scale,
                       None if t == 0 else st["logp"])
     out = dict(C=r["C"], Ck=r["Ck"], assign=r["assign"], counts=r["counts"], row_norm=r["row_norm"],
@@ -190,10 +195,12 @@ def replay_first_difference(P, cfg, data, C_gpu, Ck_gpu, ost, t):
     raise AssertionError(f"step {t}: the step's assignment differs but no replayed iteration does")
 
 
-def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl", residual_store="device"):
+def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl", residual_store="device",
+                score_only_from=None):
     """GPU DriftPath over `steps` steps with the commit rules; the oracle runs
-    its own chain for each sampled window.  Returns the number of windows whose
-    chains parted at a near-tie."""
+    its own chain for each sampled window.  From step score_only_from on, both
+    sides keep their clusters and run only the scoring half.  Returns the
+    number of windows whose chains parted at a near-tie."""
     from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
     W = cfg.W if W is None else W
     windows = list(range(W)) if windows is None else windows
@@ -237,16 +244,19 @@ def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl", residua
         say(f"  {cfg.name} step {t}: GPU")
         prevC = {w: host(path.C[w:w + 1]).copy() for w in windows}
         prevCk = {w: host(path.Ck[w:w + 1]).copy() for w in windows}
-        path.step(Hd, Krd, Vd, Qd, conf=confd)
+        recluster = score_only_from is None or t < score_only_from
+        path.step(Hd, Krd, Vd, Qd, conf=confd, recluster=recluster)
         torch.cuda.synchronize()
         for w in windows:
             gs = gpu_snapshot(path, w, t)
-            check_centre_properties(host_data[w]["H"][0], cfg.bf16, gs["row_norm"][0],
-                                    gs["assign"][0], gs["C"][0], gs["counts"][0])
+            if recluster:     # the clusters describe this step's rows
+                check_centre_properties(host_data[w]["H"][0], cfg.bf16, gs["row_norm"][0],
+                                        gs["assign"][0], gs["C"][0], gs["counts"][0])
             if w in parted:
                 continue
             say(f"  {cfg.name} step {t}: oracle window {w}")
-            o = oracle_step(cfg, ost[w], host_data[w], conf[w], t, cluster_score=cluster_score)
+            o = oracle_step(cfg, ost[w], host_data[w], conf[w], t, cluster_score=cluster_score,
+                            recluster=recluster)
             if not np.array_equal(gs["assign"], o["assign"]):
                 ties = replay_first_difference(P, cfg, host_data[w], prevC[w], prevCk[w], ost[w], t)
                 say(f"    window {w} step {t}: chains part at {len(ties)} near-tie rows")
@@ -285,6 +295,15 @@ def test_llada_layer_chained_host_residual_store(P):
     cfg = synth.CONFIGS["C2"].with_(W=2)
     say("llada layer (host residual store): windows parted at a near-tie:",
         run_chained(P, cfg, steps=3, residual_store="host"))
+
+
+def test_llada_layer_scoring_only_steps(P):
+    """Two clustered steps, then two steps that keep the clusters, keys and
+    residual codes and only score (proxy attention and drift, top-k, gather
+    with the step's own K/V rows, commit rules)."""
+    cfg = synth.CONFIGS["C2"].with_(W=2)
+    say("llada layer (scoring-only steps): windows parted at a near-tie:",
+        run_chained(P, cfg, steps=4, score_only_from=2))
 
 
 def test_dream_layer_chained(P):
