@@ -183,16 +183,21 @@ def latency_hiding(path, wl, first_input, steps):
             "hidden_fraction": 1.0 - exposed / t_d, "steps": steps}
 
 
-def bandwidth():
-    """Practical HBM ceilings with torch's own streaming kernels on 4 GiB:
-    a read-only reduction and an elementwise copy (read + write)."""
+def ceilings():
+    """Practical ceilings on this GPU, measured with torch's own kernels: HBM
+    streaming as an elementwise copy of 4 GiB (read + write bytes counted) and a
+    large bf16 GEMM (hipBLASLt) for the matrix cores."""
     import torch
     n = 1 << 31
     a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
     b = torch.empty_like(a)
+    m = 8192
+    x = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    z = torch.empty(m, m, device="cuda", dtype=torch.bfloat16)
     out = {}
-    for name, fn, nbytes in (("read_sum", lambda: a.sum(dtype=torch.float32), 2 * n),
-                             ("copy_neg", lambda: torch.neg(a, out=b), 4 * n)):
+    for name, fn, work, unit in (("hbm_copy", lambda: torch.neg(a, out=b), 4 * n, "GBs"),
+                                 ("bf16_gemm", lambda: torch.matmul(x, y, out=z), 2 * m ** 3, "TFLOPs")):
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -201,8 +206,15 @@ def bandwidth():
             fn()
         e1.record()
         torch.cuda.synchronize()
-        out[name + "_GBs"] = nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    print(json.dumps(out))
+        rate = work * 10 / (e0.elapsed_time(e1) * 1e-3)
+        out[f"{name}_{unit}"] = rate / (1e9 if unit == "GBs" else 1e12)
+    del a, b, x, y, z
+    torch.cuda.empty_cache()
+    return out
+
+
+def bandwidth():
+    print(json.dumps(ceilings()))
 
 
 def cpu_baseline(cfg, budget_s):
@@ -286,7 +298,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (counter calibration) and exit")
     ap.add_argument("--bandwidth", action="store_true",
-                    help="only measure streaming read and copy bandwidth and exit")
+                    help="only measure the practical HBM and bf16 GEMM ceilings and exit")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip measuring the practical HBM and bf16 GEMM ceilings")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -440,6 +454,13 @@ def main():
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg, args.cpu_budget)
 
+    measured = None
+    if not args.no_ceilings:
+        measured = ceilings()
+        if roof:
+            key = "hbm_copy_GBs" if roof["unit"] == "GB/s" else "bf16_gemm_TFLOPs"
+            measured["dominant_kernel_frac_of_measured"] = roof["achieved"] / measured[key]
+
     line = {
         "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -454,6 +475,7 @@ def main():
                               "block_start": cfg.block_start},
                    "input_snapshots": n_snap, "parallelism": "single GPU"},
         "roofline": roof,
+        "measured_ceilings": measured,
         "cpu_baseline": cpu,
         "fixed_point_exit": fpx,
         "graph_replay": graphed,

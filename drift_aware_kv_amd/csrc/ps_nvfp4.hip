@@ -462,14 +462,14 @@ __global__ __launch_bounds__(256) void k_group_rows(const int32_t* __restrict__ 
 // The coder over grouped rows: each wave codes kGroupRows consecutive entries
 // of its window's perm, one row at a time, and keeps the current cluster's
 // centre blocks in registers, reloading them only when the cluster changes, so
-// each centre is read about once per wave instead of once per row.  The next
-// row's h is requested before the current row is coded.  Rows the fast path
-// declines are appended to a list for k_residual_listed.  One wave per row
-// (rows of up to 4096 elements); the workgroups of a window stay on one XCD.
+// each centre is read about once per wave instead of once per row.  Rows the
+// fast path declines are appended to a list for k_residual_listed.  One wave
+// per row (rows of up to 4096 elements), three waves per SIMD (168
+// registers); the workgroups of a window stay on one XCD.
 constexpr int kGroupRows = 16;
 
 template <typename T, int BPL, bool FULL>
-__global__ __launch_bounds__(256) void k_residual_grouped(const T* __restrict__ H, const float* __restrict__ row_norm,
+__global__ __launch_bounds__(256, 3) void k_residual_grouped(const T* __restrict__ H, const float* __restrict__ row_norm,
                                                            const float* __restrict__ C,
                                                            const int32_t* __restrict__ assign,
                                                            const int32_t* __restrict__ perm,
@@ -488,21 +488,16 @@ __global__ __launch_bounds__(256) void k_residual_grouped(const T* __restrict__ 
     const int lane = (int)(threadIdx.x & 63), nb = d >> 4;
     const size_t wrow = (size_t)w * N;
     const int32_t* pw = perm + wrow;
-    // perm holds a permutation of 0 .. N-1; the clamp only keeps reads in bounds
-    int j = min(max(pw[p0], 0), N - 1);
-    uint4 hq[BPL][HW];
-    load_hblocks<T, 64, BPL>(H + (wrow + j) * d, lane, nb, hq);
     float cv[BPL][16];
     int cur = -1;
     for (int p = p0; p < p1; ++p) {
+        const int j = min(max(pw[p], 0), N - 1);
         const size_t row = wrow + j;
         int a = assign[row];
         if (a < 0 || a >= K) a = 0;
         const float n = row_norm[row];
-        const bool more = p + 1 < p1;
-        const int jn = more ? min(max(pw[p + 1], 0), N - 1) : j;
-        uint4 hn[BPL][HW];
-        if (more) load_hblocks<T, 64, BPL>(H + (wrow + jn) * d, lane, nb, hn);
+        uint4 hq[BPL][HW];
+        load_hblocks<T, 64, BPL>(H + row * d, lane, nb, hq);
         if (a != cur) {
             load_cblocks<64, BPL>(C + ((size_t)w * K + a) * d, lane, nb, cv);
             cur = a;
@@ -511,13 +506,6 @@ __global__ __launch_bounds__(256) void k_residual_grouped(const T* __restrict__ 
                                                 bscale + row * (size_t)(d >> 4), rscale + row, d, nullptr)) {
             if (lane == 0) list[atomicAdd(listed, 1)] = (int32_t)row;
         }
-        if (more) {
-#pragma unroll
-            for (int b = 0; b < BPL; ++b)
-#pragma unroll
-                for (int q = 0; q < HW; ++q) hq[b][q] = hn[b][q];
-        }
-        j = jn;
     }
 }
 
