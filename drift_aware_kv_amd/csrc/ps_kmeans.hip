@@ -523,6 +523,188 @@ __global__ __launch_bounds__(512) void k_assign_wide(const uint16_t* __restrict_
     }
 }
 
+// ---------------------------------------------------------------------------
+// assignment, bf16, K > 128, d a multiple of 32, the Lloyd passes after the
+// first (the first, which also sums the row norms, runs k_assign_wide): the
+// tile kernel above with its operands brought in by buffer loads that write
+// LDS directly (no staging registers), four 32 KB stages deep, so three
+// 32-wide chunks of centres and tokens are in flight while one is multiplied.
+// Same tiles, wave layout and per-score accumulation order as k_assign_wide,
+// so identical scores.
+//
+// A stage holds a 256-row centre tile and a 256-row token tile of 64-byte rows
+// (32 bf16).  Row r keeps its four 16-byte pieces at slots p ^ ((r >> 2) & 3),
+// so the sixteen rows a fragment read touches hit distinct banks.  Each wave
+// moves 2 x 16 rows of each tile per stage (one buffer load of 64 lanes x 16
+// bytes writes 1 KB of LDS: lane l -> row + (l >> 2), slot l & 3); rows past K
+// or N lie past the buffer descriptors' ranges and load as zeros.  The waits
+// are explicit: before chunk c is read, each wave waits until at most the
+// loads of the (up to two) later chunks are outstanding, then all waves meet
+// at a barrier, after which the buffer of chunk c - 1 is free for chunk c + 3.
+// ---------------------------------------------------------------------------
+// raw buffer descriptor over `bytes` bytes at p (gfx9 descriptor word 3):
+// offsets at or past `bytes` read as zero
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+constexpr int kDmaDK = 32;                            // d elements per stage
+constexpr int kDmaStages = 4;
+constexpr int kDmaTile = 256 * 64;                    // one operand tile (bytes)
+constexpr size_t kDmaLds = (size_t)kDmaStages * 2 * kDmaTile;   // 128 KB
+
+// s_waitcnt with vmcnt <= n (n < 16), lgkmcnt 0, expcnt untouched (gfx9 encoding)
+#define PS_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((n) | (0x7 << 4))
+
+__global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restrict__ H,
+                                                          const uint16_t* __restrict__ Cb,
+                                                          int32_t* __restrict__ assign, int N, int d, int K,
+                                                          int tiles, int nblocks, int32_t* __restrict__ dirty,
+                                                          const int32_t* __restrict__ conv)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t wlds[];
+    const int L = xcd_remap(blockIdx.x, nblocks);
+    const int w = L / tiles, tile = L - w * tiles;
+    if (conv[w]) return;  // window at a fixed point: nothing can change
+    const int tid = threadIdx.x, lane = lane_id(), v = tid >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int cq = v & 3, th = v >> 2;
+    const int tok0 = tile * 256;
+    const uint32_t rowb = (uint32_t)d * 2u;
+    const __amdgpu_buffer_rsrc_t hrs = window_rsrc(H + (size_t)w * N * d, (uint32_t)N * rowb);
+    const __amdgpu_buffer_rsrc_t crs = window_rsrc(Cb + (size_t)w * K * d, (uint32_t)K * rowb);
+    const int nchunks = d / kDmaDK;
+    const int swz = 16 * (q ^ ((r16 >> 2) & 3));        // slot of piece q in the rows this lane reads
+
+    // this lane's rows and slots in the two 16-row blocks its wave moves
+    int mrow[2];
+    uint32_t mpiece[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        mrow[i] = 16 * (2 * v + i) + (lane >> 2);
+        mpiece[i] = 16u * (uint32_t)((lane & 3) ^ ((mrow[i] >> 2) & 3));
+    }
+    float bestv[8];
+    int besti[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) { bestv[nt] = -INFINITY; besti[nt] = 0; }
+
+    for (int cg = 0; cg < K; cg += kWideCl) {
+        uint32_t coff[2], hoff[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            coff[i] = (uint32_t)(cg + mrow[i]) * rowb + mpiece[i];
+            hoff[i] = (uint32_t)(tok0 + mrow[i]) * rowb + mpiece[i];
+        }
+        auto issue = [&](int c) {
+            uint8_t* cbuf = wlds + (size_t)(c & (kDmaStages - 1)) * 2 * kDmaTile;
+            uint8_t* hbuf = cbuf + kDmaTile;
+            const int so = c * kDmaDK * 2;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    crs, (__attribute__((address_space(3))) void*)(cbuf + (2 * v + i) * 1024), 16, coff[i], so, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    hrs, (__attribute__((address_space(3))) void*)(hbuf + (2 * v + i) * 1024), 16, hoff[i], so, 0, 0);
+            }
+        };
+        floatx4 acc[4][8];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) acc[mb][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+        issue(0);
+        if (nchunks > 1) issue(1);
+        if (nchunks > 2) issue(2);
+        for (int c = 0; c < nchunks; ++c) {
+            // this wave's loads of chunk c are done once at most those of the
+            // later chunks already issued (4 loads each) are outstanding
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const int later = min(2, nchunks - 1 - c);
+            if (later == 2)      PS_WAIT_VM_LGKM0(8);
+            else if (later == 1) PS_WAIT_VM_LGKM0(4);
+            else                 PS_WAIT_VM_LGKM0(0);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (c + 3 < nchunks) issue(c + 3);
+            const uint8_t* cbuf = wlds + (size_t)(c & (kDmaStages - 1)) * 2 * kDmaTile;
+            const uint8_t* hbuf = cbuf + kDmaTile;
+            bf16x8 a[4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                a[mb] = *reinterpret_cast<const bf16x8*>(cbuf + (64 * cq + 16 * mb + r16) * 64 + swz);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const bf16x8 b = *reinterpret_cast<const bf16x8*>(hbuf + (128 * th + 16 * nt + r16) * 64 + swz);
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+                    acc[mb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[mb][nt], 0, 0, 0);
+            }
+        }
+        // every wave is done reading the stages before they are refilled
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        PS_WAIT_VM_LGKM0(0);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // merge this group's scores (ascending cluster order within a lane;
+        // strict > keeps the lowest index)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int cl = cg + 64 * cq + 16 * mb + 4 * q + r;
+                    const float sv = acc[mb][nt][r];
+                    if (cl < K && sv > bestv[nt]) { bestv[nt] = sv; besti[nt] = cl; }
+                }
+    }
+    // the four lanes (q) of a token, then the four cluster quarters (waves)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int m = 16; m <= 32; m <<= 1) {
+            const float ov = __shfl_xor(bestv[nt], m, 64);
+            const int oi = __shfl_xor(besti[nt], m, 64);
+            if (ov > bestv[nt] || (ov == bestv[nt] && oi < besti[nt])) { bestv[nt] = ov; besti[nt] = oi; }
+        }
+    float* bv = reinterpret_cast<float*>(wlds);             // [2][4][128]; the stages are free now
+    int* bi = reinterpret_cast<int*>(wlds + 4096);
+    if (q == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const int t = (th * 4 + cq) * 128 + 16 * nt + r16;
+            bv[t] = bestv[nt];
+            bi[t] = besti[nt];
+        }
+    }
+    __syncthreads();
+    if (tid < 256) {
+        const int tk = tok0 + tid;
+        if (tk < N) {
+            const int h2 = tid >> 7, tt = tid & 127;
+            float best = bv[(h2 * 4) * 128 + tt];
+            int bidx = bi[(h2 * 4) * 128 + tt];
+#pragma unroll
+            for (int cqq = 1; cqq < 4; ++cqq) {
+                const float ov = bv[(h2 * 4 + cqq) * 128 + tt];
+                const int oi = bi[(h2 * 4 + cqq) * 128 + tt];
+                if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+            }
+            int32_t* ap = assign + (size_t)w * N + tk;
+            // membership changed: both clusters must be recomputed
+            const int old = *ap;
+            if (old != bidx) {
+                if (old >= 0 && old < K) dirty[(size_t)w * K + old] = 1;
+                dirty[(size_t)w * K + bidx] = 1;
+            }
+            *ap = bidx;
+        }
+    }
+}
+
 // assignment, fp32 path (exact centres): one thread per row
 __global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ H, const float* __restrict__ C,
                                                      int32_t* __restrict__ assign,
@@ -901,7 +1083,14 @@ void launch_assign_wide(const ps_shape* s, const void* H, const KmWs& ws, int32_
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !raised[dev]) {
         raised[dev] = hipFuncSetAttribute((const void*)k_assign_wide<FIRST>,
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds) == hipSuccess;
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds) == hipSuccess &&
+                      hipFuncSetAttribute((const void*)k_assign_wide_dma,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds) == hipSuccess;
+    }
+    if (!FIRST && s->d % kDmaDK == 0) {
+        PS_LAUNCH("k_assign_wide_dma", k_assign_wide_dma, dim3(nblocks), dim3(512), kDmaLds, st,
+                  (const uint16_t*)H, ws.Cb, assign, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
+        return;
     }
     PS_LAUNCH(FIRST ? "k_assign_wide<true>" : "k_assign_wide<false>", k_assign_wide<FIRST>, dim3(nblocks),
               dim3(512), kWideLds, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks,

@@ -48,8 +48,9 @@ KM_CASES = [
     ("llada-row", 1, 256, 4096, 64, 32, 128, True),
     ("dream-rows", 1, 512, 3584, 128, 4, 128, True),   # d not a multiple of 2048
     ("k1", 2, 130, 48, 1, 1, 16, True),
-    ("k256-llada-rows", 2, 700, 4096, 256, 8, 128, True),   # the 256-cluster tile kernel
+    ("k256-llada-rows", 2, 700, 4096, 256, 8, 128, True),   # the 256-cluster tile kernel (LDS-fed)
     ("k1000-four-groups", 1, 1100, 192, 1000, 2, 32, True),  # four cluster groups, ragged
+    ("k200-d80", 2, 400, 80, 200, 1, 16, True),   # d not a multiple of 32: the register-staged tile kernel
 ]
 
 
