@@ -195,10 +195,12 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
 
     int tok[NB];
     bool tv[NB];
+    const uint16_t* hrow[NB];   // the token's row, clamped into the window
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         tok[nb] = tile * 4 * TPW + wave * TPW + nb * 16 + r16;
         tv[nb] = tok[nb] < N;
+        hrow[nb] = Hw + (size_t)min(tok[nb], N - 1) * d;
     }
     float bestv[NB];
     int besti[NB];
@@ -215,42 +217,43 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+        // Every load is issued unconditionally, its address clamped into the
+        // window (row N - 1 or K - 1, column d - 8); pieces outside are zeroed
+        // where they are used.  So no load sits behind a branch, and the wait
+        // before a chunk's MFMAs covers that chunk's loads only, not the next
+        // chunk's, which stay in flight.
         uint4 cpre[PIECES];
         uint4 hcur[NB][NS], hnext[NB][NS];
         auto load_c = [&](int c0) {
 #pragma unroll
             for (int p = 0; p < PIECES; ++p) {
-                const int piece = p * 256 + threadIdx.x;
+                const int piece = min(p * 256 + (int)threadIdx.x, NPIECE - 1);
                 const int row = piece / (DK / 8), col = (piece % (DK / 8)) * 8;
-                const int cl = cg + row, e = c0 + col;
-                cpre[p] = (piece < NPIECE && cl < K && e < d)
-                              ? *reinterpret_cast<const uint4*>(Cw + (size_t)cl * d + e)
-                              : make_uint4(0, 0, 0, 0);
+                cpre[p] = *reinterpret_cast<const uint4*>(Cw + (size_t)min(cg + row, K - 1) * d +
+                                                          min(c0 + col, d - 8));
             }
         };
-        auto store_c = [&](int buf) {
+        auto store_c = [&](int buf, int c0) {
 #pragma unroll
             for (int p = 0; p < PIECES; ++p) {
                 const int piece = p * 256 + threadIdx.x;
                 const int row = piece / (DK / 8), col = (piece % (DK / 8)) * 8;
-                if (piece < NPIECE) *reinterpret_cast<uint4*>(&lds[buf][row * ROWB + col * 2]) = cpre[p];
+                const bool ok = cg + row < K && c0 + col < d;
+                if (piece < NPIECE)
+                    *reinterpret_cast<uint4*>(&lds[buf][row * ROWB + col * 2]) = ok ? cpre[p] : make_uint4(0, 0, 0, 0);
             }
         };
         auto load_h = [&](int c0, uint4 (&hr)[NB][NS]) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    const int e = c0 + 32 * s + 8 * q;
-                    hr[nb][s] = (tv[nb] && e < d)
-                                    ? *reinterpret_cast<const uint4*>(Hw + (size_t)tok[nb] * d + e)
-                                    : make_uint4(0, 0, 0, 0);
-                }
+                for (int s = 0; s < NS; ++s)
+                    hr[nb][s] = *reinterpret_cast<const uint4*>(hrow[nb] + min(c0 + 32 * s + 8 * q, d - 8));
         };
 
         load_c(0);
         load_h(0, hcur);
-        store_c(0);
+        store_c(0, 0);
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
             const bool more = c + 1 < nchunks;
@@ -261,11 +264,14 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
             const uint8_t* buf = lds[c & 1];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
+                const bool in_d = c * DK + 32 * s + 8 * q < d;
+                uint4 hv[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) hv[nb] = (tv[nb] && in_d) ? hcur[nb][s] : make_uint4(0, 0, 0, 0);
                 if (norm_pass) {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        const uint4 hv = hcur[nb][s];
-                        const uint32_t wv[4] = {hv.x, hv.y, hv.z, hv.w};
+                        const uint32_t wv[4] = {hv[nb].x, hv[nb].y, hv[nb].z, hv[nb].w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const double lo = (double)__uint_as_float(wv[i] << 16);
@@ -282,10 +288,10 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
                         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            a, __builtin_bit_cast(bf16x8, hcur[nb][s]), acc[mb][nb], 0, 0, 0);
+                            a, __builtin_bit_cast(bf16x8, hv[nb]), acc[mb][nb], 0, 0, 0);
                 }
             }
-            if (more) store_c((c + 1) & 1);
+            if (more) store_c((c + 1) & 1, (c + 1) * DK);
             __syncthreads();
             if (more) {
 #pragma unroll
