@@ -65,27 +65,44 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
             for (int mb = 0; mb < KB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NBQ; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-            for (int e0 = 0; e0 < dh; e0 += 32) {
-                const int e = e0 + 8 * q;
-                uint4 bq[NBQ];
+            // up to U 32-wide k-steps per batch (fewer for wide cluster
+            // groups, to stay in registers): all their loads are issued first,
+            // unconditionally (addresses clamped into the tensors), and pieces
+            // outside are zeroed where the MFMAs take them
+            constexpr int U = KB <= 4 ? 4 : (KB <= 8 ? 2 : 1);
+            for (int e0 = 0; e0 < dh; e0 += 32 * U) {
+                uint4 bq[U][NBQ], av[U][KB];
 #pragma unroll
-                for (int nb = 0; nb < NBQ; ++nb) {
-                    const int i = 16 * nb + r16;
-                    bq[nb] = (i < Nb && e < dh)
-                                 ? *reinterpret_cast<const uint4*>(Q + (((size_t)w * Nb + i) * Hq + h) * dh + e)
-                                 : make_uint4(0, 0, 0, 0);
+                for (int u = 0; u < U; ++u) {
+                    const int e = min(e0 + 32 * u + 8 * q, dh - 8);
+#pragma unroll
+                    for (int nb = 0; nb < NBQ; ++nb) {
+                        const int i = min(16 * nb + r16, Nb - 1);
+                        bq[u][nb] = *reinterpret_cast<const uint4*>(Q + (((size_t)w * Nb + i) * Hq + h) * dh + e);
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < KB; ++mb) {
+                        const int kk = min(cg + 16 * mb + r16, K - 1);
+                        av[u][mb] = *reinterpret_cast<const uint4*>(Ck + (((size_t)w * K + kk) * Hkv + g) * dh + e);
+                    }
                 }
 #pragma unroll
-                for (int mb = 0; mb < KB; ++mb) {
-                    const int kk = cg + 16 * mb + r16;
-                    const uint4 av = (kk < K && e < dh)
-                                         ? *reinterpret_cast<const uint4*>(Ck + (((size_t)w * K + kk) * Hkv + g) * dh + e)
-                                         : make_uint4(0, 0, 0, 0);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+                for (int u = 0; u < U; ++u) {
+                    if (e0 + 32 * u >= dh) break;
+                    const bool in_e = e0 + 32 * u + 8 * q < dh;
+                    bf16x8 b[NBQ];
 #pragma unroll
                     for (int nb = 0; nb < NBQ; ++nb)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bq[nb]),
-                                                                              acc[mb][nb], 0, 0, 0);
+                        b[nb] = __builtin_bit_cast(bf16x8, (in_e && 16 * nb + r16 < Nb) ? bq[u][nb]
+                                                                                         : make_uint4(0, 0, 0, 0));
+#pragma unroll
+                    for (int mb = 0; mb < KB; ++mb) {
+                        const bf16x8 a = __builtin_bit_cast(
+                            bf16x8, (in_e && cg + 16 * mb + r16 < K) ? av[u][mb] : make_uint4(0, 0, 0, 0));
+#pragma unroll
+                        for (int nb = 0; nb < NBQ; ++nb)
+                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nb], acc[mb][nb], 0, 0, 0);
+                    }
                 }
             }
 #pragma unroll
