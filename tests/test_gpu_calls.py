@@ -209,7 +209,8 @@ RES_CASES = [("bf16-4096", 2, 97, 4096, 5, True), ("bf16-80", 3, 50, 80, 4, True
              ("f32-64", 2, 64, 64, 3, False), ("bf16-8192", 1, 9, 8192, 2, True),
              ("bf16-3584", 2, 40, 3584, 4, True), ("f32-2048", 1, 33, 2048, 3, False),
              ("bf16-1040", 2, 21, 1040, 3, True), ("bf16-6160", 1, 7, 6160, 2, True),
-             ("f32-4096", 1, 20, 4096, 3, False)]
+             ("f32-4096", 1, 20, 4096, 3, False),
+             ("bf16-2048-k200", 2, 300, 2048, 200, True)]   # many small clusters: a new centre almost every row
 
 
 @pytest.mark.parametrize("grouped", [False, True], ids=["row-order", "grouped"])
