@@ -50,7 +50,7 @@ def kernel_work(name, cfg):
     if name.startswith("k_proxy"):
         return (W * cfg.Nb * cfg.Hq * cfg.dh * e + W * K * KV * e + L * 4,
                 2.0 * W * cfg.Hq * cfg.Nb * K * cfg.dh)
-    if name.startswith("k_drift"):
+    if name.startswith("k_drift_kl"):
         return 2 * L * 4 + W * (cfg.Hq * cfg.Nb + cfg.Nb + K) * 4, L * 4.0
     if name.startswith("k_bucket"):
         return 2 * W * N * 4 + W * (K + 1) * 4, 0.0
