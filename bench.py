@@ -14,7 +14,7 @@ the roofline of the dominant kernel (its HIP-event average launch time over the
 timed region against its algorithmic bytes) and the CPU oracle timed on a
 bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--config C4] [--gpus 1]
+  python bench.py [--steps K] [--warmup W] [--config llada8b-batch] [--gpus 1]
 """
 import argparse
 import json
@@ -29,6 +29,8 @@ METRIC = "window-token-layers drift-scored/sec per step at 1 GPU; % HBM/MFMA roo
 UNIT = "window-token-layers/s"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+# the workloads of synth.CONFIGS (the 512-window batch is the benchmark's)
+CONFIG_NAMES = ("tiny-planted", "llada8b-layer", "dream7b-layer", "llada8b-batch", "llada8b-long")
 
 
 def kernel_work(name, cfg):
@@ -281,7 +283,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="C4", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--config", default="llada8b-batch", choices=sorted(CONFIG_NAMES))
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timer")
@@ -315,7 +317,7 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this path runs on one GPU; windows are independent, so more GPUs "
                                    "would each run their own share of the windows with no "
-                                   "communication (see DESIGN.md); --gpus must be 1"}))
+                                   "communication; --gpus must be 1"}))
         sys.exit(2)
     if args.steps < 1 or args.warmup < 1:
         print("need --steps >= 1 and --warmup >= 1 (the first warmup step is window formation)",

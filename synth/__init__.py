@@ -83,23 +83,23 @@ class Config:
 CONFIGS = {
     # tiny case: 8 planted unit directions + N(0, 0.05^2) noise, d = 64 fp32,
     # 1 head whose queries are the block's hidden rows, Kr = V = H.
-    "C1": Config("tiny-planted-N256-d64-K8", W=1, N=256, d=64, Hq=1, Hkv=1, dh=64, Nb=16, K=8,
+    "tiny-planted": Config("tiny-planted-N256-d64-K8", W=1, N=256, d=64, Hq=1, Hkv=1, dh=64, Nb=16, K=8,
                  k=2, iters=10, steps=2, dtype="f32", init0="farthest", drift="gauss",
                  drift_frac=0.10, drift_mag=0.3, planted=True),
     # LLaDA-8B-shaped single layer
-    "C2": Config("llada8b-layer-N1024-K64", W=1, N=1024, d=4096, Hq=32, Hkv=32, dh=128, Nb=32,
+    "llada8b-layer": Config("llada8b-layer-N1024-K64", W=1, N=1024, d=4096, Hq=32, Hkv=32, dh=128, Nb=32,
                  K=64, k=4, iters=8, steps=20, dtype="bf16", init0="strided", drift="gauss",
                  drift_frac=0.05, drift_mag=0.3),
     # Dream-7B-shaped single layer (GQA 28/4)
-    "C3": Config("dream7b-layer-N2048-K128", W=1, N=2048, d=3584, Hq=28, Hkv=4, dh=128, Nb=32,
+    "dream7b-layer": Config("dream7b-layer-N2048-K128", W=1, N=2048, d=3584, Hq=28, Hkv=4, dh=128, Nb=32,
                  K=128, k=8, iters=8, steps=20, dtype="bf16", init0="strided", drift="rotate",
                  drift_frac=0.10, drift_mag=0.2),
     # LLaDA-8B, all 32 layers x 16 sequences
-    "C4": Config("llada8b-32layers-16seq-N1024-K64", W=512, N=1024, d=4096, Hq=32, Hkv=32,
+    "llada8b-batch": Config("llada8b-32layers-16seq-N1024-K64", W=512, N=1024, d=4096, Hq=32, Hkv=32,
                  dh=128, Nb=32, K=64, k=4, iters=8, steps=20, dtype="bf16", init0="strided",
                  drift="gauss", drift_frac=0.05, drift_mag=0.3),
     # long window stress: LLaDA-8B, 32 layers x 4 sequences, N = 8192
-    "C5": Config("llada8b-32layers-4seq-N8192-K256", W=128, N=8192, d=4096, Hq=32, Hkv=32,
+    "llada8b-long": Config("llada8b-32layers-4seq-N8192-K256", W=128, N=8192, d=4096, Hq=32, Hkv=32,
                  dh=128, Nb=32, K=256, k=16, iters=8, steps=64, dtype="bf16", init0="strided",
                  drift="student", drift_frac=0.10, drift_mag=0.3),
 }

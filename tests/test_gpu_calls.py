@@ -160,7 +160,7 @@ def test_kmeans_chained_planted_exact(P):
     """The tiny planted case, chained end to end from FARTHEST seeding over 10
     iterations, must equal the oracle exactly."""
     import synth
-    cfg = synth.CONFIGS["C1"]
+    cfg = synth.CONFIGS["tiny-planted"]
     data = synth.generate(cfg)
     s = P.Shape(W=1, N=cfg.N, d=cfg.d, Hq=1, Hkv=1, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
     so = O.Shape(W=1, N=cfg.N, d=cfg.d, Hq=1, Hkv=1, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)

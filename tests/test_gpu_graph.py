@@ -36,7 +36,7 @@ def test_graph_replays_equal_eager_steps(case):
     from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
     P.lib()
     name, over, score = case
-    cfg = synth.CONFIGS["C2"].with_(**over)
+    cfg = synth.CONFIGS["llada8b-layer"].with_(**over)
     say("graph replay", name)
     spec = StepSpec(W=cfg.W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb,
                     K=cfg.K, k=cfg.k, iters=cfg.iters, bf16=True, softmax_scale=cfg.softmax_scale,

@@ -29,7 +29,7 @@ def test_step_on_side_stream_beside_gemms_is_bit_identical():
     import drift_aware_kv_amd as P
     from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
     P.lib()
-    cfg = synth.CONFIGS["C2"].with_(W=8)
+    cfg = synth.CONFIGS["llada8b-layer"].with_(W=8)
     spec = StepSpec(W=cfg.W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb,
                     K=cfg.K, k=cfg.k, iters=cfg.iters, bf16=True, softmax_scale=cfg.softmax_scale,
                     block_start=cfg.block_start)

@@ -273,18 +273,18 @@ def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl", residua
 
 
 def test_tiny_planted_three_steps_exact(P):
-    cfg = synth.CONFIGS["C1"]
+    cfg = synth.CONFIGS["tiny-planted"]
     assert run_chained(P, cfg, steps=3) == 0
 
 
 def test_llada_layer_chained(P):
-    cfg = synth.CONFIGS["C2"]
+    cfg = synth.CONFIGS["llada8b-layer"]
     say("llada layer: windows parted at a near-tie:", run_chained(P, cfg, steps=4))
 
 
 def test_llada_layer_chained_cosine_score(P):
     """The same chain with clusters ranked by how far their centres moved."""
-    cfg = synth.CONFIGS["C2"].with_(W=4)
+    cfg = synth.CONFIGS["llada8b-layer"].with_(W=4)
     say("llada layer (cosine ranking): windows parted at a near-tie:",
         run_chained(P, cfg, steps=3, cluster_score="cosine"))
 
@@ -292,7 +292,7 @@ def test_llada_layer_chained_cosine_score(P):
 def test_llada_layer_chained_host_residual_store(P):
     """The same chain with the residual store in pinned host memory: the gather
     fetches the selected rows across PCIe."""
-    cfg = synth.CONFIGS["C2"].with_(W=2)
+    cfg = synth.CONFIGS["llada8b-layer"].with_(W=2)
     say("llada layer (host residual store): windows parted at a near-tie:",
         run_chained(P, cfg, steps=3, residual_store="host"))
 
@@ -301,20 +301,20 @@ def test_llada_layer_scoring_only_steps(P):
     """Two clustered steps, then two steps that keep the clusters, keys and
     residual codes and only score (proxy attention and drift, top-k, gather
     with the step's own K/V rows, commit rules)."""
-    cfg = synth.CONFIGS["C2"].with_(W=2)
+    cfg = synth.CONFIGS["llada8b-layer"].with_(W=2)
     say("llada layer (scoring-only steps): windows parted at a near-tie:",
         run_chained(P, cfg, steps=4, score_only_from=2))
 
 
 def test_dream_layer_chained(P):
-    cfg = synth.CONFIGS["C3"]
+    cfg = synth.CONFIGS["dream7b-layer"]
     say("dream layer: windows parted at a near-tie:", run_chained(P, cfg, steps=3))
 
 
 def test_full_size_llada_batch_sampled(P):
     """512 windows (32 layers x 16 sequences) in one launch per call, as the
     benchmark runs them; windows 0, 301 and 511 checked against the oracle."""
-    cfg = synth.CONFIGS["C4"]
+    cfg = synth.CONFIGS["llada8b-batch"]
     say("llada batch: windows parted at a near-tie:",
         run_chained(P, cfg, steps=3, windows=[0, 301, 511]))
 
@@ -323,14 +323,14 @@ def test_full_size_long_window_sampled(P):
     """128 windows of 8192 tokens, K = 256, in one launch per call; one window
     checked with one Lloyd iteration per step (the oracle needs minutes for
     eight at this size: the iteration count does not change the kernels)."""
-    cfg = synth.CONFIGS["C5"].with_(iters=1)
+    cfg = synth.CONFIGS["llada8b-long"].with_(iters=1)
     say("long window: windows parted at a near-tie:", run_chained(P, cfg, steps=2, windows=[77]))
 
 
 def test_step_is_deterministic(P):
     """The same inputs twice give bit-identical outputs (no float atomics)."""
     from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
-    cfg = synth.CONFIGS["C2"].with_(W=4)
+    cfg = synth.CONFIGS["llada8b-layer"].with_(W=4)
     spec = StepSpec(W=4, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K,
                     k=cfg.k, iters=cfg.iters, bf16=True, softmax_scale=cfg.softmax_scale)
     data = synth.generate(cfg)

@@ -21,7 +21,7 @@ def _bf16_to_f32(b):
 
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
 def test_planted_recovery_farthest(seed):
-    cfg = synth.CONFIGS["C1"]
+    cfg = synth.CONFIGS["tiny-planted"]
     data = synth.generate(cfg, seed=synth.BASE_SEED + 1000 * seed)
     s = O.Shape(W=1, N=cfg.N, d=cfg.d, Hq=1, Hkv=1, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
     C = np.zeros((1, cfg.K, cfg.d), np.float32)
@@ -35,7 +35,7 @@ def test_planted_recovery_farthest(seed):
 
 
 def test_farthest_seeds_hit_every_planted_direction():
-    cfg = synth.CONFIGS["C1"]
+    cfg = synth.CONFIGS["tiny-planted"]
     data = synth.generate(cfg)
     s = O.Shape(W=1, N=cfg.N, d=cfg.d, K=cfg.K)
     C = O.kmeans_init(s, O.F32, data["H"], O.INIT_FARTHEST)[0]
