@@ -74,6 +74,12 @@ def test_workspace_size(L):
     assert L.ps_workspace_size(ctypes.byref(_shape(K=65)), 1, ctypes.byref(n)) == SHAPE
     assert L.ps_workspace_size(ctypes.byref(_shape()), 7, ctypes.byref(n)) == DTYPE
     assert L.ps_workspace_size(None, 1, ctypes.byref(n)) == NULL
+    # the same scratch also serves the NVFP4 coder (8 W N + 16 bytes), also on
+    # shapes whose K-Means needs are smaller than that
+    for kw in (dict(W=3, N=4000, d=16, K=1), dict(W=1, N=64, d=32, K=4), dict(W=7, N=300, d=4096, K=64)):
+        for dt in (0, 1):
+            assert L.ps_workspace_size(ctypes.byref(_shape(**kw)), dt, ctypes.byref(n)) == OK
+            assert n.value >= 8 * kw["W"] * kw["N"] + 16, (kw, dt, n.value)
 
 
 def _fit(L, shape, dtype=1, init=1, iters=2, H=FAKE, ws=FAKE, ws_bytes=1 << 30, C=FAKE, Kr=None,
