@@ -530,23 +530,28 @@ __global__ __launch_bounds__(512) void k_assign_wide(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// assignment, bf16, K > 128, d a multiple of 32, the Lloyd passes after the
+// assignment, bf16, K > 128, d a multiple of 64, the Lloyd passes after the
 // first (the first, which also sums the row norms, runs k_assign_wide): the
 // tile kernel above with its operands brought in by buffer loads that write
-// LDS directly (no staging registers), four 32 KB stages deep, so three
-// 32-wide chunks of centres and tokens are in flight while one is multiplied.
-// Same tiles, wave layout and per-score accumulation order as k_assign_wide,
-// so identical scores.
+// LDS directly (no staging registers).  Same tiles, wave layout and per-score
+// accumulation order as k_assign_wide, so identical scores.
 //
-// A stage holds a 256-row centre tile and a 256-row token tile of 64-byte rows
-// (32 bf16).  Row r keeps its four 16-byte pieces at slots p ^ ((r >> 2) & 3),
-// so the sixteen rows a fragment read touches hit distinct banks.  Each wave
-// moves 2 x 16 rows of each tile per stage (one buffer load of 64 lanes x 16
-// bytes writes 1 KB of LDS: lane l -> row + (l >> 2), slot l & 3); rows past K
-// or N lie past the buffer descriptors' ranges and load as zeros.  The waits
-// are explicit: before chunk c is read, each wave waits until at most the
-// loads of the (up to two) later chunks are outstanding, then all waves meet
-// at a barrier, after which the buffer of chunk c - 1 is free for chunk c + 3.
+// A chunk is 64 d-elements: every row piece a load requests is a whole
+// 128-byte line (a 32-element chunk reads half lines, and the per-CU load
+// rate halves with it).  Tokens come from HBM and are kept two chunks ahead
+// (three 32 KB token buffers), centres come from L2 and are kept one chunk
+// ahead (two 32 KB centre buffers): 160 KB of LDS.  In chunk c's step, after
+// the barrier, each wave issues the centres of chunk c + 1 and then the
+// tokens of chunk c + 2, so before chunk c is read it waits until at most the
+// (4 loads of the) tokens of chunk c + 1 are outstanding.
+//
+// Row r of a 256-row tile keeps its eight 16-byte pieces at slots
+// p ^ ((r >> 1) & 7): the sixteen rows of one fragment read then fall on
+// sixteen distinct 16-byte bank groups.  One buffer load of a wave writes
+// 1 KB of LDS, lane l -> row 8 i + (l >> 3), slot l & 7, so the lane fetches
+// the piece that belongs in that slot; each wave moves 32 rows of each tile
+// per chunk.  Rows past K or N lie past the buffer descriptors' ranges and
+// load as zeros.
 // ---------------------------------------------------------------------------
 // raw buffer descriptor over `bytes` bytes at p (gfx9 descriptor word 3):
 // offsets at or past `bytes` read as zero
@@ -555,10 +560,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window_rsrc(const void* p, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 
-constexpr int kDmaDK = 32;                            // d elements per stage
-constexpr int kDmaStages = 4;
-constexpr int kDmaTile = 256 * 64;                    // one operand tile (bytes)
-constexpr size_t kDmaLds = (size_t)kDmaStages * 2 * kDmaTile;   // 128 KB
+constexpr int kDmaDK = 64;                            // d elements per chunk
+constexpr int kDmaTile = 256 * 128;                   // one operand tile of one chunk (bytes)
+constexpr int kDmaTokBufs = 3;
+constexpr int kDmaCenBufs = 2;
+constexpr size_t kDmaLds = (size_t)(kDmaTokBufs + kDmaCenBufs) * kDmaTile;   // 160 KB
 
 // s_waitcnt with vmcnt <= n (n < 16), lgkmcnt 0, expcnt untouched (gfx9 encoding)
 #define PS_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((n) | (0x7 << 4))
@@ -570,6 +576,8 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
                                                           const int32_t* __restrict__ conv)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t wlds[];
+    uint8_t* const tbufs = wlds;                                  // [3][256 rows][128 B]
+    uint8_t* const cbufs = wlds + kDmaTokBufs * kDmaTile;         // [2][256 rows][128 B]
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int w = L / tiles, tile = L - w * tiles;
     if (conv[w]) return;  // window at a fixed point: nothing can change
@@ -581,15 +589,17 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
     const __amdgpu_buffer_rsrc_t hrs = window_rsrc(H + (size_t)w * N * d, (uint32_t)N * rowb);
     const __amdgpu_buffer_rsrc_t crs = window_rsrc(Cb + (size_t)w * K * d, (uint32_t)K * rowb);
     const int nchunks = d / kDmaDK;
-    const int swz = 16 * (q ^ ((r16 >> 2) & 3));        // slot of piece q in the rows this lane reads
+    // slots of this lane's fragment pieces: k-step ks reads piece 4 ks + q of
+    // rows r16 (mod 16), and (r >> 1) & 7 = (r16 >> 1) & 7 for those rows
+    const int sw = (r16 >> 1) & 7;
+    const int slot0 = 16 * (q ^ sw), slot1 = 16 * ((4 + q) ^ sw);
 
-    // this lane's rows and slots in the two 16-row blocks its wave moves
-    int mrow[2];
-    uint32_t mpiece[2];
+    // the rows and pieces this lane loads: row 32 v + 8 i + (lane >> 3)
+    uint32_t mrow[4], mpiece[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        mrow[i] = 16 * (2 * v + i) + (lane >> 2);
-        mpiece[i] = 16u * (uint32_t)((lane & 3) ^ ((mrow[i] >> 2) & 3));
+    for (int i = 0; i < 4; ++i) {
+        mrow[i] = (uint32_t)(32 * v + 8 * i + (lane >> 3));
+        mpiece[i] = 16u * (uint32_t)((lane & 7) ^ ((mrow[i] >> 1) & 7));
     }
     float bestv[8];
     int besti[8];
@@ -597,23 +607,27 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
     for (int nt = 0; nt < 8; ++nt) { bestv[nt] = -INFINITY; besti[nt] = 0; }
 
     for (int cg = 0; cg < K; cg += kWideCl) {
-        uint32_t coff[2], hoff[2];
+        uint32_t coff[4], hoff[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            coff[i] = (uint32_t)(cg + mrow[i]) * rowb + mpiece[i];
-            hoff[i] = (uint32_t)(tok0 + mrow[i]) * rowb + mpiece[i];
+        for (int i = 0; i < 4; ++i) {
+            coff[i] = ((uint32_t)cg + mrow[i]) * rowb + mpiece[i];
+            hoff[i] = ((uint32_t)tok0 + mrow[i]) * rowb + mpiece[i];
         }
-        auto issue = [&](int c) {
-            uint8_t* cbuf = wlds + (size_t)(c & (kDmaStages - 1)) * 2 * kDmaTile;
-            uint8_t* hbuf = cbuf + kDmaTile;
+        auto issue_tok = [&](int c) {
+            uint8_t* buf = tbufs + (size_t)(c % kDmaTokBufs) * kDmaTile + (size_t)v * 4096;
             const int so = c * kDmaDK * 2;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < 4; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    crs, (__attribute__((address_space(3))) void*)(cbuf + (2 * v + i) * 1024), 16, coff[i], so, 0, 0);
+                    hrs, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, hoff[i], so, 0, 0);
+        };
+        auto issue_cen = [&](int c) {
+            uint8_t* buf = cbufs + (size_t)(c & 1) * kDmaTile + (size_t)v * 4096;
+            const int so = c * kDmaDK * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    hrs, (__attribute__((address_space(3))) void*)(hbuf + (2 * v + i) * 1024), 16, hoff[i], so, 0, 0);
-            }
+                    crs, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, coff[i], so, 0, 0);
         };
         floatx4 acc[4][8];
 #pragma unroll
@@ -621,35 +635,40 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) acc[mb][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-        issue(0);
-        if (nchunks > 1) issue(1);
-        if (nchunks > 2) issue(2);
+        issue_tok(0);
+        issue_cen(0);
+        if (nchunks > 1) issue_tok(1);
         for (int c = 0; c < nchunks; ++c) {
-            // this wave's loads of chunk c are done once at most those of the
-            // later chunks already issued (4 loads each) are outstanding
+            // chunk c's loads are done once at most the tokens of chunk c + 1
+            // (issued after them) are outstanding
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const int later = min(2, nchunks - 1 - c);
-            if (later == 2)      PS_WAIT_VM_LGKM0(8);
-            else if (later == 1) PS_WAIT_VM_LGKM0(4);
+            if (c + 1 < nchunks) PS_WAIT_VM_LGKM0(4);
             else                 PS_WAIT_VM_LGKM0(0);
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (c + 3 < nchunks) issue(c + 3);
-            const uint8_t* cbuf = wlds + (size_t)(c & (kDmaStages - 1)) * 2 * kDmaTile;
-            const uint8_t* hbuf = cbuf + kDmaTile;
-            bf16x8 a[4];
+            // every wave is past chunk c - 1: its buffers take chunk c + 1's
+            // centres and chunk c + 2's tokens
+            if (c + 1 < nchunks) issue_cen(c + 1);
+            if (c + 2 < nchunks) issue_tok(c + 2);
+            const uint8_t* cb = cbufs + (size_t)(c & 1) * kDmaTile;
+            const uint8_t* hb = tbufs + (size_t)(c % kDmaTokBufs) * kDmaTile;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                a[mb] = *reinterpret_cast<const bf16x8*>(cbuf + (64 * cq + 16 * mb + r16) * 64 + swz);
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const bf16x8 b = *reinterpret_cast<const bf16x8*>(hbuf + (128 * th + 16 * nt + r16) * 64 + swz);
+            for (int ks = 0; ks < 2; ++ks) {
+                const int slot = ks ? slot1 : slot0;
+                bf16x8 a[4];
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb)
-                    acc[mb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[mb][nt], 0, 0, 0);
+                    a[mb] = *reinterpret_cast<const bf16x8*>(cb + (64 * cq + 16 * mb + r16) * 128 + slot);
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) {
+                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(hb + (128 * th + 16 * nt + r16) * 128 + slot);
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+                        acc[mb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[mb][nt], 0, 0, 0);
+                }
             }
         }
-        // every wave is done reading the stages before they are refilled
+        // every wave is done reading the buffers before they are refilled
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         PS_WAIT_VM_LGKM0(0);
         __builtin_amdgcn_s_barrier();
@@ -676,7 +695,7 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
             const int oi = __shfl_xor(besti[nt], m, 64);
             if (ov > bestv[nt] || (ov == bestv[nt] && oi < besti[nt])) { bestv[nt] = ov; besti[nt] = oi; }
         }
-    float* bv = reinterpret_cast<float*>(wlds);             // [2][4][128]; the stages are free now
+    float* bv = reinterpret_cast<float*>(wlds);             // [2][4][128]; the buffers are free now
     int* bi = reinterpret_cast<int*>(wlds + 4096);
     if (q == 0) {
 #pragma unroll

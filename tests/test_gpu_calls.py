@@ -112,7 +112,13 @@ def test_kmeans_iterations(P, case):
 
 
 ITER_CASES = [("ragged-bf16", 3, 300, 80, 37, True), ("llada-rows", 2, 1024, 4096, 64, True),
-              ("f32", 2, 256, 64, 8, False)]
+              ("f32", 2, 256, 64, 8, False),
+              # above 128 clusters: passes after the first run the LDS-fed tile
+              # kernel, a single pass the register-staged one (same score order)
+              ("k256-llada-rows", 2, 700, 4096, 256, True),
+              ("k300-two-groups-ragged", 1, 640, 192, 300, True),
+              ("k150-one-chunk", 2, 300, 64, 150, True),
+              ("k200-d96", 1, 500, 96, 200, True)]   # d not a multiple of 64: register-staged passes
 
 
 @pytest.mark.parametrize("case", ITER_CASES, ids=[c[0] for c in ITER_CASES])
