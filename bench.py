@@ -33,9 +33,11 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 CONFIG_NAMES = ("tiny-planted", "llada8b-layer", "dream7b-layer", "llada8b-batch", "llada8b-long")
 
 
-def kernel_work(name, cfg):
+def kernel_work(name, cfg, gathered=None):
     """Algorithmic (bytes, flops) of ONE launch of a library kernel over all W
-    windows: every input the kernel needs read once, every output written once."""
+    windows: every input the kernel needs read once, every output written once.
+    `gathered` is the mean number of rows the refresh gather selected per
+    window (data-dependent: measured in the run)."""
     W, N, d, K = cfg.W, cfg.N, cfg.d, cfg.K
     e = 2 if cfg.bf16 else 4
     KV = cfg.Hkv * cfg.dh
@@ -62,6 +64,14 @@ def kernel_work(name, cfg):
         return W * K * d * (4 + 2), 0.0
     if name.startswith("k_group_rows"):
         return 2 * W * N * 4, 0.0
+    if name.startswith("k_gather_select"):
+        return W * N * 4 + W * cfg.k * 4 + (gathered or 0.0) * W * 4 + W * 4, 0.0
+    if name.startswith("k_gather_rows") and gathered is not None:
+        # per selected row: codes, block and row scales, norm, assignment and
+        # position read, rebuilt row written, K and V rows read and written;
+        # per window: the k selected centres read
+        per_row = d // 2 + d // 16 + 4 * 4 + d * e + 4 * KV * e
+        return gathered * W * per_row + W * cfg.k * d * 4, gathered * W * d * 4.0
     if name.startswith("k_commit_block"):
         Nb = cfg.Nb
         return W * Nb * (4 + 4 + 16 + 1 + 4) + W * 8, 0.0
@@ -377,13 +387,20 @@ def main():
     value = args.steps * cfg.W * cfg.N / elapsed
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # rows the refresh gather selected per window in the last timed step
+    gathered = float(torch.clamp(path.count, max=spec.cap).double().mean().item())
     kernels = {k: v for k, v in prof.items() if not k.startswith("#")}
-    breakdown = {k: {"launches": v[0], "avg_ms": v[1] / v[0], "total_ms_per_step": v[1] / args.steps}
-                 for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][1])}
+    breakdown = {}
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][1]):
+        breakdown[k] = {"launches": v[0], "avg_ms": v[1] / v[0], "total_ms_per_step": v[1] / args.steps}
+        work = kernel_work(k, cfg, gathered)
+        if work and not k.startswith("k_update"):   # the update's later passes re-sum dirty clusters only
+            breakdown[k]["algorithmic_GB_per_launch"] = work[0] / 1e9
+            breakdown[k]["achieved_GBs"] = work[0] / (v[1] / v[0] * 1e-3) / 1e9
     roof = None
     if kernels:
         name, (n, tot, mn, mx) = max(kernels.items(), key=lambda kv: kv[1][1])
-        work = kernel_work(name, cfg)
+        work = kernel_work(name, cfg, gathered)
         avg_s = tot / n / 1e3
         if work:
             byts, flops = work
@@ -407,7 +424,7 @@ def main():
     if kernels:
         total_bytes = 0.0
         for kname, (n, tot, mn, mx) in kernels.items():
-            work = kernel_work(kname, cfg)
+            work = kernel_work(kname, cfg, gathered)
             if work:
                 total_bytes += work[0] * (args.steps if kname.startswith("k_update") else n)
         per_step = total_bytes / args.steps
@@ -503,6 +520,7 @@ def main():
         "graph_replay": graphed,
         "scoring_only": scoring,
         "step_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1]},
+        "gathered_rows_per_window": gathered,
         "latency_hiding": hiding,
         "kernels": breakdown,
     }

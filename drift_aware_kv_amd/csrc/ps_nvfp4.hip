@@ -566,7 +566,10 @@ __global__ __launch_bounds__(64) void k_gather_select(const int32_t* __restrict_
     if (lane == 0) count[w] = running;
 }
 
-// rebuild / copy the gathered rows; grid (G, W), each workgroup strides over slots
+// rebuild / copy the gathered rows; grid (G, W), each workgroup strides over
+// slots.  A slot's reads (codes, block scales, centre row, K and V rows; up
+// to 512 pieces of each per round) are all issued before its first store, so
+// a workgroup waits on memory once per round rather than once per piece.
 template <typename T>
 __global__ __launch_bounds__(256) void k_gather_rows(const int32_t* __restrict__ pos,
                                                       const int32_t* __restrict__ count, int cap,
@@ -580,41 +583,61 @@ __global__ __launch_bounds__(256) void k_gather_rows(const int32_t* __restrict__
                                                       const T* __restrict__ Vc, T* __restrict__ K_out,
                                                       T* __restrict__ V_out, int N, int d, int K, int KV)
 {
-    const int w = blockIdx.y;
+    const int w = blockIdx.y, tid = threadIdx.x;
     const int cnt = count[w];
     const int M = cnt < cap ? cnt : cap;
-    const int kv16 = (int)((size_t)KV * sizeof(T) / 16);
+    const int nh = H_hat ? (d >> 3) : 0;                              // 8-element chunks
+    const int npc = (int)((size_t)KV * sizeof(T) / 16);               // 16-byte pieces of a K/V row
+    const int nk = Kc ? npc : 0, nv = Vc ? npc : 0;
+    const int rounds = (max(nh, max(nk, nv)) + 511) / 512;
     for (int slot = blockIdx.x; slot < M; slot += gridDim.x) {
         const int j = pos[(size_t)w * cap + slot];
         const size_t row = (size_t)w * N + j;
         const size_t orow = (size_t)w * cap + slot;
+        float g = 0.0f, n = 0.0f;
+        const float* c = C;
         if (H_hat) {
             int a = assign[row];
             if (a < 0 || a >= K) a = 0;
-            const float g = rscale[row], n = row_norm[row];
-            const float* c = C + ((size_t)w * K + a) * d;
-            for (int ch = threadIdx.x; ch < (d >> 3); ch += 256) {
-                const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + row * (size_t)(d >> 1) + 4 * ch);
-                const float sh = e4m3_decode(bscale[row * (size_t)(d >> 4) + (ch >> 1)]);
-                float cv[8], o[8];
-                load8(c + 8 * ch, cv);
+            g = rscale[row];
+            n = row_norm[row];
+            c = C + ((size_t)w * K + a) * d;
+        }
+        const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes + row * (size_t)(d >> 1));
+        const uint8_t* bs = bscale + row * (size_t)(d >> 4);
+        const uint4* ks = Kc ? reinterpret_cast<const uint4*>(Kc + row * KV) : nullptr;
+        const uint4* vs = Vc ? reinterpret_cast<const uint4*>(Vc + row * KV) : nullptr;
+        for (int r = 0; r < rounds; ++r) {
+            uint32_t word[2] = {0u, 0u}, sb[2] = {0u, 0u};
+            float cv[2][8];
+            uint4 kq[2], vq[2];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const float rh = (e2m1_decode((word >> (4 * t)) & 15u) * sh) * g;
-                    o[t] = (cv[t] + rh) * n;
+            for (int u = 0; u < 2; ++u) {
+                const int i = 512 * r + 256 * u + tid;
+                if (i < nh) {
+                    word[u] = cw[i];
+                    sb[u] = bs[i >> 1];
+                    load8(c + 8 * i, cv[u]);
                 }
-                store8(H_hat + orow * d + 8 * ch, o);
+                if (i < nk) kq[u] = ks[i];
+                if (i < nv) vq[u] = vs[i];
             }
-        }
-        if (Kc) {
-            const uint4* src = reinterpret_cast<const uint4*>(Kc + row * KV);
-            uint4* dst = reinterpret_cast<uint4*>(K_out + orow * KV);
-            for (int i = threadIdx.x; i < kv16; i += 256) dst[i] = src[i];
-        }
-        if (Vc) {
-            const uint4* src = reinterpret_cast<const uint4*>(Vc + row * KV);
-            uint4* dst = reinterpret_cast<uint4*>(V_out + orow * KV);
-            for (int i = threadIdx.x; i < kv16; i += 256) dst[i] = src[i];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = 512 * r + 256 * u + tid;
+                if (i < nh) {
+                    const float sh = e4m3_decode(sb[u]);
+                    float o[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const float rh = (e2m1_decode((word[u] >> (4 * t)) & 15u) * sh) * g;
+                        o[t] = (cv[u][t] + rh) * n;
+                    }
+                    store8(H_hat + orow * d + 8 * i, o);
+                }
+                if (i < nk) reinterpret_cast<uint4*>(K_out + orow * KV)[i] = kq[u];
+                if (i < nv) reinterpret_cast<uint4*>(V_out + orow * KV)[i] = vq[u];
+            }
         }
     }
 }
@@ -765,8 +788,9 @@ extern "C" ps_status ps_refresh_gather(const ps_shape* s, ps_dtype dtype, const 
     (void)hipGetLastError();
     PS_LAUNCH("k_gather_select", k_gather_select, dim3(s->W), dim3(64), 0, stm, assign, idx, k, cap, pos, count, s->N, s->K);
     if (cap > 0 && (H_hat || Kc || Vc)) {
+        // about one slot per workgroup at the mean selection size (N k / K rows)
         const int64_t expect = ((int64_t)s->N * k + s->K - 1) / s->K;
-        int G = (int)((expect + 3) / 4);
+        int G = (int)std::min<int64_t>(2 * expect, 65535);
         if (G < 1) G = 1;
         if (G > cap) G = cap;
         const int KV = (Kc || Vc) ? s->Hkv * s->dh : 0;

@@ -438,6 +438,70 @@ def test_refresh_gather_bit_exact(P, bf, cap_mode, store):
             assert np.all(host(pos)[w, m:] == -1)       # slots past count untouched
 
 
+GATHER_PART_CASES = [
+    # name, bf16, d, Hkv, dh, outputs (H_hat, K, V)
+    ("d8192-all", True, 8192, 8, 128, (True, True, True)),      # two rounds of rebuilt chunks
+    ("d8192-h-only", True, 8192, 8, 128, (True, False, False)),
+    ("k-only", True, 4096, 32, 128, (False, True, False)),
+    ("v-only", True, 4096, 32, 128, (False, False, True)),
+    ("kv-long-rows", True, 256, 64, 160, (False, True, True)),   # 1280 pieces: three rounds
+    ("f32-d4160-all", False, 4160, 4, 64, (True, True, True)),   # ragged second round
+]
+
+
+@pytest.mark.parametrize("case", GATHER_PART_CASES, ids=[c[0] for c in GATHER_PART_CASES])
+def test_refresh_gather_rows_and_partial_outputs(P, case):
+    """Rows longer than one round of the gather workgroup and every subset of
+    the outputs (the kernel reads only what it writes)."""
+    name, bf, d, Hkv, dh, (want_h, want_k, want_v) = case
+    say("gather", name)
+    rng = np.random.default_rng(d + Hkv)
+    W, N, K, k = 2, 150, 6, 2
+    H32 = rng.standard_normal((W, N, d)).astype(np.float32)
+    H = O.f32_to_bf16(H32) if bf else H32
+    Hf = bf16f(H) if bf else H
+    rn = np.sqrt((Hf.astype(np.float64) ** 2).sum(-1)).astype(np.float32)
+    C = rng.standard_normal((W, K, d)).astype(np.float32)
+    C /= np.linalg.norm(C, axis=-1, keepdims=True)
+    assign = rng.integers(0, K, (W, N)).astype(np.int32)
+    so = O.Shape(W=W, N=N, d=d, Hq=Hkv, Hkv=Hkv, dh=dh, K=K)
+    dt_o = O.BF16 if bf else O.F32
+    q = O.residual_nvfp4(so, dt_o, H, rn, C, assign)
+    idx = np.stack([rng.choice(K, k, replace=False) for _ in range(W)]).astype(np.int32)
+    mk = (lambda: rnd_bf16(rng, (W, N, Hkv, dh))) if bf else \
+        (lambda: rng.standard_normal((W, N, Hkv, dh)).astype(np.float32))
+    Kc, Vc = mk(), mk()
+    cap = N
+    r = O.refresh_gather(so, dt_o, assign, idx, k, cap, q["codes"], q["bscale"], q["rscale"], C, rn,
+                         want_h, Kc if want_k else None, Vc if want_v else None)
+    s = P.Shape(W=W, N=N, d=d, Hq=Hkv, Hkv=Hkv, dh=dh, K=K)
+    et = torch.bfloat16 if bf else torch.float32
+    pos = torch.full((W, cap), -1, dtype=torch.int32, device="cuda")
+    count = torch.zeros(W, dtype=torch.int32, device="cuda")
+    Hh = torch.zeros(W, cap, d, dtype=et, device="cuda") if want_h else None
+    Ko = torch.zeros(W, cap, Hkv, dh, dtype=et, device="cuda") if want_k else None
+    Vo = torch.zeros(W, cap, Hkv, dh, dtype=et, device="cuda") if want_v else None
+    P.ps_refresh_gather(s, P.PS_BF16 if bf else P.PS_F32, dev(assign), dev(idx), k, cap, pos, count,
+                        dev(q["codes"]), dev(q["bscale"]), dev(q["rscale"]), dev(C), dev(rn), Hh,
+                        dev(Kc) if want_k else None, dev(Vc) if want_v else None, Ko, Vo)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(count), r["count"])
+    u = np.uint16 if bf else np.uint32
+    for w in range(W):
+        m = int(r["count"][w])
+        assert m > 0
+        assert np.array_equal(host(pos)[w, :m], r["pos"][w, :m])
+        if want_h:
+            assert np.array_equal(host(Hh)[w, :m].view(u), r["H_hat"][w, :m].view(u))
+            assert not host(Hh)[w, m:].any(), "rows past the count untouched"
+        if want_k:
+            assert np.array_equal(host(Ko)[w, :m].view(u), r["K_out"][w, :m].view(u))
+            assert not host(Ko)[w, m:].any()
+        if want_v:
+            assert np.array_equal(host(Vo)[w, :m].view(u), r["V_out"][w, :m].view(u))
+            assert not host(Vo)[w, m:].any()
+
+
 def test_w_zero_is_a_no_op(P):
     s = P.Shape(W=0, N=64, d=32, K=4)
     z = torch.zeros(16, dtype=torch.int32, device="cuda")
