@@ -1102,17 +1102,25 @@ void launch_assign_wide(const ps_shape* s, const void* H, const KmWs& ws, int32_
 {
     const int tiles = (s->N + kWideTok - 1) / kWideTok;
     const int nblocks = s->W * tiles;
-    // the LDS limit is raised once per device (outside any stream capture
-    // that a caller may run later); a failure shows up as a launch error
+    // the LDS limits are raised once per device (outside any stream capture
+    // that a caller may run later).  Without the 160 KB the LDS-fed kernel
+    // needs, the passes run the register-staged kernel; a failure to raise the
+    // latter's limit shows up as a launch error.
+    static int8_t dma_ok[64] = {};               // 0 unknown, 1 raised, -1 refused
     static bool raised[64] = {};
     int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !raised[dev]) {
-        raised[dev] = hipFuncSetAttribute((const void*)k_assign_wide<FIRST>,
+    const bool known = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+    if (known && !raised[dev]) {
+        raised[dev] = hipFuncSetAttribute((const void*)k_assign_wide<true>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds) == hipSuccess &&
-                      hipFuncSetAttribute((const void*)k_assign_wide_dma,
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds) == hipSuccess;
+                      hipFuncSetAttribute((const void*)k_assign_wide<false>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds) == hipSuccess;
+        dma_ok[dev] = hipFuncSetAttribute((const void*)k_assign_wide_dma,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds) == hipSuccess
+                          ? 1 : -1;
+        (void)hipGetLastError();
     }
-    if (!FIRST && s->d % kDmaDK == 0) {
+    if (!FIRST && s->d % kDmaDK == 0 && known && dma_ok[dev] == 1) {
         PS_LAUNCH("k_assign_wide_dma", k_assign_wide_dma, dim3(nblocks), dim3(512), kDmaLds, st,
                   (const uint16_t*)H, ws.Cb, assign, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
         return;
