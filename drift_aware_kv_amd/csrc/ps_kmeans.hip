@@ -530,11 +530,15 @@ __global__ __launch_bounds__(512) void k_assign_wide(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// assignment, bf16, K > 128, d a multiple of 64, the Lloyd passes after the
-// first (the first, which also sums the row norms, runs k_assign_wide): the
-// tile kernel above with its operands brought in by buffer loads that write
-// LDS directly (no staging registers).  Same tiles, wave layout and per-score
-// accumulation order as k_assign_wide, so identical scores.
+// assignment, bf16, K > 128, d a multiple of 64: the tile kernel above with
+// its operands brought in by buffer loads that write LDS directly (no staging
+// registers).  Same tiles, wave layout and per-score accumulation order as
+// k_assign_wide, so identical scores.  In the first pass of a call each
+// thread also sums the squares of half a token row of every chunk (fp64, four
+// partial sums), for the row norms.  Those reads of the token tile are written
+// as inline assembly with their own wait: the compiler would otherwise make
+// them wait for every buffer load still writing LDS (the later chunks), which
+// is the prefetch this kernel is built on.
 //
 // A chunk is 64 d-elements: every row piece a load requests is a whole
 // 128-byte line (a 32-element chunk reads half lines, and the per-CU load
@@ -569,9 +573,11 @@ constexpr size_t kDmaLds = (size_t)(kDmaTokBufs + kDmaCenBufs) * kDmaTile;   // 
 // s_waitcnt with vmcnt <= n (n < 16), lgkmcnt 0, expcnt untouched (gfx9 encoding)
 #define PS_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt((n) | (0x7 << 4))
 
+template <bool FIRST>
 __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restrict__ H,
                                                           const uint16_t* __restrict__ Cb,
-                                                          int32_t* __restrict__ assign, int N, int d, int K,
+                                                          int32_t* __restrict__ assign,
+                                                          float* __restrict__ row_norm, int N, int d, int K,
                                                           int tiles, int nblocks, int32_t* __restrict__ dirty,
                                                           const int32_t* __restrict__ conv)
 {
@@ -580,13 +586,16 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
     uint8_t* const cbufs = wlds + kDmaTokBufs * kDmaTile;         // [2][256 rows][128 B]
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int w = L / tiles, tile = L - w * tiles;
-    if (conv[w]) return;  // window at a fixed point: nothing can change
+    if (!FIRST && conv[w]) return;  // window at a fixed point: nothing can change
     const int tid = threadIdx.x, lane = lane_id(), v = tid >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const int cq = v & 3, th = v >> 2;
     const int tok0 = tile * 256;
     const uint32_t rowb = (uint32_t)d * 2u;
     const __amdgpu_buffer_rsrc_t hrs = window_rsrc(H + (size_t)w * N * d, (uint32_t)N * rowb);
+    // first pass: this thread's half (pieces 4 nh .. 4 nh + 3) of token row nr
+    const int nr = tid >> 1, nh = tid & 1, nsw = (nr >> 1) & 7;
+    double ss[4] = {0.0, 0.0, 0.0, 0.0};
     const __amdgpu_buffer_rsrc_t crs = window_rsrc(Cb + (size_t)w * K * d, (uint32_t)K * rowb);
     const int nchunks = d / kDmaDK;
     // slots of this lane's fragment pieces: k-step ks reads piece 4 ks + q of
@@ -667,6 +676,35 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
                         acc[mb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[mb][nt], 0, 0, 0);
                 }
             }
+            if (FIRST && cg == 0) {
+                // the four pieces of this thread's half row (chunk c is
+                // complete in LDS: its loads were waited for before the
+                // barrier, and later loads write other buffers)
+                const uint32_t base = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)(hb + nr * 128);
+                uint4 pv[4];
+                asm volatile("ds_read_b128 %0, %4\n\t"
+                             "ds_read_b128 %1, %5\n\t"
+                             "ds_read_b128 %2, %6\n\t"
+                             "ds_read_b128 %3, %7\n\t"
+                             "s_waitcnt lgkmcnt(0)"
+                             : "=&v"(pv[0]), "=&v"(pv[1]), "=&v"(pv[2]), "=&v"(pv[3])
+                             : "v"(base + 16u * (uint32_t)((4 * nh + 0) ^ nsw)),
+                               "v"(base + 16u * (uint32_t)((4 * nh + 1) ^ nsw)),
+                               "v"(base + 16u * (uint32_t)((4 * nh + 2) ^ nsw)),
+                               "v"(base + 16u * (uint32_t)((4 * nh + 3) ^ nsw))
+                             : "memory");
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t wd[4] = {pv[j].x, pv[j].y, pv[j].z, pv[j].w};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const double lo = (double)__uint_as_float(wd[t] << 16);
+                        const double hi = (double)__uint_as_float(wd[t] & 0xffff0000u);
+                        ss[t] = fma(lo, lo, ss[t]);
+                        ss[t] = fma(hi, hi, ss[t]);
+                    }
+                }
+            }
         }
         // every wave is done reading the buffers before they are refilled
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -685,6 +723,13 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
                     const float sv = acc[mb][nt][r];
                     if (cl < K && sv > bestv[nt]) { bestv[nt] = sv; besti[nt] = cl; }
                 }
+    }
+    if (FIRST) {
+        // the two halves of a row sit in adjacent lanes
+        double t = (ss[0] + ss[1]) + (ss[2] + ss[3]);
+        t += shfl_xor_d(t, 1);
+        const int tk = tok0 + nr;
+        if (nh == 0 && tk < N) row_norm[(size_t)w * N + tk] = (float)sqrt(t);
     }
     // the four lanes (q) of a token, then the four cluster quarters (waves)
 #pragma unroll
@@ -719,11 +764,13 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
                 if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
             }
             int32_t* ap = assign + (size_t)w * N + tk;
-            // membership changed: both clusters must be recomputed
-            const int old = *ap;
-            if (old != bidx) {
-                if (old >= 0 && old < K) dirty[(size_t)w * K + old] = 1;
-                dirty[(size_t)w * K + bidx] = 1;
+            if (!FIRST) {
+                // membership changed: both clusters must be recomputed
+                const int old = *ap;
+                if (old != bidx) {
+                    if (old >= 0 && old < K) dirty[(size_t)w * K + old] = 1;
+                    dirty[(size_t)w * K + bidx] = 1;
+                }
             }
             *ap = bidx;
         }
@@ -1115,14 +1162,15 @@ void launch_assign_wide(const ps_shape* s, const void* H, const KmWs& ws, int32_
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds) == hipSuccess &&
                       hipFuncSetAttribute((const void*)k_assign_wide<false>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds) == hipSuccess;
-        dma_ok[dev] = hipFuncSetAttribute((const void*)k_assign_wide_dma,
+        dma_ok[dev] = hipFuncSetAttribute((const void*)k_assign_wide_dma<FIRST>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds) == hipSuccess
                           ? 1 : -1;
         (void)hipGetLastError();
     }
-    if (!FIRST && s->d % kDmaDK == 0 && known && dma_ok[dev] == 1) {
-        PS_LAUNCH("k_assign_wide_dma", k_assign_wide_dma, dim3(nblocks), dim3(512), kDmaLds, st,
-                  (const uint16_t*)H, ws.Cb, assign, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
+    if (s->d % kDmaDK == 0 && known && dma_ok[dev] == 1) {
+        PS_LAUNCH(FIRST ? "k_assign_wide_dma<true>" : "k_assign_wide_dma<false>", k_assign_wide_dma<FIRST>,
+                  dim3(nblocks), dim3(512), kDmaLds, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K,
+                  tiles, nblocks, ws.dirty, ws.conv);
         return;
     }
     PS_LAUNCH(FIRST ? "k_assign_wide<true>" : "k_assign_wide<false>", k_assign_wide<FIRST>, dim3(nblocks),
