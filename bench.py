@@ -46,13 +46,15 @@ def kernel_work(name, cfg, gathered=None):
         return W * N * d * e + W * K * d * e + W * N * 4, 2.0 * W * N * K * d
     if name.startswith("k_update"):
         return W * N * d * e + 2 * W * N * 4 + W * K * d * (4 + e) + W * (K + 1) * 4, W * N * d * 2.0
-    if name.startswith("k_residual"):
+    if name.startswith("k_residual_grouped") or name.startswith("k_residual<"):
         return (W * N * d * e + W * K * d * 4 + 3 * W * N * 4 + W * N * d // 2 + W * N * d // 16,
                 W * N * d * 8.0)
     if name.startswith("k_keys"):
         return W * N * KV * e + W * N * 4 + W * K * KV * e, W * N * KV * 1.0
     if name.startswith("k_proxy"):
-        return (W * cfg.Nb * cfg.Hq * cfg.dh * e + W * K * KV * e + L * 4,
+        # Q and the keys read, log-probabilities written, and (after window
+        # formation, the drift fused into the epilogue) the previous step's read
+        return (W * cfg.Nb * cfg.Hq * cfg.dh * e + W * K * KV * e + 2 * L * 4,
                 2.0 * W * cfg.Hq * cfg.Nb * K * cfg.dh)
     if name.startswith("k_drift_kl"):
         return 2 * L * 4 + W * (cfg.Hq * cfg.Nb + cfg.Nb + K) * 4, L * 4.0
