@@ -542,7 +542,7 @@ __global__ __launch_bounds__(512) void k_assign_wide(const uint16_t* __restrict_
 //
 // A chunk is 64 d-elements: every row piece a load requests is a whole
 // 128-byte line (a 32-element chunk reads half lines, and the per-CU load
-// rate halves with it).  Tokens come from HBM and are kept two chunks ahead
+// rate drops by about a third with it).  Tokens come from HBM and are kept two chunks ahead
 // (three 32 KB token buffers), centres come from L2 and are kept one chunk
 // ahead (two 32 KB centre buffers): 160 KB of LDS.  In chunk c's step, after
 // the barrier, each wave issues the centres of chunk c + 1 and then the
