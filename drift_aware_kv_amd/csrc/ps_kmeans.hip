@@ -593,11 +593,11 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
     const int tok0 = tile * 256;
     const uint32_t rowb = (uint32_t)d * 2u;
     const __amdgpu_buffer_rsrc_t hrs = window_rsrc(H + (size_t)w * N * d, (uint32_t)N * rowb);
+    const __amdgpu_buffer_rsrc_t crs = window_rsrc(Cb + (size_t)w * K * d, (uint32_t)K * rowb);
+    const int nchunks = d / kDmaDK;
     // first pass: this thread's half (pieces 4 nh .. 4 nh + 3) of token row nr
     const int nr = tid >> 1, nh = tid & 1, nsw = (nr >> 1) & 7;
     double ss[4] = {0.0, 0.0, 0.0, 0.0};
-    const __amdgpu_buffer_rsrc_t crs = window_rsrc(Cb + (size_t)w * K * d, (uint32_t)K * rowb);
-    const int nchunks = d / kDmaDK;
     // slots of this lane's fragment pieces: k-step ks reads piece 4 ks + q of
     // rows r16 (mod 16), and (r >> 1) & 7 = (r16 >> 1) & 7 for those rows
     const int sw = (r16 >> 1) & 7;
