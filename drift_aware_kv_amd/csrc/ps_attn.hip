@@ -54,11 +54,38 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) dacc[nb] = 0.0f;
 
+    // the previous step's log-probabilities of this lane's (query, cluster)
+    // pairs are requested with the head's operands (one memory wait per head
+    // instead of two), where registers allow (up to 8 16x16 blocks of pairs
+    // per lane); addresses clamped into the tensor, values outside masked
+    // where used
+    constexpr bool kEarlyPrev = KB * NBQ <= 8;
+    const bool early = kEarlyPrev && fused && prev != nullptr && ngroups == 1;
     for (int h = wave; h < Hq; h += 4) {
         const int g = h / G;
         float M[NBQ], S[NBQ];
 #pragma unroll
         for (int nb = 0; nb < NBQ; ++nb) { M[nb] = -INFINITY; S[nb] = 0.0f; }
+        float ppre[kEarlyPrev ? NBQ : 1][kEarlyPrev ? KB : 1][4];
+        if (kEarlyPrev && early) {
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) {
+                const int i = min(16 * nb + r16, Nb - 1);
+                const float* pr = prev + (((size_t)w * Hq + h) * Nb + i) * K;
+#pragma unroll
+                for (int mb = 0; mb < KB; ++mb) {
+                    const int k0 = 16 * mb + 4 * q;
+                    if (vec) {
+                        const float4 v4 = *reinterpret_cast<const float4*>(pr + min(k0, K - 4));
+                        ppre[nb][mb][0] = v4.x; ppre[nb][mb][1] = v4.y;
+                        ppre[nb][mb][2] = v4.z; ppre[nb][mb][3] = v4.w;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) ppre[nb][mb][r] = pr[min(k0 + r, K - 1)];
+                    }
+                }
+            }
+        }
         floatx4 acc[KB][NBQ];
         for (int cg = 0; cg < K; cg += GK) {
 #pragma unroll
@@ -171,7 +198,10 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
                     }
                     if (fused && prev) {
                         float pp[4] = {0.f, 0.f, 0.f, 0.f};
-                        if (iv) {
+                        if (kEarlyPrev) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) pp[r] = ppre[kEarlyPrev ? nb : 0][kEarlyPrev ? mb : 0][r];
+                        } else if (iv) {
                             const float* pr = prev + row;
                             if (vec && k0 + 3 < K) {
                                 const float4 v = *reinterpret_cast<const float4*>(pr + k0);
