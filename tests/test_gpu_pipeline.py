@@ -348,3 +348,39 @@ def test_step_is_deterministic(P):
                                               p.idx, p.pos, p.H_hat)])
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_windows_are_independent_of_the_batch(P):
+    """A window's step outputs are bit-identical whether it runs alone or in a
+    batch with others: no kernel reads another window's data, and no result
+    depends on how many windows a launch covers."""
+    from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
+    cfg = synth.CONFIGS["llada8b-layer"].with_(W=3)
+
+    def spec_for(W):
+        return StepSpec(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K,
+                        k=cfg.k, iters=cfg.iters, bf16=True, softmax_scale=cfg.softmax_scale,
+                        block_start=cfg.block_start)
+
+    data = synth.generate(cfg)
+    steps = []
+    for t in range(3):
+        if t:
+            synth.apply_drift(cfg, data, t)
+        steps.append({k: data[k].copy() for k in ("H", "Kr", "V", "Q")} | {"conf": synth.confidences(cfg, t)})
+    names = ("C", "assign", "counts", "row_norm", "Ck", "codes", "bscale", "rscale", "D_i", "score", "idx",
+             "pos", "count", "H_hat", "K_out", "V_out", "commit_block", "commit_suffix", "suffix_flag")
+    batch = DriftPath(spec_for(3))
+    for st in steps:
+        batch.step(*[dev(st[k]) for k in ("H", "Kr", "V", "Q", "conf")])
+    torch.cuda.synchronize()
+    for w in range(3):
+        say("window", w, "alone")
+        alone = DriftPath(spec_for(1))
+        for st in steps:
+            alone.step(*[dev(st[k][w:w + 1]) for k in ("H", "Kr", "V", "Q", "conf")])
+        torch.cuda.synchronize()
+        for name in names:
+            a = host(getattr(batch, name))[w:w + 1]
+            b = host(getattr(alone, name))
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (w, name)
