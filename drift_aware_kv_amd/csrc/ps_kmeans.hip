@@ -1192,6 +1192,37 @@ void launch_assign_bf16(const ps_shape* s, const void* H, const float* C, const 
                   (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
 }
 
+// compute units of the current device (cached per device; 256 if unknown)
+int device_cus()
+{
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                       ? n : 256;
+        (void)hipGetLastError();
+    }
+    return cus[dev];
+}
+
+// The tile kernel with NB 16-token blocks per wave, or with one when the
+// launch would leave compute units idle (few windows): a quarter of the
+// tokens per workgroup and four times the workgroups.  The number of tokens
+// a wave owns does not change any score's accumulation order, so both give
+// bit-identical results.
+template <int KB, int NB>
+void launch_assign_bf16_fit(const ps_shape* s, const void* H, const float* C, const KmWs& ws, int32_t* assign,
+                            float* rn, int first, hipStream_t st)
+{
+    const int64_t tiles = (int64_t)s->W * ((s->N + 64 * NB - 1) / (64 * NB));
+    if (NB > 1 && tiles < device_cus())
+        launch_assign_bf16<KB, 1>(s, H, C, ws, assign, rn, first, st);
+    else
+        launch_assign_bf16<KB, NB>(s, H, C, ws, assign, rn, first, st);
+}
+
 }  // namespace
 
 extern "C" ps_status ps_workspace_size(const ps_shape* s, ps_dtype dtype, size_t* bytes)
@@ -1257,10 +1288,10 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
     for (int it = 0; it < iters; ++it) {
         const int first = it == 0;
         if (bf) {
-            if (KBn <= 1)      launch_assign_bf16<1, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
-            else if (KBn <= 2) launch_assign_bf16<2, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
-            else if (KBn <= 4) launch_assign_bf16<4, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
-            else if (KBn <= 8) launch_assign_bf16<8, PS_ASSIGN_NB_LARGEK>(s, H, C, L, assign, row_norm, first, stm);
+            if (KBn <= 1)      launch_assign_bf16_fit<1, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
+            else if (KBn <= 2) launch_assign_bf16_fit<2, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
+            else if (KBn <= 4) launch_assign_bf16_fit<4, PS_ASSIGN_NB_SMALLK>(s, H, C, L, assign, row_norm, first, stm);
+            else if (KBn <= 8) launch_assign_bf16_fit<8, PS_ASSIGN_NB_LARGEK>(s, H, C, L, assign, row_norm, first, stm);
             else if (first)    launch_assign_wide<true>(s, H, L, assign, row_norm, stm);
             else               launch_assign_wide<false>(s, H, L, assign, row_norm, stm);
         } else {

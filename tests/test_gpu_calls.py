@@ -162,6 +162,37 @@ def test_iteration_paths_agree(P, case):
         assert np.array_equal(a.view(np.uint8), x.view(np.uint8)), key
 
 
+@pytest.mark.parametrize("K", [64, 128])
+def test_assign_tile_width_does_not_change_results(P, K):
+    """Launches with fewer token tiles than compute units give each wave one
+    16-token block instead of several: 80 windows in one call (several
+    blocks per wave) and the same windows one at a time (one block) must give
+    bit-identical centres, assignments, counts, norms, keys and objective."""
+    rng = np.random.default_rng(K)
+    W, N, d, Hkv, dh = 80, 1024, 64, 1, 16
+    H = rnd_bf16(rng, (W, N, d))
+    Kr = rnd_bf16(rng, (W, N, Hkv, dh))
+
+    def fit(h, kr):
+        Wc = h.shape[0]
+        s = P.Shape(W=Wc, N=N, d=d, Hq=Hkv, Hkv=Hkv, dh=dh, Nb=1, K=K)
+        out = dict(C=torch.zeros(Wc, K, d, device="cuda"), a=torch.zeros(Wc, N, dtype=torch.int32, device="cuda"),
+                   cnt=torch.zeros(Wc, K, dtype=torch.int32, device="cuda"), rn=torch.zeros(Wc, N, device="cuda"),
+                   Ck=torch.zeros(Wc, K, Hkv, dh, dtype=torch.bfloat16, device="cuda"),
+                   obj=torch.zeros(Wc, dtype=torch.float64, device="cuda"))
+        P.ps_kmeans_fit(s, P.PS_BF16, dev(h), dev(kr), P.PS_INIT_STRIDED, 4, out["C"], out["a"], out["cnt"],
+                        out["rn"], out["Ck"], out["obj"], P.workspace(s, P.PS_BF16))
+        torch.cuda.synchronize()
+        return {k: host(v) for k, v in out.items()}
+
+    batch = fit(H, Kr)
+    for w in (0, 37, 79):
+        say("window", w, "alone, K =", K)
+        alone = fit(H[w:w + 1], Kr[w:w + 1])
+        for key, v in alone.items():
+            assert np.array_equal(batch[key][w:w + 1].view(np.uint8), v.view(np.uint8)), (w, key)
+
+
 def test_kmeans_chained_planted_exact(P):
     """The tiny planted case, chained end to end from FARTHEST seeding over 10
     iterations, must equal the oracle exactly."""
