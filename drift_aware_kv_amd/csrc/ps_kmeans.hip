@@ -347,10 +347,12 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
 // the tile: 4 x 8 MFMA blocks of 16x16.  Both operands are staged through
 // LDS in 64-wide d-chunks, each chunk loaded once for the eight waves
 // (double-buffered, padded 144-byte rows); per chunk a wave reads 8 KB of
-// centre and 16 KB of token fragments for 64 MFMAs, so neither LDS nor the
-// centre traffic per token limits the MFMA rate.  Each score accumulates over
-// d in the same ascending order as in the smaller kernel, so the scores, and
-// the argmax, are identical.
+// centre and 16 KB of token fragments for 64 MFMAs.  Each score accumulates
+// over d in the same ascending order as in the smaller kernel, so the
+// scores, and the argmax, are identical.  The buffer-load kernel below runs
+// the same tiles faster (no staging registers, deeper prefetch); this one
+// serves d not a multiple of 64, or a device that refuses that kernel's
+// 160 KB of LDS.
 // ---------------------------------------------------------------------------
 constexpr int kWideTok = 256;                  // tokens per workgroup
 constexpr int kWideCl = 256;                   // clusters per pass
