@@ -569,3 +569,81 @@ def test_drift_cosine(P, W, K, d):
     assert cosine_close(got, want, d), f"max diff {np.abs(got - want).max()}"
     # the unmoved centre scores 1 - ||c||^2: zero up to its fp32 normalisation
     assert abs(got[0, 0]) < 1e-6
+
+
+def test_maximum_window_length(P):
+    """The longest window the calls accept (N = 2^24 - 1 rows, ragged against
+    every tile size), with planted, well-separated clusters so that no row is
+    a near-tie: K-Means from farthest-first seeds, then the NVFP4 coder, the
+    gather of one cluster and the suffix commit rule on the oracle's own
+    clustering, each against the oracle."""
+    N, d, K = (1 << 24) - 1, 16, 3
+    rng = np.random.default_rng(24)
+    u = rng.standard_normal((K, d))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    x = (u[rng.integers(0, K, N)] + 0.05 * rng.standard_normal((N, d))).astype(np.float32)
+    xb = x.view(np.uint32)
+    H = ((xb + 0x7FFF + ((xb >> 16) & 1)) >> 16).astype(np.uint16).reshape(1, N, d)
+    del x, xb
+    Kr = H.reshape(1, N, 1, d)
+    s = P.Shape(W=1, N=N, d=d, Hq=1, Hkv=1, dh=d, Nb=32, K=K)
+    so = O.Shape(W=1, N=N, d=d, Hq=1, Hkv=1, dh=d, Nb=32, K=K)
+    say("maximum window: oracle K-Means")
+    r = O.kmeans_fit(so, O.BF16, H, Kr, O.INIT_FARTHEST, 2, np.zeros((1, K, d), np.float32))
+    Hd, Krd = dev(H), dev(Kr)
+    C = torch.zeros(1, K, d, device="cuda")
+    a = torch.zeros(1, N, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, K, dtype=torch.int32, device="cuda")
+    rn = torch.zeros(1, N, device="cuda")
+    Ck = torch.zeros(1, K, 1, d, dtype=torch.bfloat16, device="cuda")
+    obj = torch.zeros(1, dtype=torch.float64, device="cuda")
+    ws = P.workspace(s, P.PS_BF16)
+    P.ps_kmeans_fit(s, P.PS_BF16, Hd, Krd, P.PS_INIT_FARTHEST, 2, C, a, cnt, rn, Ck, obj, ws)
+    torch.cuda.synchronize()
+    assert max_rel(host(rn), r["row_norm"]) <= 1.2e-7, "row norms"
+    assert np.array_equal(host(a), r["assign"]), "assignments"
+    assert np.array_equal(host(cnt), r["counts"]), "counts"
+    assert close(host(C), r["C"], 1e-6, 1e-7), "centres"
+    assert np.array_equal(host(Ck), r["Ck"]), "centroid keys"
+
+    say("maximum window: NVFP4 coder")
+    q = O.residual_nvfp4(so, O.BF16, H, r["row_norm"], r["C"], r["assign"])
+    codes = torch.zeros(1, N, d // 2, dtype=torch.uint8, device="cuda")
+    bscale = torch.zeros(1, N, d // 16, dtype=torch.uint8, device="cuda")
+    rscale = torch.zeros(1, N, device="cuda")
+    rn_o, C_o, a_o = dev(r["row_norm"]), dev(r["C"]), dev(r["assign"])
+    P.ps_residual_nvfp4(s, P.PS_BF16, Hd, rn_o, C_o, a_o, codes, bscale, rscale, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(codes), q["codes"]), "codes"
+    assert np.array_equal(host(bscale), q["bscale"]), "block scales"
+    assert np.array_equal(host(rscale).view(np.uint32), q["rscale"].view(np.uint32)), "row scales"
+    del codes, bscale, rscale
+
+    say("maximum window: gather of one cluster")
+    idx = np.array([[1]], np.int32)
+    cap = 6_000_000                                   # above the ~N/3 members of a cluster
+    g = O.refresh_gather(so, O.BF16, r["assign"], idx, 1, cap, q["codes"], q["bscale"], q["rscale"], r["C"],
+                         r["row_norm"], True, Kr, None)
+    pos = torch.full((1, cap), -1, dtype=torch.int32, device="cuda")
+    count = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Hh = torch.zeros(1, cap, d, dtype=torch.bfloat16, device="cuda")
+    Ko = torch.zeros(1, cap, 1, d, dtype=torch.bfloat16, device="cuda")
+    P.ps_refresh_gather(s, P.PS_BF16, a_o, dev(idx), 1, cap, pos, count, dev(q["codes"]), dev(q["bscale"]),
+                        dev(q["rscale"]), C_o, rn_o, Hh, Krd, None, Ko, None)
+    torch.cuda.synchronize()
+    m = int(g["count"][0])
+    assert 0 < m <= cap and int(host(count)[0]) == m
+    assert np.array_equal(host(pos)[0, :m], g["pos"][0, :m])
+    assert np.array_equal(host(Hh)[0, :m], g["H_hat"][0, :m])
+    assert np.array_equal(host(Ko)[0, :m], g["K_out"][0, :m])
+    del pos, Hh, Ko
+
+    say("maximum window: suffix commit rule")
+    b0 = N // 2 - 16
+    conf = rng.random((1, N), dtype=np.float32)
+    cs = O.commit_suffix(so, r["assign"], idx, 1, b0, conf, 0.9)
+    flag = torch.zeros(1, dtype=torch.uint8, device="cuda")
+    commit = torch.zeros(1, N, dtype=torch.uint8, device="cuda")
+    P.ps_commit_suffix(s, a_o, dev(idx), 1, b0, dev(conf), 0.9, flag, commit)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(flag), cs["flag"]) and np.array_equal(host(commit), cs["commit"])
