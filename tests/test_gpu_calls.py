@@ -51,6 +51,8 @@ KM_CASES = [
     ("k256-llada-rows", 2, 700, 4096, 256, 8, 128, True),   # the 256-cluster tile kernel (LDS-fed)
     ("k1000-four-groups", 1, 1100, 192, 1000, 2, 32, True),  # four cluster groups, ragged
     ("k200-d80", 2, 400, 80, 200, 1, 16, True),   # d not a multiple of 32: the register-staged tile kernel
+    ("d8192", 1, 300, 8192, 70, 2, 64, True),     # the longest rows the update accepts
+    ("k200-d8192", 1, 400, 8192, 200, 2, 64, True),
 ]
 
 
@@ -118,7 +120,8 @@ ITER_CASES = [("ragged-bf16", 3, 300, 80, 37, True), ("llada-rows", 2, 1024, 409
               ("k256-llada-rows", 2, 700, 4096, 256, True),
               ("k300-two-groups-ragged", 1, 640, 192, 300, True),
               ("k150-one-chunk", 2, 300, 64, 150, True),
-              ("k200-d96", 1, 500, 96, 200, True)]   # d not a multiple of 64: register-staged passes
+              ("k200-d96", 1, 500, 96, 200, True),   # d not a multiple of 64: register-staged passes
+              ("k200-d8192", 1, 400, 8192, 200, True)]
 
 
 @pytest.mark.parametrize("case", ITER_CASES, ids=[c[0] for c in ITER_CASES])
