@@ -1,0 +1,83 @@
+"""The benchmark's accounting, on the CPU: the algorithmic bytes and flops it
+divides by the measured times (every input a kernel needs read once, every
+output written once), the recorded-traffic lookup, and the refusal of more
+than one GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+CFG = synth.CONFIGS["llada8b-batch"]
+
+
+def test_benchmark_workload_shape():
+    assert (CFG.W, CFG.N, CFG.d, CFG.K, CFG.Hq, CFG.Hkv, CFG.dh, CFG.Nb, CFG.k, CFG.iters) == \
+        (512, 1024, 4096, 64, 32, 32, 128, 32, 4, 8)
+    assert CFG.bf16
+
+
+def test_assign_pass_bytes_and_flops():
+    W, N, d, K = CFG.W, CFG.N, CFG.d, CFG.K
+    byts, flops = bench.kernel_work("k_assign_bf16<KB, NB, false>", CFG)
+    assert byts == W * N * d * 2 + W * K * d * 2 + W * N * 4 == 4_565_499_904
+    assert flops == 2 * W * N * K * d
+    # arithmetic intensity K flop/B: under the bf16 ridge, so the HBM roofline applies
+    assert flops / byts < bench.BF16_PEAK_TFLOPS * 1e12 / (bench.HBM_PEAK_GBS * 1e9)
+
+
+def test_coder_bytes():
+    W, N, d, K = CFG.W, CFG.N, CFG.d, CFG.K
+    byts, _ = bench.kernel_work("k_residual_grouped<T, BPL, FULL>", CFG)
+    # H, fp32 centres, norm + assignment + row scale, E2M1 codes, E4M3 block scales
+    assert byts == W * N * d * 2 + W * K * d * 4 + 3 * W * N * 4 + W * N * d // 2 + W * N * d // 16
+    # the exact-path kernel codes a handful of listed rows: no full-pass figure
+    assert bench.kernel_work("k_residual_listed<T, CPL>", CFG) is None
+
+
+def test_proxy_counts_the_previous_distribution():
+    L = CFG.W * CFG.Hq * CFG.Nb * CFG.K
+    byts, flops = bench.kernel_work("k_proxy_bf16<KB, NBQ>", CFG)
+    q = CFG.W * CFG.Nb * CFG.Hq * CFG.dh * 2
+    ck = CFG.W * CFG.K * CFG.Hkv * CFG.dh * 2
+    assert byts == q + ck + 2 * L * 4
+    assert flops == 2.0 * CFG.W * CFG.Hq * CFG.Nb * CFG.K * CFG.dh
+
+
+def test_gather_scales_with_the_rows_selected():
+    assert bench.kernel_work("k_gather_rows<uint16_t>", CFG) is None     # rows unknown
+    a, _ = bench.kernel_work("k_gather_rows<uint16_t>", CFG, 50.0)
+    b, _ = bench.kernel_work("k_gather_rows<uint16_t>", CFG, 100.0)
+    per_row = (b - a) / (50.0 * CFG.W)
+    KV = CFG.Hkv * CFG.dh
+    assert per_row == CFG.d // 2 + CFG.d // 16 + 16 + CFG.d * 2 + 4 * KV * 2
+
+
+def test_recorded_traffic_is_tied_to_the_sources():
+    name, wl = "k_assign_bf16<KB, NB, false>", CFG.name
+    got = bench.recorded_traffic(name, wl)
+    if got is not None:       # the committed counters match the committed kernel sources
+        assert 0.99 < got / bench.kernel_work(name, CFG)[0] < 1.05
+    assert bench.recorded_traffic(name, "another-workload") is None
+    assert bench.recorded_traffic("k_keys<uint16_t>", wl) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    msg = json.loads(p.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+@pytest.mark.parametrize("name", bench.CONFIG_NAMES)
+def test_every_named_workload_exists(name):
+    assert name in synth.CONFIGS
