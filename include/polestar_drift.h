@@ -125,6 +125,7 @@ ps_status ps_workspace_size(const ps_shape* shape, ps_dtype dtype, size_t* bytes
  * is the last update, so each c_k is the normalised mean of its members.
  * Clusters whose member set did not change since the previous iteration keep
  * their centre without being re-summed (the sum would be bit-identical).
+ * Also requires d <= 8192 (PS_ERR_SHAPE above).
  */
 ps_status ps_kmeans_fit(const ps_shape* shape, ps_dtype dtype, const void* H, const void* Kr,
                         ps_init init, int32_t iters, uint32_t flags, float* C, int32_t* assign,
@@ -156,6 +157,8 @@ ps_status ps_kmeans_fit(const ps_shape* shape, ps_dtype dtype, const void* H, co
  *                                    member rows; results are identical
  *                                    either way.  A smaller non-NULL ws:
  *                                    PS_ERR_WORKSPACE.
+ *
+ * Also requires d <= 8192 (PS_ERR_SHAPE above).
  */
 ps_status ps_residual_nvfp4(const ps_shape* shape, ps_dtype dtype, const void* H,
                             const float* row_norm, const float* C, const int32_t* assign,
@@ -175,6 +178,8 @@ ps_status ps_residual_nvfp4(const ps_shape* shape, ps_dtype dtype, const void* H
  *   logp_cur  [W][Hq][Nb][K] f32  out
  *   logp_prev [W][Hq][Nb][K] f32  in   (nullable; must not alias logp_cur)
  *   D_hi [W][Hq][Nb] f32 out (nullable), D_i [W][Nb] f32 out, score [W][K] f32 out
+ *
+ * Also requires Nb <= 64 and Hq * Nb + 4 * K <= 16384 (PS_ERR_SHAPE above).
  */
 ps_status ps_proxy_attn(const ps_shape* shape, ps_dtype dtype, const void* Q, const void* Ck,
                         float softmax_scale, float* logp_cur, const float* logp_prev,
@@ -188,6 +193,8 @@ ps_status ps_proxy_attn(const ps_shape* shape, ps_dtype dtype, const void* Q, co
  *
  *   logp_cur, logp_prev [W][Hq][Nb][K] f32 in
  *   D_hi [W][Hq][Nb] f32 out (nullable), D_i [W][Nb] f32 out, score [W][K] f32 out
+ *
+ * Also requires Hq * Nb + 4 * K <= 16384 (PS_ERR_SHAPE above).
  */
 ps_status ps_drift_kl(const ps_shape* shape, const float* logp_cur, const float* logp_prev,
                       ps_score score_kind, float* D_hi, float* D_i, float* score, void* stream);

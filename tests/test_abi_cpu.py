@@ -95,6 +95,7 @@ def test_kmeans_fit_argument_checks(L):
     assert _fit(L, s, Kr=FAKE, Ck=None) == NULL           # Kr and Ck come together
     assert _fit(L, s, dtype=3) == DTYPE
     assert _fit(L, _shape(d=24)) == SHAPE                   # d % 16
+    assert _fit(L, _shape(d=8208)) == SHAPE                 # d > 8192
     assert _fit(L, _shape(K=65)) == SHAPE                   # K > N
     assert _fit(L, _shape(K=0)) == SHAPE
     assert _fit(L, _shape(Hq=3, Hkv=2), Kr=FAKE, Ck=FAKE) == SHAPE   # Hq % Hkv
@@ -116,6 +117,7 @@ def test_residual_argument_checks(L):
     assert f(H=None) == NULL
     assert f(dt=5) == DTYPE
     assert f(s=_shape(d=8)) == SHAPE
+    assert f(s=_shape(d=8208)) == SHAPE                      # d > 8192
     assert f(H=MISALIGNED) == ALIGN
     assert f(ws=MISALIGNED, wsb=1 << 20) == ALIGN
     assert f(ws=FAKE, wsb=8 * 2 * 64 + 15) == WORKSPACE    # needs 8 * W * N + 16 bytes
@@ -132,6 +134,7 @@ def test_proxy_and_drift_argument_checks(L):
     assert f(prev=FAKE, cur=FAKE) == RANGE                 # logp_prev aliases logp_cur
     assert f(s=_shape(Hq=3)) == SHAPE
     assert f(s=_shape(Nb=65)) == SHAPE
+    assert f(s=_shape(Hq=256, Hkv=256, Nb=64)) == SHAPE       # Hq * Nb + 4 K > 16384
     assert f(s=_shape(W=0), prev=None) == OK
     g = lambda s=s, kind=0: L.ps_drift_kl(ctypes.byref(s), FAKE, ctypes.c_void_p(0x20000), kind, None,
                                           FAKE, FAKE, None)
