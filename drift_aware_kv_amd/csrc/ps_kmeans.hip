@@ -165,11 +165,14 @@ __global__ __launch_bounds__(256) void k_centres_to_bf16(const float* __restrict
 // reads); each wave streams its token rows straight into registers one chunk
 // ahead (NB*2 16-byte loads per lane per chunk, each load covering 16 rows x
 // 64 contiguous bytes).  FIRST: the first iteration of a call, which also
-// writes the fp64 row norms and marks nothing; later iterations mark the old
-// and new cluster of every row that moves and skip windows at a fixed point.
+// writes the fp64 row norms and marks nothing, and takes the caller's fp32
+// centres as `Cop`, rounding each staged piece to bf16 on its way to LDS (the
+// same rounding as the stored copy, which the first update then writes for
+// every cluster); later iterations take that bf16 copy, mark the old and new
+// cluster of every row that moves and skip windows at a fixed point.
 template <int KB, int NB, bool FIRST>
 __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict__ H,
-                                                      const uint16_t* __restrict__ Cb,
+                                                      const void* __restrict__ Cop,
                                                       int32_t* __restrict__ assign,
                                                       float* __restrict__ row_norm, int N, int d,
                                                       int K, int tiles, int nblocks,
@@ -191,7 +194,8 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const uint16_t* Hw = H + (size_t)w * N * d;
-    const uint16_t* Cw = Cb + (size_t)w * K * d;
+    const uint16_t* Cw = reinterpret_cast<const uint16_t*>(Cop) + (size_t)w * K * d;    // later passes
+    const float* Cf = reinterpret_cast<const float*>(Cop) + (size_t)w * K * d;          // first pass
 
     int tok[NB];
     bool tv[NB];
@@ -223,14 +227,20 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
         // before a chunk's MFMAs covers that chunk's loads only, not the next
         // chunk's, which stay in flight.
         uint4 cpre[PIECES];
+        float4 cpre32[FIRST ? PIECES : 1][2];
         uint4 hcur[NB][NS], hnext[NB][NS];
         auto load_c = [&](int c0) {
 #pragma unroll
             for (int p = 0; p < PIECES; ++p) {
                 const int piece = min(p * 256 + (int)threadIdx.x, NPIECE - 1);
                 const int row = piece / (DK / 8), col = (piece % (DK / 8)) * 8;
-                cpre[p] = *reinterpret_cast<const uint4*>(Cw + (size_t)min(cg + row, K - 1) * d +
-                                                          min(c0 + col, d - 8));
+                const size_t off = (size_t)min(cg + row, K - 1) * d + min(c0 + col, d - 8);
+                if (FIRST) {
+                    cpre32[FIRST ? p : 0][0] = *reinterpret_cast<const float4*>(Cf + off);
+                    cpre32[FIRST ? p : 0][1] = *reinterpret_cast<const float4*>(Cf + off + 4);
+                } else {
+                    cpre[p] = *reinterpret_cast<const uint4*>(Cw + off);
+                }
             }
         };
         auto store_c = [&](int buf, int c0) {
@@ -239,6 +249,13 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
                 const int piece = p * 256 + threadIdx.x;
                 const int row = piece / (DK / 8), col = (piece % (DK / 8)) * 8;
                 const bool ok = cg + row < K && c0 + col < d;
+                if (FIRST) {
+                    const float4 a = cpre32[FIRST ? p : 0][0], b = cpre32[FIRST ? p : 0][1];
+                    cpre[p] = make_uint4(f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16),
+                                         f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16),
+                                         f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16),
+                                         f32_to_bf16(b.z) | (f32_to_bf16(b.w) << 16));
+                }
                 if (piece < NPIECE)
                     *reinterpret_cast<uint4*>(&lds[buf][row * ROWB + col * 2]) = ok ? cpre[p] : make_uint4(0, 0, 0, 0);
             }
@@ -1046,6 +1063,19 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
                 if (Cb) store8(Cb + ((size_t)w * K + k) * d + e, v);
             }
         }
+    } else if (all && Cb) {
+        // a kept centre: its bf16 copy for the later passes (the first pass
+        // read the fp32 centres directly)
+        const float* c_in = C + ((size_t)w * K + k) * d;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int e = (threadIdx.x + 256 * c) * 8;
+            if (e < d) {
+                float v[8];
+                load8(c_in + e, v);
+                store8(Cb + ((size_t)w * K + k) * d + e, v);
+            }
+        }
     }
 }
 
@@ -1188,7 +1218,8 @@ void launch_assign_bf16(const ps_shape* s, const void* H, const float* C, const 
     const int nblocks = s->W * tiles;
     if (first)
         PS_LAUNCH("k_assign_bf16<KB, NB, true>", (k_assign_bf16<KB, NB, true>), dim3(nblocks), dim3(256), 0, st,
-                  (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
+                  (const uint16_t*)H, (const void*)C, assign, rn, s->N, s->d, s->K, tiles, nblocks, ws.dirty,
+                  ws.conv);
     else
         PS_LAUNCH("k_assign_bf16<KB, NB, false>", (k_assign_bf16<KB, NB, false>), dim3(nblocks), dim3(256), 0, st,
                   (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
@@ -1276,7 +1307,9 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
         if (bf) PS_LAUNCH("k_init_farthest<uint16_t>", k_init_farthest<uint16_t>, dim3(W), dim3(256), shm, stm, (const uint16_t*)H, C, L.fm, L.fn, N, d, K);
         else    PS_LAUNCH("k_init_farthest<float>", k_init_farthest<float>, dim3(W), dim3(256), shm, stm, (const float*)H, C, L.fm, L.fn, N, d, K);
     }
-    if (bf) {
+    if (bf && K > 128) {
+        // the tile kernels above 128 clusters read the bf16 copy from the
+        // first pass on; below, the first pass rounds the fp32 centres itself
         const size_t n8 = (size_t)W * K * d / 8;
         const int blocks = (int)std::min<size_t>((n8 + 255) / 256, 8192);
         PS_LAUNCH("k_centres_to_bf16", k_centres_to_bf16, dim3(blocks), dim3(256), 0, stm, C, L.Cb, n8);
