@@ -43,7 +43,9 @@ def kernel_work(name, cfg, gathered=None):
     KV = cfg.Hkv * cfg.dh
     L = W * cfg.Hq * cfg.Nb * K
     if name.startswith("k_assign"):
-        return W * N * d * e + W * K * d * e + W * N * 4, 2.0 * W * N * K * d
+        # the first pass of a call below 129 clusters reads the fp32 centres
+        ce = 4 if (name.startswith("k_assign_bf16") and name.endswith("true>")) else e
+        return W * N * d * e + W * K * d * ce + W * N * 4, 2.0 * W * N * K * d
     if name.startswith("k_update"):
         return W * N * d * e + 2 * W * N * 4 + W * K * d * (4 + e) + W * (K + 1) * 4, W * N * d * 2.0
     if name.startswith("k_residual_grouped") or name.startswith("k_residual<"):

@@ -32,6 +32,9 @@ def test_assign_pass_bytes_and_flops():
     assert flops == 2 * W * N * K * d
     # arithmetic intensity K flop/B: under the bf16 ridge, so the HBM roofline applies
     assert flops / byts < bench.BF16_PEAK_TFLOPS * 1e12 / (bench.HBM_PEAK_GBS * 1e9)
+    # the first pass reads the fp32 centres
+    first, _ = bench.kernel_work("k_assign_bf16<KB, NB, true>", CFG)
+    assert first == byts + W * K * d * 2
 
 
 def test_coder_bytes():
