@@ -8,6 +8,15 @@ using namespace ps;
 
 namespace {
 
+// e^x and ln x on the hardware's base-2 exponential and logarithm
+// (v_exp_f32, v_log_f32, about one ulp each) after one fp32 scaling: the
+// math library's expf and logf add range reduction and special-case selects,
+// about a dozen VALU instructions a call, which made the softmax and KL
+// epilogue the larger half of proxy attention's instruction stream.
+// exp_hw(-inf) = 0; results below 2^-126 may flush to zero.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float log_hw(float x) { return __builtin_amdgcn_logf(x) * 0.693147180559945309f; }
+
 // Per-cluster score term for one (head, query, cluster): the additive KL
 // share p (l - l'), its magnitude, or the attention-weighted drift p * D.
 __device__ __forceinline__ float score_term(int kind, float p, float t, float D)
@@ -153,12 +162,12 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int kk = cg + 16 * mb + 4 * q + r;
-                        if (kk < K) se += expf(acc[mb][nb][r] - zmax);
+                        if (kk < K) se += exp_hw(acc[mb][nb][r] - zmax);
                     }
                 se += __shfl_xor(se, 16, 64);
                 se += __shfl_xor(se, 32, 64);
                 const float Mn = fmaxf(M[nb], zmax);
-                S[nb] = S[nb] * expf(M[nb] - Mn) + se * expf(zmax - Mn);
+                S[nb] = S[nb] * exp_hw(M[nb] - Mn) + se * exp_hw(zmax - Mn);
                 M[nb] = Mn;
                 if (ngroups > 1 && i < Nb) {
                     float* out = logp + (((size_t)w * Hq + h) * Nb + i) * K;
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
         for (int nb = 0; nb < NBQ; ++nb) {
             const int i = 16 * nb + r16;
             const bool iv = i < Nb;
-            const float lse = M[nb] + logf(S[nb]);
+            const float lse = M[nb] + log_hw(S[nb]);
             const size_t row = (((size_t)w * Hq + h) * Nb + (iv ? i : 0)) * K;
             float* out = logp + row;
             if (ngroups == 1) {
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const bool ok = iv && k0 + r < K;
-                            pv[mb][r] = ok ? expf(lv[mb][r]) : 0.0f;
+                            pv[mb][r] = ok ? exp_hw(lv[mb][r]) : 0.0f;
                             tv[mb][r] = ok ? pv[mb][r] * (lv[mb][r] - pp[r]) : 0.0f;
                             tsum += tv[mb][r];
                         }
@@ -293,8 +302,8 @@ __global__ __launch_bounds__(256) void k_proxy_f32(const float* __restrict__ Q, 
     float zmax = -INFINITY;
     for (int k = 0; k < K; ++k) zmax = fmaxf(zmax, zk(k));
     float se = 0.0f;
-    for (int k = 0; k < K; ++k) se += expf(zk(k) - zmax);
-    const float lse = zmax + logf(se);
+    for (int k = 0; k < K; ++k) se += exp_hw(zk(k) - zmax);
+    const float lse = zmax + log_hw(se);
     float* out = logp + (((size_t)w * Hq + h) * Nb + i) * K;
     for (int k = 0; k < K; ++k) out[k] = zk(k) - lse;
 }
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(256) void k_drift_kl(const float* __restrict__ cur,
             pv[m] = tv[m] = 0.0f;
             if (k < K) {
                 const float l = lc[k];
-                pv[m] = expf(l);
+                pv[m] = exp_hw(l);
                 tv[m] = pv[m] * (l - lp[k]);
             }
             part += tv[m];
