@@ -282,6 +282,434 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
         D_i[(size_t)w * Nb + i] = (((dred[0][i] + dred[1][i]) + dred[2][i]) + dred[3][i]) * invH;
 }
 
+// ---------------------------------------------------------------------------
+// proxy attention, bf16, with the drift fused, software-pipelined over heads.
+// For one cluster group (K <= 16*KB), dh <= 128 and a previous step, the
+// same per-lane arithmetic as k_proxy_bf16 in the same order (identical
+// results), but a wave requests its next head's operands and previous
+// log-probabilities before it computes the current head, so every wave keeps
+// one head's loads (about 32 KB) in flight while its MFMAs and softmax/KL
+// epilogue run; in k_proxy_bf16 all waves load, wait, then compute together
+// and the memory system idles during the epilogue.  Two heads' operands need
+// about 256 registers, so the kernel runs one wave per SIMD.
+// ---------------------------------------------------------------------------
+template <int KB, int NBQ>
+struct ProxyHeadOps {
+    uint4 q[4][NBQ];       // Q rows 16*nb + (lane % 16), dh pieces 32*u + 8*(lane / 16)
+    uint4 c[4][KB];        // centroid-key rows 16*mb + (lane % 16), same pieces
+    float p[NBQ][KB][4];   // previous log-probabilities of the lane's (query, cluster) pairs
+};
+
+// Requests head h's operands (K a multiple of 4: whole float4s of the previous
+// log-probabilities); every address clamped into its tensor, pieces and
+// pairs outside the shape masked where they are used.
+template <int KB, int NBQ>
+__device__ __forceinline__ void proxy_head_load(ProxyHeadOps<KB, NBQ>& o, const uint16_t* __restrict__ Q,
+                                                const uint16_t* __restrict__ Ck, const float* __restrict__ prev,
+                                                int w, int h, int g, int q, int r16, int Hq, int Hkv, int dh,
+                                                int Nb, int K)
+{
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = min(32 * u + 8 * q, dh - 8);
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) {
+            const int i = min(16 * nb + r16, Nb - 1);
+            o.q[u][nb] = *reinterpret_cast<const uint4*>(Q + (((size_t)w * Nb + i) * Hq + h) * dh + e);
+        }
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb) {
+            const int kk = min(16 * mb + r16, K - 1);
+            o.c[u][mb] = *reinterpret_cast<const uint4*>(Ck + (((size_t)w * K + kk) * Hkv + g) * dh + e);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) {
+        const int i = min(16 * nb + r16, Nb - 1);
+        const float* pr = prev + (((size_t)w * Hq + h) * Nb + i) * K;
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb) {
+            const float4 v4 = *reinterpret_cast<const float4*>(pr + min(16 * mb + 4 * q, K - 4));
+            o.p[nb][mb][0] = v4.x; o.p[nb][mb][1] = v4.y;
+            o.p[nb][mb][2] = v4.z; o.p[nb][mb][3] = v4.w;
+        }
+    }
+}
+
+// One head from loaded operands: scores on MFMA, log-softmax over the K
+// clusters, log-probabilities stored, D_{h,i} and the per-lane score terms.
+template <int KB, int NBQ>
+__device__ __forceinline__ void proxy_head_compute(const ProxyHeadOps<KB, NBQ>& o, float sigma,
+                                                   float* __restrict__ logp, int kind, float* __restrict__ D_hi,
+                                                   float (&sacc)[KB][4], float (&dacc)[NBQ], int w, int h,
+                                                   int q, int r16, int Hq, int dh, int Nb, int K)
+{
+    floatx4 acc[KB][NBQ];
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (32 * u >= dh) break;
+        const bool in_e = 32 * u + 8 * q < dh;
+        bf16x8 b[NBQ];
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb)
+            b[nb] = __builtin_bit_cast(bf16x8, (in_e && 16 * nb + r16 < Nb) ? o.q[u][nb] : make_uint4(0, 0, 0, 0));
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb) {
+            const bf16x8 a =
+                __builtin_bit_cast(bf16x8, (in_e && 16 * mb + r16 < K) ? o.c[u][mb] : make_uint4(0, 0, 0, 0));
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nb], acc[mb][nb], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) {
+        const int i = 16 * nb + r16;
+        const bool iv = i < Nb;
+        // the log-sum-exp exactly as k_proxy_bf16 forms it for one group
+        float zmax = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float z = acc[mb][nb][r] * sigma;
+                acc[mb][nb][r] = z;
+                if (16 * mb + 4 * q + r < K) zmax = fmaxf(zmax, z);
+            }
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+        float se = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (16 * mb + 4 * q + r < K) se += exp_hw(acc[mb][nb][r] - zmax);
+        se += __shfl_xor(se, 16, 64);
+        se += __shfl_xor(se, 32, 64);
+        const float lse = zmax + log_hw(se);
+        float* out = logp + (((size_t)w * Hq + h) * Nb + (iv ? i : 0)) * K;
+        float pv[KB][4], tv[KB][4];
+        float tsum = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb) {
+            const int k0 = 16 * mb + 4 * q;
+            float lv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lv[r] = acc[mb][nb][r] - lse;
+            if (iv) {
+                if (k0 < K) *reinterpret_cast<float4*>(out + k0) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = iv && k0 + r < K;
+                pv[mb][r] = ok ? exp_hw(lv[r]) : 0.0f;
+                tv[mb][r] = ok ? pv[mb][r] * (lv[r] - o.p[nb][mb][r]) : 0.0f;
+                tsum += tv[mb][r];
+            }
+        }
+        float D = tsum + __shfl_xor(tsum, 16, 64);
+        D = D + __shfl_xor(D, 32, 64);
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[mb][r] += score_term(kind, pv[mb][r], tv[mb][r], D);
+        if (iv) {
+            dacc[nb] += D;
+            if (D_hi && q == 0) D_hi[((size_t)w * Hq + h) * Nb + i] = D;
+        }
+    }
+}
+
+template <int KB, int NBQ>
+__global__ __launch_bounds__(256, 1) void k_proxy_pipe(const uint16_t* __restrict__ Q,
+                                                        const uint16_t* __restrict__ Ck, float sigma,
+                                                        float* __restrict__ logp, const float* __restrict__ prev,
+                                                        int kind, float* __restrict__ D_hi, float* __restrict__ D_i,
+                                                        float* __restrict__ score, int Hq, int Hkv, int dh, int Nb,
+                                                        int K)
+{
+    __shared__ float sred[4][16 * KB];
+    __shared__ float dred[4][16 * NBQ];
+    const int w = blockIdx.x;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int G = Hq / Hkv;
+    float sacc[KB][4];
+    float dacc[NBQ];
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[mb][r] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) dacc[nb] = 0.0f;
+    // the wave's heads are wave, wave + 4, ...; loads past the last head are
+    // clamped to it (issued so that every trip requests the same loads) and
+    // never used
+    ProxyHeadOps<KB, NBQ> A, B;
+    int hl = min(wave, Hq - 1);
+    proxy_head_load(A, Q, Ck, prev, w, hl, hl / G, q, r16, Hq, Hkv, dh, Nb, K);
+    for (int h = wave; h < Hq; h += 8) {
+        hl = min(h + 4, Hq - 1);
+        proxy_head_load(B, Q, Ck, prev, w, hl, hl / G, q, r16, Hq, Hkv, dh, Nb, K);
+        proxy_head_compute(A, sigma, logp, kind, D_hi, sacc, dacc, w, h, q, r16, Hq, dh, Nb, K);
+        if (h + 4 >= Hq) break;
+        hl = min(h + 8, Hq - 1);
+        proxy_head_load(A, Q, Ck, prev, w, hl, hl / G, q, r16, Hq, Hkv, dh, Nb, K);
+        proxy_head_compute(B, sigma, logp, kind, D_hi, sacc, dacc, w, h + 4, q, r16, Hq, dh, Nb, K);
+    }
+    // scores: sum over the 16 query lanes, then over the four waves in order
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = sacc[mb][r];
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            v += __shfl_xor(v, 4, 64);
+            v += __shfl_xor(v, 8, 64);
+            if (r16 == 0) sred[wave][16 * mb + 4 * q + r] = v;
+        }
+    if (q == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) dred[wave][16 * nb + r16] = dacc[nb];
+    }
+    __syncthreads();
+    const float invH = 1.0f / (float)Hq;
+    for (int k = threadIdx.x; k < K; k += 256)
+        score[(size_t)w * K + k] = (((sred[0][k] + sred[1][k]) + sred[2][k]) + sred[3][k]) * invH;
+    for (int i = threadIdx.x; i < Nb; i += 256)
+        D_i[(size_t)w * Nb + i] = (((dred[0][i] + dred[1][i]) + dred[2][i]) + dred[3][i]) * invH;
+}
+
+// ---------------------------------------------------------------------------
+// proxy attention, bf16, drift fused, for K = 64 clusters and dh = 128 (every
+// operand row 256 bytes), whole rows per load.  The MFMA fragment layout
+// makes each load instruction of k_proxy_pipe read 16 rows x 64 bytes, half
+// of every 128-byte line it touches, which measured at about two thirds of
+// the per-CU load rate of whole lines.  Here a load instruction reads 4 rows
+// x 256 bytes (lane l: row 4 j + l / 16, 16-byte piece l % 16) into
+// registers, one head ahead as in k_proxy_pipe; the wave stores the pieces
+// into its own LDS tiles (Q, centroid keys, previous log-probabilities),
+// piece p of row r at slot p ^ (r % 16), and reads the MFMA fragments and the
+// epilogue's previous values back from there: the sixteen rows one fragment
+// read touches fall on sixteen distinct 16-byte slots, so no bank conflicts.
+// Two waves per workgroup (32 KB of LDS each); a wave's heads are wave,
+// wave + 2, ...; results bit-identical to k_proxy_bf16's.
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int NBQ>
+struct ProxyRowOps {
+    u32x4 q[4 * NBQ];   // Q rows 4 j + lane / 16, piece lane % 16
+    u32x4 c[16];        // centroid-key rows 4 j + lane / 16
+    u32x4 p[4 * NBQ];   // previous log-probability rows 4 j + lane / 16 (four floats a piece)
+};
+
+constexpr int kRowTileQ = 0;            // byte offsets in a wave's 32 KB of LDS
+constexpr int kRowTileC = 32 * 256;
+constexpr int kRowTileP = 96 * 256;
+constexpr int kRowTileBytes = 128 * 256;
+
+template <int NBQ>
+__device__ __forceinline__ void proxy_rows_load(ProxyRowOps<NBQ>& o, const uint16_t* __restrict__ Q,
+                                                const uint16_t* __restrict__ Ck, const float* __restrict__ prev,
+                                                int w, int h, int g, int lane, int Hq, int Hkv, int Nb)
+{
+    const int rr = lane >> 4, pc = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 4 * NBQ; ++j) {
+        const int i = min(4 * j + rr, Nb - 1);
+        o.q[j] = *reinterpret_cast<const u32x4*>(Q + (((size_t)w * Nb + i) * Hq + h) * 128 + 8 * pc);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int k = 4 * j + rr;
+        o.c[j] = *reinterpret_cast<const u32x4*>(Ck + (((size_t)w * 64 + k) * Hkv + g) * 128 + 8 * pc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4 * NBQ; ++j) {
+        const int i = min(4 * j + rr, Nb - 1);
+        o.p[j] = *reinterpret_cast<const u32x4*>(prev + (((size_t)w * Hq + h) * Nb + i) * 64 + 4 * pc);
+    }
+}
+
+template <int NBQ>
+__device__ __forceinline__ void proxy_rows_compute(const ProxyRowOps<NBQ>& o, uint8_t* __restrict__ tile,
+                                                   float sigma, float* __restrict__ logp, int kind,
+                                                   float* __restrict__ D_hi, float (&sacc)[4][4],
+                                                   float (&dacc)[NBQ], int w, int h, int lane, int Hq, int Nb)
+{
+    const int rr = lane >> 4, pc = lane & 15;
+    const int q = lane >> 4, r16 = lane & 15;
+    // whole rows into the wave's tiles: row r = 4 j + rr has r % 16 = 4 (j % 4) + rr
+#pragma unroll
+    for (int j = 0; j < 4 * NBQ; ++j) {
+        const int off = (4 * j + rr) * 256 + 16 * (pc ^ (4 * (j & 3) + rr));
+        *reinterpret_cast<u32x4*>(tile + kRowTileQ + off) = o.q[j];
+        *reinterpret_cast<u32x4*>(tile + kRowTileP + off) = o.p[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        *reinterpret_cast<u32x4*>(tile + kRowTileC + (4 * j + rr) * 256 + 16 * (pc ^ (4 * (j & 3) + rr))) = o.c[j];
+    floatx4 acc[4][NBQ];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // fragment reads: row 16 x + r16, piece 4 u + q at slot (4 u + q) ^ r16
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int so = 16 * ((4 * u + q) ^ r16);
+        bf16x8 b[NBQ];
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) {
+            const uint4 v = *reinterpret_cast<const uint4*>(tile + kRowTileQ + (16 * nb + r16) * 256 + so);
+            b[nb] = __builtin_bit_cast(bf16x8, 16 * nb + r16 < Nb ? v : make_uint4(0, 0, 0, 0));
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const bf16x8 a =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tile + kRowTileC + (16 * mb + r16) * 256 + so));
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nb], acc[mb][nb], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) {
+        const int i = 16 * nb + r16;
+        const bool iv = i < Nb;
+        float zmax = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float z = acc[mb][nb][r] * sigma;
+                acc[mb][nb][r] = z;
+                zmax = fmaxf(zmax, z);
+            }
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+        float se = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) se += exp_hw(acc[mb][nb][r] - zmax);
+        se += __shfl_xor(se, 16, 64);
+        se += __shfl_xor(se, 32, 64);
+        const float lse = zmax + log_hw(se);
+        float* out = logp + (((size_t)w * Hq + h) * Nb + (iv ? i : 0)) * 64;
+        float pv[4][4], tv[4][4];
+        float tsum = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int k0 = 16 * mb + 4 * q;
+            const float4 pp = *reinterpret_cast<const float4*>(tile + kRowTileP + i * 256 + 16 * ((4 * mb + q) ^ r16));
+            const float ppv[4] = {pp.x, pp.y, pp.z, pp.w};
+            float lv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lv[r] = acc[mb][nb][r] - lse;
+            if (iv) *reinterpret_cast<float4*>(out + k0) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pv[mb][r] = iv ? exp_hw(lv[r]) : 0.0f;
+                tv[mb][r] = iv ? pv[mb][r] * (lv[r] - ppv[r]) : 0.0f;
+                tsum += tv[mb][r];
+            }
+        }
+        float D = tsum + __shfl_xor(tsum, 16, 64);
+        D = D + __shfl_xor(D, 32, 64);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[mb][r] += score_term(kind, pv[mb][r], tv[mb][r], D);
+        if (iv) {
+            dacc[nb] += D;
+            if (D_hi && q == 0) D_hi[((size_t)w * Hq + h) * Nb + i] = D;
+        }
+    }
+}
+
+template <int NBQ>
+__global__ __launch_bounds__(128, 1) void k_proxy_rows(const uint16_t* __restrict__ Q,
+                                                        const uint16_t* __restrict__ Ck, float sigma,
+                                                        float* __restrict__ logp, const float* __restrict__ prev,
+                                                        int kind, float* __restrict__ D_hi, float* __restrict__ D_i,
+                                                        float* __restrict__ score, int Hq, int Hkv, int Nb)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kRowTileBytes];
+    const int w = blockIdx.x;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int G = Hq / Hkv;
+    uint8_t* const tile = tiles[wave];
+    // per-lane partial sums in four streams, heads h % 4 = 0..3 (this wave
+    // keeps streams wave and wave + 2), combined in stream order at the end:
+    // the same additions in the same order as the four-wave kernels, so a
+    // window's results do not depend on which kernel the launch size picks
+    float sacc[2][4][4];
+    float dacc[2][NBQ];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[t][mb][r] = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) dacc[t][nb] = 0.0f;
+    }
+    // loads past the wave's last head are clamped to it and never used
+    ProxyRowOps<NBQ> A, B;
+    int hl = min(wave, Hq - 1);
+    proxy_rows_load(A, Q, Ck, prev, w, hl, hl / G, lane, Hq, Hkv, Nb);
+    for (int h = wave; h < Hq; h += 4) {
+        hl = min(h + 2, Hq - 1);
+        proxy_rows_load(B, Q, Ck, prev, w, hl, hl / G, lane, Hq, Hkv, Nb);
+        proxy_rows_compute(A, tile, sigma, logp, kind, D_hi, sacc[0], dacc[0], w, h, lane, Hq, Nb);
+        if (h + 2 >= Hq) break;
+        hl = min(h + 4, Hq - 1);
+        proxy_rows_load(A, Q, Ck, prev, w, hl, hl / G, lane, Hq, Hkv, Nb);
+        proxy_rows_compute(B, tile, sigma, logp, kind, D_hi, sacc[1], dacc[1], w, h + 2, lane, Hq, Nb);
+    }
+    // scores: sum over the 16 query lanes, then over the four streams in
+    // order; a wave's partials go to the start of its own tile, which it no
+    // longer reads: [stream wave: 64 scores, 32 drifts][stream wave + 2: ...]
+    float* const red = reinterpret_cast<float*>(tile);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = sacc[t][mb][r];
+                v += __shfl_xor(v, 1, 64);
+                v += __shfl_xor(v, 2, 64);
+                v += __shfl_xor(v, 4, 64);
+                v += __shfl_xor(v, 8, 64);
+                if (r16 == 0) red[96 * t + 16 * mb + 4 * q + r] = v;
+            }
+        if (q == 0) {
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) red[96 * t + 64 + 16 * nb + r16] = dacc[t][nb];
+        }
+    }
+    __syncthreads();
+    // stream v is wave v % 2's partial set v / 2
+    const float* s0 = reinterpret_cast<const float*>(tiles[0]);
+    const float* s1 = reinterpret_cast<const float*>(tiles[1]);
+    const float* s2 = s0 + 96;
+    const float* s3 = s1 + 96;
+    const float invH = 1.0f / (float)Hq;
+    for (int k = threadIdx.x; k < 64; k += 128)
+        score[(size_t)w * 64 + k] = (((s0[k] + s1[k]) + s2[k]) + s3[k]) * invH;
+    for (int i = threadIdx.x; i < Nb; i += 128)
+        D_i[(size_t)w * Nb + i] = (((s0[64 + i] + s1[64 + i]) + s2[64 + i]) + s3[64 + i]) * invH;
+}
+
 // proxy attention, fp32 path: one thread per (h, i), three passes over K
 __global__ __launch_bounds__(256) void k_proxy_f32(const float* __restrict__ Q, const float* __restrict__ Ck,
                                                     float sigma, float* __restrict__ logp, int Hq, int Hkv,
@@ -491,10 +919,44 @@ __global__ __launch_bounds__(64) void k_topk(const float* __restrict__ score, in
     }
 }
 
+// compute units of the current device (cached per device; 256 if unknown)
+int attn_device_cus()
+{
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                       ? n : 256;
+        (void)hipGetLastError();
+    }
+    return cus[dev];
+}
+
+// Drift-step proxy attention (a previous step given) takes the whole-row
+// kernel at K = 64, dh = 128 when its two waves per window give every SIMD
+// a wave (four per compute unit); with fewer windows, or other shapes whose
+// operands fit, the four-wave pipelined kernel; otherwise k_proxy_bf16.
 template <int KB, int NBQ>
 void launch_proxy(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, const float* prev,
                   int kind, int fused, float* D_hi, float* D_i, float* score, hipStream_t st)
 {
+    if constexpr (KB == 4 && NBQ <= 2) {
+        if (fused && prev && s->dh == 128 && s->K == 64 && 2 * (int64_t)s->W >= 4 * (int64_t)attn_device_cus()) {
+            PS_LAUNCH("k_proxy_rows<NBQ>", k_proxy_rows<NBQ>, dim3(s->W), dim3(128), 0, st, (const uint16_t*)Q,
+                      (const uint16_t*)Ck, sigma, logp, prev, kind, D_hi, D_i, score, s->Hq, s->Hkv, s->Nb);
+            return;
+        }
+    }
+    if constexpr (KB * NBQ <= 8) {
+        if (fused && prev && s->dh <= 128 && s->K % 4 == 0) {
+            PS_LAUNCH("k_proxy_pipe<KB, NBQ>", (k_proxy_pipe<KB, NBQ>), dim3(s->W), dim3(256), 0, st,
+                      (const uint16_t*)Q, (const uint16_t*)Ck, sigma, logp, prev, kind, D_hi, D_i, score, s->Hq,
+                      s->Hkv, s->dh, s->Nb, s->K);
+            return;
+        }
+    }
     PS_LAUNCH("k_proxy_bf16<KB, NBQ>", (k_proxy_bf16<KB, NBQ>), dim3(s->W), dim3(256), 0, st, (const uint16_t*)Q,
               (const uint16_t*)Ck, sigma, logp, prev, kind, fused, D_hi, D_i, score, s->Hq, s->Hkv, s->dh, s->Nb,
               s->K);

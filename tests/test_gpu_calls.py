@@ -375,6 +375,38 @@ def test_proxy_attn_and_drift(P, case, kind):
     assert not host(Di).any() and not host(sc).any() and not host(Dhi).any()
 
 
+@pytest.mark.parametrize("Hkv", [32, 8])
+def test_proxy_kernels_agree_bitwise(P, Hkv):
+    """With two windows per compute unit and more, drift-step proxy attention
+    at K = 64, dh = 128 runs the whole-row kernel (two waves per window); a
+    single window runs the four-wave pipelined kernel.  Both add the same
+    terms in the same order, so a window's log-probabilities, drifts and
+    scores are bit-identical either way."""
+    W = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    Nb, Hq, dh, K = 32, 32, 128, 64
+    say("proxy kernels agree", W, Hkv)
+    g = torch.Generator(device="cuda").manual_seed(21)
+    Q = torch.randn(W, Nb, Hq, dh, device="cuda", generator=g).to(torch.bfloat16)
+    Ck = (torch.randn(W, K, Hkv, dh, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    prev = torch.log_softmax(torch.randn(W, Hq, Nb, K, device="cuda", generator=g) * 2.0, dim=-1)
+    sigma = float(np.float32(dh ** -0.5))
+
+    def run(sl, n):
+        s = P.Shape(W=n, N=K, d=16, Hq=Hq, Hkv=Hkv, dh=dh, Nb=Nb, K=K)
+        out = (torch.zeros(n, Hq, Nb, K, device="cuda"), torch.zeros(n, Hq, Nb, device="cuda"),
+               torch.zeros(n, Nb, device="cuda"), torch.zeros(n, K, device="cuda"))
+        P.ps_proxy_attn(s, P.PS_BF16, Q[sl].contiguous(), Ck[sl].contiguous(), sigma, out[0],
+                        prev[sl].contiguous(), 0, out[1], out[2], out[3])
+        torch.cuda.synchronize()
+        return [host(x) for x in out]
+
+    full = run(slice(0, W), W)
+    for w in (0, 137 % W, W - 1):
+        one = run(slice(w, w + 1), 1)
+        for a, b in zip(full, one):
+            assert np.array_equal(a[w].view(np.uint32), b[0].view(np.uint32)), f"window {w}"
+
+
 def test_drift_identical_is_exactly_zero(P):
     rng = np.random.default_rng(14)
     W, Hq, Nb, K = 2, 8, 16, 64
