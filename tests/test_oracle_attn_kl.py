@@ -161,3 +161,76 @@ def test_fused_equals_unfused():
     assert np.array_equal(fused["logp"], alone["logp"])
     for key in ("D_hi", "D_i", "score"):
         assert np.array_equal(fused[key], kl[key])
+
+
+# Hand-worked case for the two score kinds that the invariants above leave
+# open: 2 heads x 2 block rows x K = 2, with distributions whose terms
+# p (l - l') have opposite signs on the same cluster, so that an absolute
+# value taken after the sum, or weights taken from the previous step, change
+# the result.  [h][i] -> (current distribution p, previous distribution q).
+_WORKED = {
+    (0, 0): ((3 / 4, 1 / 4), (1 / 2, 1 / 2)),
+    (0, 1): ((1 / 4, 3 / 4), (1 / 2, 1 / 2)),
+    (1, 0): ((1 / 2, 1 / 2), (3 / 4, 1 / 4)),
+    (1, 1): ((7 / 8, 1 / 8), (1 / 8, 7 / 8)),
+}
+_L = np.log
+# the terms p_k ln(p_k / q_k) of each (head, row), worked out by hand
+_TERMS = {
+    (0, 0): (3 / 4 * _L(3 / 2), 1 / 4 * _L(1 / 2)),
+    (0, 1): (1 / 4 * _L(1 / 2), 3 / 4 * _L(3 / 2)),
+    (1, 0): (1 / 2 * _L(2 / 3), 1 / 2 * _L(2)),
+    (1, 1): (7 / 8 * _L(7), 1 / 8 * _L(1 / 7)),
+}
+
+
+def _worked_inputs():
+    cur = np.zeros((1, 2, 2, 2), np.float32)
+    prev = np.zeros((1, 2, 2, 2), np.float32)
+    for (h, i), (p, q) in _WORKED.items():
+        cur[0, h, i] = np.log(p)
+        prev[0, h, i] = np.log(q)
+    return O.Shape(W=1, N=2, d=16, Hq=2, Nb=2, K=2), cur, prev
+
+
+def test_worked_case_drift_per_head_and_token():
+    """D_{h,i} is the sum of the row's two terms; D_i their mean over the two
+    heads (values: 0.1308, 0.1308, 0.1438, 1.4594)."""
+    s, cur, prev = _worked_inputs()
+    r = O.drift_kl(s, cur, prev)
+    D = {hi: t[0] + t[1] for hi, t in _TERMS.items()}
+    assert abs(D[(0, 0)] - 0.130812) < 1e-6 and abs(D[(1, 1)] - 1.459433) < 1e-6
+    for (h, i), v in D.items():
+        assert abs(r["D_hi"][0, h, i] - v) < 1e-6
+    for i in range(2):
+        assert abs(r["D_i"][0, i] - (D[(0, i)] + D[(1, i)]) / 2) < 1e-6
+
+
+def test_worked_case_share_and_abs_scores():
+    """KL_SHARE: s_k = (1/Hq) sum_{h,i} term_k; KL_SHARE_ABS: the same sum of
+    |term_k|.  Cluster 0 collects +0.3041, -0.1733, -0.2027 and +1.7027, so the
+    two differ (0.8154 vs 1.1914), and an absolute value of the sum (0.8154)
+    is caught."""
+    s, cur, prev = _worked_inputs()
+    share = O.drift_kl(s, cur, prev, O.SCORE_KL_SHARE)["score"][0]
+    ab = O.drift_kl(s, cur, prev, O.SCORE_KL_SHARE_ABS)["score"][0]
+    for k in range(2):
+        want_share = sum(t[k] for t in _TERMS.values()) / 2
+        want_abs = sum(abs(t[k]) for t in _TERMS.values()) / 2
+        assert abs(share[k] - want_share) < 1e-6, (k, share[k], want_share)
+        assert abs(ab[k] - want_abs) < 1e-6, (k, ab[k], want_abs)
+    assert abs(ab[0] - 1.191395) < 1e-6 and abs(share[0] - 0.815375) < 1e-6
+    assert abs(ab[1] - 0.533599) < 1e-6 and abs(share[1] - 0.117073) < 1e-6
+
+
+def test_worked_case_attention_weighted_score():
+    """ATTN_WEIGHTED: s_k = (1/Hq) sum_{h,i} p_{h,i,k} D_{h,i} with the CURRENT
+    step's attention p; weights from the previous step would give 0.2106 and
+    0.7219 instead of 0.7399 and 0.1926."""
+    s, cur, prev = _worked_inputs()
+    got = O.drift_kl(s, cur, prev, O.SCORE_ATTN_WEIGHTED)["score"][0]
+    D = {hi: t[0] + t[1] for hi, t in _TERMS.items()}
+    for k in range(2):
+        want = sum(_WORKED[hi][0][k] * D[hi] for hi in D) / 2
+        assert abs(got[k] - want) < 1e-6, (k, got[k], want)
+    assert abs(got[0] - 0.739868) < 1e-6 and abs(got[1] - 0.192581) < 1e-6

@@ -26,7 +26,8 @@ SRC = os.path.join(os.path.dirname(O.__file__), "polestar_oracle.c")
 HDR = os.path.join(os.path.dirname(O.__file__), "polestar_oracle.h")
 
 # name, text in the source (must occur exactly once), planted replacement,
-# pins (test function, args) expected to notice
+# pins (test function, args) expected to notice; a mistake spanning several
+# places gives tuples of texts and replacements
 MUTATIONS = [
     ("e4m3 ties to odd", "(dist == bestd && (c & 1) == 0)", "(dist == bestd && (c & 1) == 1)",
      [(T_fmt.test_e4m3_encode_matches_torch_in_range_and_on_ties, ())]),
@@ -121,6 +122,16 @@ MUTATIONS = [
      [(T_attn.test_abs_score_bounds_share, ())]),
     ("attention-weighted score ignores the attention", "sacc[k] += p * D;", "sacc[k] += D;",
      [(T_attn.test_scores_decompose_the_drift, (O.SCORE_ATTN_WEIGHTED,))]),
+    ("attention-weighted score by the previous step's attention", "sacc[k] += p * D;",
+     "sacc[k] += exp(lp) * D;",
+     [(T_attn.test_worked_case_attention_weighted_score, ())]),
+    ("abs score as the absolute value of the summed terms",
+     ("sacc[k] += fabs(term);",
+      "score[(size_t)w * K + k] = (float)(sacc[k] / (double)Hq);"),
+     ("sacc[k] += term;",
+      "score[(size_t)w * K + k] = (float)((score_kind == PSO_SCORE_KL_SHARE_ABS ? fabs(sacc[k]) : sacc[k])"
+      " / (double)Hq);"),
+     [(T_attn.test_worked_case_share_and_abs_scores, ())]),
     ("top-k ranks the lowest scores first", "if (!na && a != b) return a > b;", "if (!na && a != b) return a < b;",
      [(T_tg.test_topk_matches_brute_force, (0,))]),
     ("unit rows by a rounded reciprocal", "return n > 0.0f ? h / n : 0.0f;", "return n > 0.0f ? h * (1.0f / n) : 0.0f;",
@@ -145,11 +156,16 @@ def mutants():
     hdr = open(HDR).read()
     jobs = []
     for i, (name, old, new, _) in enumerate(MUTATIONS):
-        assert base.count(old) == 1, f"mutation {name!r}: target text occurs {base.count(old)} times"
+        # one mistake may need edits in several places: tuples of texts
+        olds, news = (old, new) if isinstance(old, tuple) else ((old,), (new,))
+        src = base
+        for o, n in zip(olds, news):
+            assert base.count(o) == 1, f"mutation {name!r}: target text occurs {base.count(o)} times"
+            src = src.replace(o, n)
         d = os.path.join(tmp.name, f"m{i}")
         os.makedirs(d)
         open(os.path.join(d, "polestar_oracle.h"), "w").write(hdr)
-        open(os.path.join(d, "polestar_oracle.c"), "w").write(base.replace(old, new))
+        open(os.path.join(d, "polestar_oracle.c"), "w").write(src)
         jobs.append((name, os.path.join(d, "polestar_oracle.c"), os.path.join(d, "libmutant.so")))
     with ThreadPoolExecutor(max_workers=8) as ex:
         results = list(ex.map(_compile, jobs))
