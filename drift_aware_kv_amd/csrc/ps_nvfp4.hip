@@ -12,6 +12,7 @@
 // stated convention (every fp32 step one correctly rounded operation) bit for
 // bit; rows outside the proof's conditions take the exact path.  The gather is bandwidth bound: one workgroup per selected row.
 #include "ps_common.h"
+#include "ps_nvfp4_fast.h"
 
 using namespace ps;
 
@@ -27,9 +28,7 @@ namespace {
 // 2^-50 of a / b.  y is RN64(1/b) for the norm n and the constants 6 and
 // 2688; for the row scale g and each block's eff, both normal fp32 numbers in
 // [2^-126, 2^126) on this path, it is the fp32 reciprocal estimate refined by
-// two Newton steps in fp64 (`recip_nr`: the relative error e of the start
-// becomes e^4 plus fp64 rounding; checked exhaustively over that range, below
-// 2^-53).  Below the normal
+// two Newton steps in fp64 (`recip_nr`, within 2^-52 over that range).  Below the normal
 // range the midpoints are coarser than that argument covers: a row with a
 // non-zero |h| or |r| whose exponent is 125 or more below its divisor's, or
 // subnormal, is redone with divisions (`residual_row_exact`); so is a row with
@@ -37,27 +36,9 @@ namespace {
 // block-scale quotients lose their margin.  With max |r| >= 2^-100 a block whose Ab/6 is below 2^-125
 // has (Ab/6)/g below 2^-13, which encodes to the E4M3 zero either way.
 //
-// E2M1 rounding on the fast path uses gfx950's fp32 -> fp4 conversion with
-// scale 1.0: checked exhaustively over every finite fp32 input, it returns the
-// nearest-even, saturating E2M1 code of the convention except that a negative
-// input rounding to zero comes back as -0 (nibble 0x8); `plus_zero` clears
-// those signs.
-__device__ __forceinline__ uint32_t plus_zero(uint32_t w)
-{
-    const uint32_t m = w & 0x77777777u;                              // magnitudes
-    const uint32_t nz = (m | (m >> 1) | (m >> 2)) & 0x11111111u;     // magnitude != 0
-    return m | (w & (nz << 3));
-}
-
-// 1/b within 2^-52 (relative) for a normal fp32 b in [2^-126, 2^126)
-__device__ __forceinline__ double recip_nr(float b)
-{
-    const double b64 = (double)b;
-    double y = (double)__builtin_amdgcn_rcpf(b);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) y = fma(y, fma(-b64, y, 1.0), y);
-    return y;
-}
+// E2M1 and E4M3 rounding on the fast path use gfx950's conversions
+// (ps_nvfp4_fast.h states the range over which each equals the convention's
+// rounding; the test suite sweeps every input of those ranges on the GPU).
 
 __device__ __forceinline__ uint32_t wave_max_u(uint32_t v)
 {
@@ -280,21 +261,21 @@ __device__ __forceinline__ bool residual_row_fast(const uint4 (&hq)[BPL][sizeof(
         if (!zero_row) {
             const float q1 = (float)((double)__uint_as_float(bmax[b]) * (1.0 / 6.0));
             const float q2 = (float)((double)q1 * inv_g);
-            sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q2, 0, false) & 0xffu;
-            const float eff = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
+            sb = e4m3_fast(q2);
+            const float eff = e4m3_fast_decode(sb) * g;
             if (eff != 0.0f) {
                 const double y = recip_nr(eff);
                 float v[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) v[t] = (float)((double)r[b][t] * y);
-                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[0], v[1], 1.0f, 0);
-                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[2], v[3], 1.0f, 1);
-                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[4], v[5], 1.0f, 2);
-                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[6], v[7], 1.0f, 3);
-                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[8], v[9], 1.0f, 0);
-                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[10], v[11], 1.0f, 1);
-                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[12], v[13], 1.0f, 2);
-                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[14], v[15], 1.0f, 3);
+                w0 = e2m1x2_fast<0>(w0, v[0], v[1]);
+                w0 = e2m1x2_fast<1>(w0, v[2], v[3]);
+                w0 = e2m1x2_fast<2>(w0, v[4], v[5]);
+                w0 = e2m1x2_fast<3>(w0, v[6], v[7]);
+                w1 = e2m1x2_fast<0>(w1, v[8], v[9]);
+                w1 = e2m1x2_fast<1>(w1, v[10], v[11]);
+                w1 = e2m1x2_fast<2>(w1, v[12], v[13]);
+                w1 = e2m1x2_fast<3>(w1, v[14], v[15]);
                 w0 = plus_zero(w0);
                 w1 = plus_zero(w1);
             }

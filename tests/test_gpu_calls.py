@@ -5,6 +5,7 @@ documented near-ties; floating-point results within 1e-3 relative / 1e-5
 absolute.  Shapes span several tiles with ragged tails (N not a multiple of
 128, K not a multiple of 16, d not a multiple of 64, dh not a multiple of 32)."""
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -58,15 +59,17 @@ KM_CASES = [
 
 @pytest.mark.parametrize("case", KM_CASES, ids=[c[0] for c in KM_CASES])
 def test_kmeans_iterations(P, case):
-    """Four Lloyd iterations, one call each, on both sides, each side chained
-    on its own centres (STRIDED first, then GIVEN).  Every iteration must give
-    the same assignment, counts, centres, keys and objective; a row assigned
-    differently must be a near-tie under the centres both sides started the
-    iteration from, and ends the comparison of the case (the chains then
-    legitimately part)."""
+    """Four Lloyd iterations, one call each, on both sides (STRIDED first,
+    then GIVEN).  Every iteration must give the same assignment, counts,
+    centres, keys and objective.  A row assigned differently must be a
+    near-tie under the centres both sides started the iteration from; the
+    clusters such rows touch are then left out of that iteration's
+    comparison, and the device restarts the next iteration from the oracle's
+    centres and keys, so every iteration is compared on every other cluster.
+    The data of each case come from a fixed seed (crc32 of its name)."""
     name, W, N, d, K, Hkv, dh, bf = case
     say("kmeans iterations", name)
-    rng = np.random.default_rng(abs(hash(name)) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
     dt = P.PS_BF16 if bf else P.PS_F32
     H = rnd_bf16(rng, (W, N, d)) if bf else rng.standard_normal((W, N, d)).astype(np.float32)
     Kr = rnd_bf16(rng, (W, N, Hkv, dh)) if bf else rng.standard_normal((W, N, Hkv, dh)).astype(np.float32)
@@ -83,6 +86,7 @@ def test_kmeans_iterations(P, case):
     odt = O.BF16 if bf else O.F32
     oC = np.zeros((W, K, d), np.float32)                       # the oracle's own chain
     oCk = np.zeros((W, K, Hkv, dh), np.uint16 if bf else np.float32)
+    full = 0
     for it in range(4):
         init = P.PS_INIT_STRIDED if it == 0 else P.PS_INIT_GIVEN
         C_in = O.kmeans_init(so, odt, H, O.INIT_STRIDED) if it == 0 else oC.copy()
@@ -94,23 +98,31 @@ def test_kmeans_iterations(P, case):
         assert max_rel(gn, r["row_norm"]) <= 1.2e-7, "row norms"
         for w in range(W):
             check_centre_properties(H[w], bf, gn[w], ga[w], gC[w], gcnt[w])
-        ties = []
+        keep = np.ones((W, K), bool)       # clusters no near-tie row touches
+        n_ties = 0
         for w in range(W):
             t_w, real = assignment_mismatches(H[w], C_in[w], bf, ga[w], r["assign"][w],
                                               r["row_norm"][w])
             assert not real, f"iter {it} window {w}: {len(real)} assignment disagreements"
-            ties += t_w
-        if ties:
-            say(f"  iteration {it}: {len(ties)} near-tie rows; the chains part here")
-            return
-        assert np.array_equal(gcnt, r["counts"])
-        assert close(gC, r["C"], 1e-6, 1e-7), f"centres iter {it}: {max_rel(gC, r['C'])}"
+            keep[w, ga[w][t_w]] = False
+            keep[w, r["assign"][w][t_w]] = False
+            n_ties += len(t_w)
+        assert np.array_equal(gcnt[keep], r["counts"][keep])
+        assert close(gC[keep], r["C"][keep], 1e-6, 1e-7), f"centres iter {it}: {max_rel(gC, r['C'])}"
         if bf:
-            assert np.array_equal(gCk, r["Ck"]), "centroid keys"
+            assert np.array_equal(gCk[keep], r["Ck"][keep]), "centroid keys"
         else:
-            assert close(gCk, r["Ck"], 1e-6, 1e-7)
-        assert close(gobj, r["objective"], 1e-9, 1e-9)
+            assert close(gCk[keep], r["Ck"][keep], 1e-6, 1e-7)
+        if n_ties:
+            say(f"  iteration {it}: {n_ties} near-tie rows; {int((~keep).sum())} clusters left out, "
+                "the device restarts from the oracle's centres")
+            C.copy_(dev(r["C"]))
+            Ck.copy_(dev(r["Ck"]).view(Ck.dtype) if bf else dev(r["Ck"]))
+        else:
+            assert close(gobj, r["objective"], 1e-9, 1e-9)
+            full += 1
         oC, oCk = r["C"], r["Ck"]
+    say(f"  {full} of 4 iterations compared on every cluster")
 
 
 ITER_CASES = [("ragged-bf16", 3, 300, 80, 37, True), ("llada-rows", 2, 1024, 4096, 64, True),

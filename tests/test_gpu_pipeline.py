@@ -11,10 +11,12 @@ computed.  Where the two sides assign a row differently, the step is replayed
 one Lloyd iteration at a time on both sides, each from its own state, to find
 the first iteration that differs; every row that differs there must be a
 near-tie (oracle fp64 gap <= 1e-6 on the cosine scale) under the centres both
-sides started that iteration from.  That window's chains then legitimately
-part and its later steps are checked only for properties that hold on their
-own (counts, unit centres along their members)."""
+sides started that iteration from.  That window's chains would then
+legitimately part, but for the committed seeds no chain does: the tests
+require every sampled window to be compared in full at every step, codes,
+scales and rebuilt rows bit for bit on every row."""
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -118,11 +120,12 @@ def compare_step(cfg, g, o, conf, t, d_hist):
     a = o["assign"][0]
     same_c = np.all(g["C"][0].view(np.uint32) == o["C"][0].view(np.uint32), axis=-1)
     rows = same_c[a] & (g["row_norm"][0].view(np.uint32) == o["row_norm"][0].view(np.uint32))
-    assert rows.mean() >= 0.99, f"only {rows.mean():.4f} of the rows have bit-identical coder inputs"
-    assert np.array_equal(g["codes"][0][rows], o["codes"][0][rows]), "codes"
-    assert np.array_equal(g["bscale"][0][rows], o["bscale"][0][rows]), "block scales"
-    assert np.array_equal(g["rscale"][0][rows].view(np.uint32), o["rscale"][0][rows].view(np.uint32))
-    assert close(g["rscale"], o["rscale"], 1e-6, 0.0)
+    # both sides sum the same fp64 terms in the same order: on an intact chain
+    # every row's coder inputs are bit-identical, and so must every code be
+    assert rows.all(), f"{int((~rows).sum())} rows have coder inputs that differ in some bit"
+    assert np.array_equal(g["codes"], o["codes"]), "codes"
+    assert np.array_equal(g["bscale"], o["bscale"]), "block scales"
+    assert np.array_equal(g["rscale"].view(np.uint32), o["rscale"].view(np.uint32)), "row scales"
     assert close(g["logp"], o["logp"]), f"logp {max_rel(g['logp'], o['logp'])}"
     if t == 0:
         assert not g["D_i"].any() and not g["score"].any()
@@ -152,9 +155,8 @@ def compare_step(cfg, g, o, conf, t, d_hist):
     assert np.array_equal(g["pos"][0, :m], o["pos"][0, :m])
     assert np.array_equal(g["K_out"][0, :m], o["K_out"][0, :m])
     assert np.array_equal(g["V_out"][0, :m], o["V_out"][0, :m])
-    gr = rows[o["pos"][0, :m]]           # rebuilt rows whose coder inputs were bit-identical
     view = np.uint16 if cfg.bf16 else np.uint32
-    assert np.array_equal(g["H_hat"][0, :m][gr].view(view), o["H_hat"][0, :m][gr].view(view))
+    assert np.array_equal(g["H_hat"][0, :m].view(view), o["H_hat"][0, :m].view(view)), "rebuilt rows"
     assert np.array_equal(g["suffix_flag"], o["suffix_flag"]), "suffix flag"
     assert np.array_equal(g["commit_suffix"], o["commit_suffix"]), "suffix commit"
 
@@ -200,7 +202,8 @@ def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl", residua
     """GPU DriftPath over `steps` steps with the commit rules; the oracle runs
     its own chain for each sampled window.  From step score_only_from on, both
     sides keep their clusters and run only the scoring half.  Returns the
-    number of windows whose chains parted at a near-tie."""
+    number of windows whose chains parted at a near-tie (the tests require
+    none for their seeds: every sampled window is compared at every step)."""
     from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
     W = cfg.W if W is None else W
     windows = list(range(W)) if windows is None else windows
@@ -247,6 +250,14 @@ def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl", residua
         recluster = score_only_from is None or t < score_only_from
         path.step(Hd, Krd, Vd, Qd, conf=confd, recluster=recluster)
         torch.cuda.synchronize()
+        live = [w for w in windows if w not in parted]
+        say(f"  {cfg.name} step {t}: oracle windows {live}")
+        # the oracle's windows are independent: one host thread each (the
+        # oracle library releases the interpreter lock while it runs)
+        with ThreadPoolExecutor(max_workers=max(1, min(len(live), 16))) as ex:
+            ores = dict(zip(live, ex.map(
+                lambda w: oracle_step(cfg, ost[w], host_data[w], conf[w], t, cluster_score=cluster_score,
+                                      recluster=recluster), live)))
         for w in windows:
             gs = gpu_snapshot(path, w, t)
             if recluster:     # the clusters describe this step's rows
@@ -254,9 +265,7 @@ def run_chained(P, cfg, steps, windows=None, W=None, cluster_score="kl", residua
                                         gs["assign"][0], gs["C"][0], gs["counts"][0])
             if w in parted:
                 continue
-            say(f"  {cfg.name} step {t}: oracle window {w}")
-            o = oracle_step(cfg, ost[w], host_data[w], conf[w], t, cluster_score=cluster_score,
-                            recluster=recluster)
+            o = ores[w]
             if not np.array_equal(gs["assign"], o["assign"]):
                 ties = replay_first_difference(P, cfg, host_data[w], prevC[w], prevCk[w], ost[w], t)
                 say(f"    window {w} step {t}: chains part at {len(ties)} near-tie rows")
@@ -279,22 +288,20 @@ def test_tiny_planted_three_steps_exact(P):
 
 def test_llada_layer_chained(P):
     cfg = synth.CONFIGS["llada8b-layer"]
-    say("llada layer: windows parted at a near-tie:", run_chained(P, cfg, steps=4))
+    assert run_chained(P, cfg, steps=4) == 0
 
 
 def test_llada_layer_chained_cosine_score(P):
     """The same chain with clusters ranked by how far their centres moved."""
     cfg = synth.CONFIGS["llada8b-layer"].with_(W=4)
-    say("llada layer (cosine ranking): windows parted at a near-tie:",
-        run_chained(P, cfg, steps=3, cluster_score="cosine"))
+    assert run_chained(P, cfg, steps=3, cluster_score="cosine") == 0
 
 
 def test_llada_layer_chained_host_residual_store(P):
     """The same chain with the residual store in pinned host memory: the gather
     fetches the selected rows across PCIe."""
     cfg = synth.CONFIGS["llada8b-layer"].with_(W=2)
-    say("llada layer (host residual store): windows parted at a near-tie:",
-        run_chained(P, cfg, steps=3, residual_store="host"))
+    assert run_chained(P, cfg, steps=3, residual_store="host") == 0
 
 
 def test_llada_layer_scoring_only_steps(P):
@@ -302,30 +309,30 @@ def test_llada_layer_scoring_only_steps(P):
     residual codes and only score (proxy attention and drift, top-k, gather
     with the step's own K/V rows, commit rules)."""
     cfg = synth.CONFIGS["llada8b-layer"].with_(W=2)
-    say("llada layer (scoring-only steps): windows parted at a near-tie:",
-        run_chained(P, cfg, steps=4, score_only_from=2))
+    assert run_chained(P, cfg, steps=4, score_only_from=2) == 0
 
 
 def test_dream_layer_chained(P):
     cfg = synth.CONFIGS["dream7b-layer"]
-    say("dream layer: windows parted at a near-tie:", run_chained(P, cfg, steps=3))
+    assert run_chained(P, cfg, steps=3) == 0
 
 
 def test_full_size_llada_batch_sampled(P):
     """512 windows (32 layers x 16 sequences) in one launch per call, as the
     benchmark runs them; windows 0, 301 and 511 checked against the oracle."""
     cfg = synth.CONFIGS["llada8b-batch"]
-    say("llada batch: windows parted at a near-tie:",
-        run_chained(P, cfg, steps=3, windows=[0, 301, 511]))
+    assert run_chained(P, cfg, steps=3, windows=[0, 301, 511]) == 0
 
 
+@pytest.mark.timeout(900)
 def test_full_size_long_window_sampled(P):
-    """128 windows of 8192 tokens, K = 256, in one launch per call; one window
-    checked with two Lloyd iterations per step (the first pass and a later
-    pass, which run different variants of the tile kernel; the oracle needs
-    minutes for eight at this size, and more passes run the same kernels)."""
-    cfg = synth.CONFIGS["llada8b-long"].with_(iters=2)
-    say("long window: windows parted at a near-tie:", run_chained(P, cfg, steps=2, windows=[77]))
+    """128 windows of 8192 tokens, K = 256, all eight Lloyd iterations per
+    step, in one launch per call as the benchmark runs them; windows 5 and 77
+    checked against the oracle over window formation and one drift step (the
+    oracle takes about a minute per window-step at this size, one host thread
+    per window)."""
+    cfg = synth.CONFIGS["llada8b-long"]
+    assert run_chained(P, cfg, steps=2, windows=[5, 77]) == 0
 
 
 def test_step_is_deterministic(P):
