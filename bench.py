@@ -9,12 +9,18 @@ A step is one pass of the whole path over one batch of W windows:
 Inputs are seeded synthetic tensors already resident in HBM (one snapshot per
 denoising step, generated on the device before the timed region).
 
+The headline workload is the long-window batch (LLaDA-8B shape, 32 layers x
+4 sequences, N = 8192, K = 256): the largest workload that fits one GPU.  The
+512-window LLaDA-8B batch (N = 1024, K = 64) is timed after it as a secondary
+figure in the same line.
+
 Prints one JSON line: metric, value (window-token-layers scored per second),
 the roofline of the dominant kernel (its HIP-event average launch time over the
-timed region against its algorithmic bytes) and the CPU oracle timed on a
-bounded sample of the same workload.
+timed region against its algorithmic bytes), the step against the compulsory
+bytes and flops of the method, and the CPU oracle timed on a bounded sample of
+the same workload and the same input bytes.
 
-  python bench.py [--steps K] [--warmup W] [--config llada8b-batch] [--gpus 1]
+  python bench.py [--steps K] [--warmup W] [--config llada8b-long] [--gpus 1]
 """
 import argparse
 import json
@@ -29,7 +35,8 @@ METRIC = "window-token-layers drift-scored/sec per step at 1 GPU; % HBM/MFMA roo
 UNIT = "window-token-layers/s"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-# the workloads of synth.CONFIGS (the 512-window batch is the benchmark's)
+# the workloads of synth.CONFIGS (the long-window batch is the headline; the
+# 512-window batch its secondary figure)
 CONFIG_NAMES = ("tiny-planted", "llada8b-layer", "dream7b-layer", "llada8b-batch", "llada8b-long")
 
 
@@ -43,7 +50,9 @@ def kernel_work(name, cfg, gathered=None):
     KV = cfg.Hkv * cfg.dh
     L = W * cfg.Hq * cfg.Nb * K
     if name.startswith("k_assign"):
-        # the first pass of a call below 129 clusters reads the fp32 centres
+        # H and the centres read, the assignment written (the fp64 norms of the
+        # first pass are a by-product); the first pass of a call below 129
+        # clusters reads the fp32 centres
         ce = 4 if (name.startswith("k_assign_bf16") and name.endswith("true>")) else e
         return W * N * d * e + W * K * d * ce + W * N * 4, 2.0 * W * N * K * d
     if name.startswith("k_update"):
@@ -84,7 +93,29 @@ def kernel_work(name, cfg, gathered=None):
     return None
 
 
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_k_assign_llada8b_512win.txt")
+def compulsory_work(cfg, gathered):
+    """The method's compulsory (bytes, flops) of one step over all W windows:
+    H and the key rows read once (the window's H reused across the Lloyd
+    iterations), norms and assignments written, the fp32 centres read and
+    written, the centroid keys written and read, NVFP4 codes and scales
+    written, the queries read, the log-probabilities written and the previous
+    step's read, and for each gathered row its codes read, the rebuilt row
+    written and its K and V rows read and written; flops: iters * 2NKd for the
+    assignment plus 2 Hq Nb K dh for proxy attention.  `gathered` is the mean
+    number of rows the gather selected per window."""
+    e = 2 if cfg.bf16 else 4
+    N, d, K = cfg.N, cfg.d, cfg.K
+    KV = cfg.Hkv * cfg.dh
+    M = gathered
+    per_window = (N * d * e + N * KV * e + 2 * N * 4 + 2 * K * d * 4 + 2 * K * KV * e
+                  + N * d // 2 + N * d // 16 + N * 4 + cfg.Nb * cfg.Hq * cfg.dh * e
+                  + 2 * cfg.Hq * cfg.Nb * K * 4
+                  + M * (d // 2 + d // 16 + 4) + M * d * e + 4 * M * KV * e)
+    flops = cfg.iters * 2.0 * N * K * d + 2.0 * cfg.Hq * cfg.Nb * K * cfg.dh
+    return cfg.W * per_window, cfg.W * flops
+
+
+PROFILES = os.path.join(HERE, "profiles")
 KERNEL_SOURCES = [os.path.join(HERE, "drift_aware_kv_amd", "csrc", f)
                   for f in ("ps_kmeans.hip", "ps_common.h")]
 
@@ -98,16 +129,19 @@ def kernel_source_hash():
 
 
 def recorded_traffic(kernel_name, cfg_name):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, if it was taken on this kernel source and workload; else
-    None."""
-    try:
-        kv = dict(l.strip().split("=", 1) for l in open(TRAFFIC_FILE) if "=" in l and not l.startswith("#"))
-    except OSError:
-        return None
-    if kv.get("source_sha256") != kernel_source_hash() or kv.get("workload") != cfg_name or kv.get("kernel") != kernel_name:
-        return None
-    return float(kv["traffic_bytes_per_launch"])
+    """HBM bytes per launch of a K-Means kernel from the committed rocprofv3
+    counter summaries (profiles/traffic_*.txt), if one was taken on this
+    kernel source, kernel and workload; else None."""
+    import glob
+    src = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "traffic_*.txt"))):
+        try:
+            kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
+        except (OSError, ValueError):
+            continue
+        if kv.get("source_sha256") == src and kv.get("workload") == cfg_name and kv.get("kernel") == kernel_name:
+            return float(kv["traffic_bytes_per_launch"])
+    return None
 
 
 def copy_calibration():
@@ -237,59 +271,222 @@ def bandwidth():
     print(json.dumps(ceilings()))
 
 
-def cpu_baseline(cfg, budget_s):
-    """The oracle, unchanged, on a bounded sample: one steady-state step
-    (warm-started K-Means, residuals, proxy attention + KL, top-k, gather,
-    commit rules) of
-    independent windows, fanned out over host threads (ctypes releases the
-    GIL).  The formation step that produces each window's state is untimed."""
+def cpu_threads():
+    """Host threads for the oracle baseline: the cores this process may run
+    on, at most 16 (the host share of one GPU on the benchmark machines)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def sample_windows(cfg, wl, n):
+    """Host copies of n windows, spread over the batch, of the device inputs of
+    step 0 (window formation) and step 1: the same bytes the GPU ran on."""
+    import numpy as np
+    import torch
+
+    def host(t):
+        t = t.detach()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    ws = sorted({min(cfg.W - 1, (i * cfg.W) // n) for i in range(n)})
+    out = []
+    for w in ws:
+        snaps = []
+        for step in (0, 1):
+            H, Kr, V, Q, conf = wl.inputs(step)
+            snaps.append({k: np.ascontiguousarray(host(x[w:w + 1]))
+                          for k, x in (("H", H), ("Kr", Kr), ("V", V), ("Q", Q), ("conf", conf))})
+        out.append((w, snaps))
+    return out
+
+
+def cpu_baseline(cfg, samples, alpha, tau_s):
+    """The oracle, unchanged, on a bounded sample of the workload: for each
+    sampled window (the device's own input bytes), window formation at step 0
+    (untimed) and then one steady-state step at step 1 (timed): warm-started
+    K-Means, residuals, proxy attention + KL, top-k, gather, commit rules.
+    One window per host thread, all threads started together (ctypes releases
+    the interpreter lock inside the oracle)."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle as O
-    import synth
 
-    P = min(16, os.cpu_count() or 1)
     s = O.Shape(W=1, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K)
     dt = O.BF16 if cfg.bf16 else O.F32
 
-    def prepare(w):
-        data = synth.generate(cfg, w0=w, Wc=1)
+    def prepare(sample):
+        _, (s0, _) = sample
         init = O.INIT_FARTHEST if cfg.init0 == "farthest" else O.INIT_STRIDED
-        r = O.kmeans_fit(s, dt, data["H"], data["Kr"], init, cfg.iters,
-                         np.zeros((1, cfg.K, cfg.d), np.float32))
-        lp = O.proxy_attn(s, dt, data["Q"], r["Ck"], cfg.softmax_scale)["logp"]
-        synth.apply_drift(cfg, data, 1, w0=w)
-        conf = synth.confidences(cfg, 1, w0=w, Wc=1)
-        return data, r["C"], r["Ck"], lp, conf
+        ck0 = np.zeros((1, cfg.K, cfg.Hkv, cfg.dh), np.uint16 if cfg.bf16 else np.float32)
+        r = O.kmeans_fit(s, dt, s0["H"], s0["Kr"], init, cfg.iters,
+                         np.zeros((1, cfg.K, cfg.d), np.float32), ck0)
+        lp = O.proxy_attn(s, dt, s0["Q"], r["Ck"], cfg.softmax_scale)["logp"]
+        return r["C"], r["Ck"], lp
 
     def step(args):
-        data, C, Ck, lp, conf = args
+        (_, (_, x)), (C, Ck, lp) = args
         hist_sum, hist_n = np.zeros((1, cfg.Nb)), np.zeros(1, np.int32)
         t0 = time.perf_counter()
-        r = O.kmeans_fit(s, dt, data["H"], data["Kr"], O.INIT_GIVEN, cfg.iters, C.copy(), Ck.copy())
-        q = O.residual_nvfp4(s, dt, data["H"], r["row_norm"], r["C"], r["assign"])
-        pa = O.proxy_attn(s, dt, data["Q"], r["Ck"], cfg.softmax_scale, lp)
+        r = O.kmeans_fit(s, dt, x["H"], x["Kr"], O.INIT_GIVEN, cfg.iters, C.copy(), Ck.copy())
+        q = O.residual_nvfp4(s, dt, x["H"], r["row_norm"], r["C"], r["assign"])
+        pa = O.proxy_attn(s, dt, x["Q"], r["Ck"], cfg.softmax_scale, lp)
         tk = O.topk_clusters(s, pa["score"], cfg.k)
         O.refresh_gather(s, dt, r["assign"], tk["idx"], cfg.k, cfg.N, q["codes"], q["bscale"],
-                         q["rscale"], r["C"], r["row_norm"], True, data["Kr"], data["V"])
-        O.commit_block(s, pa["D_i"], conf, cfg.block_start, 0.1, 0.9, hist_sum, hist_n)
-        O.commit_suffix(s, r["assign"], tk["idx"], cfg.k, cfg.block_start, conf, 0.9)
+                         q["rscale"], r["C"], r["row_norm"], True, x["Kr"], x["V"])
+        O.commit_block(s, pa["D_i"], x["conf"], cfg.block_start, alpha, tau_s, hist_sum, hist_n)
+        O.commit_suffix(s, r["assign"], tk["idx"], cfg.k, cfg.block_start, x["conf"], tau_s)
         return time.perf_counter() - t0
 
-    # size the sample from one window timed alone: n windows, one per thread,
-    # about budget_s seconds of CPU work in total
-    one = step(prepare(0))
-    n = max(1, min(P, int(round(budget_s / max(one, 1e-3)))))
+    n = len(samples)
     with ThreadPoolExecutor(max_workers=n) as ex:
-        states = list(ex.map(prepare, range(1, n + 1)))
+        p0 = time.perf_counter()
+        states = list(ex.map(prepare, samples))
+        prep = time.perf_counter() - p0
         t0 = time.perf_counter()
-        list(ex.map(step, states))
+        times = list(ex.map(step, zip(samples, states)))
         wall = time.perf_counter() - t0
+    times.sort()
+    med = times[len(times) // 2]
     return {"value": n * cfg.N / wall, "unit": UNIT, "cores": n, "kind": "oracle",
-            "sample": f"{n} windows x 1 steady-state step of {cfg.name} "
-                      f"(N={cfg.N}, d={cfg.d}, K={cfg.K}, {cfg.iters} iterations), one window per "
-                      f"thread on {n} threads; one window's step alone took {one:.2f} s"}
+            "sample": f"{n} windows (of {cfg.W}: {', '.join(str(w) for w, _ in samples)}) x 1 steady-state "
+                      f"step (step 1, warm-started from an untimed formation at step 0, on the device's "
+                      f"own input bytes of those steps) of {cfg.name} (N={cfg.N}, d={cfg.d}, K={cfg.K}, "
+                      f"{cfg.iters} Lloyd iterations), one window per thread on {n} threads started together",
+            "value_per_core": cfg.N / med,
+            "per_core_note": "one thread's own window-step time (median over the threads) while all "
+                             f"{n} run: the 1-core rate",
+            "step_s": {"median": med, "min": times[0], "max": times[-1]},
+            "wall_s": wall, "formation_s": prep}
+
+
+def timed_steps(path, wl, first, steps, profile, max_launches=0):
+    """Run steps first .. first+steps-1 between a synchronisation on each side;
+    returns (elapsed seconds, sorted per-step HIP-event ms, kernel timer
+    summary or {})."""
+    import torch
+    import drift_aware_kv_amd as P
+    if profile:
+        P.profile_begin(max_launches)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    marks[0].record()
+    for i in range(first, first + steps):
+        path.step(*wl.inputs(i))
+        marks[i - first + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    prof = {}
+    if profile:
+        P.profile_end()
+        prof = P.profile_summary()
+    return t1 - t0, step_ms, prof
+
+
+def kernel_figures(cfg, prof, steps, gathered, ms_per_step):
+    """Per-kernel table, the dominant kernel's roofline and the whole step's
+    figures against the compulsory work, from the kernel timer's summary of
+    the timed steps."""
+    kernels = {k: v for k, v in prof.items() if not k.startswith("#")}
+    breakdown = {}
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][1]):
+        breakdown[k] = {"launches": v[0], "avg_ms": v[1] / v[0], "total_ms_per_step": v[1] / steps}
+        work = kernel_work(k, cfg, gathered)
+        if work and not k.startswith("k_update"):   # the update's later passes re-sum dirty clusters only
+            breakdown[k]["algorithmic_GB_per_launch"] = work[0] / 1e9
+            breakdown[k]["achieved_GBs"] = work[0] / (v[1] / v[0] * 1e-3) / 1e9
+    roof = None
+    if kernels:
+        name, (n, tot, mn, mx) = max(kernels.items(), key=lambda kv: kv[1][1])
+        work = kernel_work(name, cfg, gathered)
+        avg_s = tot / n / 1e3
+        if work:
+            byts, flops = work
+            ai = flops / byts
+            if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+                ach = flops / avg_s / 1e12
+                roof = {"kernel": name, "bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
+            else:
+                ach = byts / avg_s / 1e9
+                roof = {"kernel": name, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+            roof.update({"algorithmic_bytes_per_launch": byts, "flops_per_launch": flops,
+                         "avg_launch_ms": avg_s * 1e3, "launches": n,
+                         "mfma_frac": flops / avg_s / 1e12 / BF16_PEAK_TFLOPS})
+            roof["traffic"] = recorded_traffic(name, cfg.name)
+    # the whole step against the method's compulsory bytes and flops (H read
+    # once per step); the bytes the kernels move by their own accounting (H
+    # streamed once per Lloyd pass, by the coder, ...) are given beside it
+    cb, cf = compulsory_work(cfg, gathered)
+    t = ms_per_step * 1e-3
+    hbm, mfma = cb / t / 1e9 / HBM_PEAK_GBS, cf / t / 1e12 / BF16_PEAK_TFLOPS
+    moved = 0.0
+    for kname, (n, tot, mn, mx) in kernels.items():
+        work = kernel_work(kname, cfg, gathered)
+        if work:
+            moved += work[0] * (steps if kname.startswith("k_update") else n)
+    step_roof = {"compulsory_bytes_per_step": cb, "compulsory_flops_per_step": cf,
+                 "bound": "mfma" if cf / (BF16_PEAK_TFLOPS * 1e12) > cb / (HBM_PEAK_GBS * 1e9) else "hbm",
+                 "hbm_frac": hbm, "mfma_frac": mfma, "frac": max(hbm, mfma),
+                 "roofline_ms_per_step": 1e3 * max(cf / (BF16_PEAK_TFLOPS * 1e12), cb / (HBM_PEAK_GBS * 1e9)),
+                 "kernel_bytes_per_step": moved / steps if kernels else None}
+    return roof, step_roof, breakdown
+
+
+def make_path(cfg, args):
+    from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
+    spec = StepSpec(W=cfg.W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb,
+                    K=cfg.K, k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
+                    softmax_scale=cfg.softmax_scale, cap=cfg.N, block_start=cfg.block_start,
+                    cluster_score=args.cluster_score, residual_store=args.residual_store)
+    return DriftPath(spec)
+
+
+def load_workload(cfg, total):
+    import torch
+    from synth.device import DeviceWorkload
+    free = torch.cuda.mem_get_info()[0]
+    snap = DeviceWorkload.snapshot_bytes(cfg)
+    out_bytes = 3 * snap  # gather outputs at cap = N, plus state: generous
+    n_snap = max(2, min(total, int((0.6 * free - out_bytes) // snap)))
+    print(f"[bench] {cfg.name}: generating {n_snap} input snapshots of {snap / 2**30:.1f} GiB",
+          file=sys.stderr, flush=True)
+    return DeviceWorkload(cfg, n_snap), n_snap
+
+
+def secondary_workload(name, args):
+    """The same measurement, shorter, on another workload: value, step time,
+    the dominant kernel's roofline and the step against the compulsory work."""
+    import torch
+    import synth
+    cfg = synth.CONFIGS[name]
+    warm = 2
+    wl, n_snap = load_workload(cfg, warm + args.steps)
+    path = make_path(cfg, args)
+    for i in range(warm):
+        path.step(*wl.inputs(i))
+    elapsed, step_ms, prof = timed_steps(path, wl, warm, args.steps, True, 64 * args.steps * (cfg.iters + 8))
+    ms = 1e3 * elapsed / args.steps
+    gathered = float(torch.clamp(path.count, max=path.cap).double().mean().item())
+    roof, step_roof, _ = kernel_figures(cfg, prof, args.steps, gathered, ms)
+    print(f"[bench] secondary {cfg.name}: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    out = {"workload": cfg.name, "windows": cfg.W, "window_tokens": cfg.N, "clusters": cfg.K,
+           "top_k": cfg.k, "value": args.steps * cfg.W * cfg.N / elapsed, "ms_per_step": ms,
+           "steps": args.steps, "warmup": warm,
+           "step_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1]},
+           "roofline": roof, "step_roofline": step_roof, "gathered_rows_per_window": gathered}
+    del path, wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -297,9 +494,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="llada8b-batch", choices=sorted(CONFIG_NAMES))
-    ap.add_argument("--cpu-budget", type=float, default=20.0,
-                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--config", default="llada8b-long", choices=sorted(CONFIG_NAMES))
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads (= sampled windows) for the CPU oracle baseline (0 = the cores "
+                         "this process may use, at most 16)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary figure on the 512-window LLaDA-8B batch")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timer")
     ap.add_argument("--no-fixed-point", action="store_true",
                     help="skip the secondary timing with the exact fixed-point exit")
@@ -342,8 +543,6 @@ def main():
 
     import drift_aware_kv_amd as P
     import synth
-    from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
-    from synth.device import DeviceWorkload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -351,18 +550,9 @@ def main():
     P.lib()
     cfg = synth.CONFIGS[args.config]
     total = args.warmup + args.steps
-    free = torch.cuda.mem_get_info()[0]
-    snap = DeviceWorkload.snapshot_bytes(cfg)
-    out_bytes = 3 * snap  # gather outputs at cap = N, plus state: generous
-    n_snap = max(2, min(total, int((0.6 * free - out_bytes) // snap)))
-    print(f"[bench] {cfg.name}: generating {n_snap} input snapshots of {snap / 2**30:.1f} GiB",
-          file=sys.stderr, flush=True)
-    wl = DeviceWorkload(cfg, n_snap)
-    spec = StepSpec(W=cfg.W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb,
-                    K=cfg.K, k=cfg.k, iters=cfg.iters, bf16=cfg.bf16, init0=cfg.init0,
-                    softmax_scale=cfg.softmax_scale, cap=cfg.N, block_start=cfg.block_start,
-                    cluster_score=args.cluster_score, residual_store=args.residual_store)
-    path = DriftPath(spec)
+    wl, n_snap = load_workload(cfg, total)
+    path = make_path(cfg, args)
+    spec = path.spec
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -370,71 +560,24 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    if not args.no_profile:
-        P.profile_begin(64 * args.steps * (cfg.iters + 8))
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    marks[0].record()
-    for i in range(args.warmup, total):
-        path.step(*wl.inputs(i))
-        marks[i - args.warmup + 1].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
-    prof = {}
-    if not args.no_profile:
-        P.profile_end()
-        prof = P.profile_summary()
-    elapsed = t1 - t0
+    # the timed region: every kernel bracketed by the kernel timer's events
+    elapsed, step_ms, prof = timed_steps(path, wl, args.warmup, args.steps, not args.no_profile,
+                                         64 * args.steps * (cfg.iters + 8))
     ms_per_step = 1e3 * elapsed / args.steps
     value = args.steps * cfg.W * cfg.N / elapsed
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
-
     # rows the refresh gather selected per window in the last timed step
     gathered = float(torch.clamp(path.count, max=spec.cap).double().mean().item())
-    kernels = {k: v for k, v in prof.items() if not k.startswith("#")}
-    breakdown = {}
-    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][1]):
-        breakdown[k] = {"launches": v[0], "avg_ms": v[1] / v[0], "total_ms_per_step": v[1] / args.steps}
-        work = kernel_work(k, cfg, gathered)
-        if work and not k.startswith("k_update"):   # the update's later passes re-sum dirty clusters only
-            breakdown[k]["algorithmic_GB_per_launch"] = work[0] / 1e9
-            breakdown[k]["achieved_GBs"] = work[0] / (v[1] / v[0] * 1e-3) / 1e9
-    roof = None
-    if kernels:
-        name, (n, tot, mn, mx) = max(kernels.items(), key=lambda kv: kv[1][1])
-        work = kernel_work(name, cfg, gathered)
-        avg_s = tot / n / 1e3
-        if work:
-            byts, flops = work
-            ai = flops / byts
-            if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-                ach = flops / avg_s / 1e12
-                roof = {"kernel": name, "bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
-                        "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
-            else:
-                ach = byts / avg_s / 1e9
-                roof = {"kernel": name, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
-            roof.update({"algorithmic_bytes_per_launch": byts, "flops_per_launch": flops,
-                         "avg_launch_ms": avg_s * 1e3, "launches": n})
-            roof["traffic"] = recorded_traffic(name, cfg.name)
+    roof, step_roof, breakdown = kernel_figures(cfg, prof, args.steps, gathered, ms_per_step)
+    nxt = total
 
-    # the whole step against HBM: algorithmic bytes of every kernel launch of
-    # the timed steps (the update counted once per step: after its first pass
-    # it re-sums only the clusters whose members moved), over the step time
-    step_roof = None
-    if kernels:
-        total_bytes = 0.0
-        for kname, (n, tot, mn, mx) in kernels.items():
-            work = kernel_work(kname, cfg, gathered)
-            if work:
-                total_bytes += work[0] * (args.steps if kname.startswith("k_update") else n)
-        per_step = total_bytes / args.steps
-        ach = per_step / (ms_per_step * 1e-3) / 1e9
-        step_roof = {"bytes_per_step": per_step, "achieved": ach, "unit": "GB/s", "peak": HBM_PEAK_GBS,
-                     "frac": ach / HBM_PEAK_GBS}
+    # the same number of steps again without the kernel timer (its events are
+    # the only difference): how much the timer itself costs
+    untimed = None
+    if not args.no_profile:
+        u_el, _, _ = timed_steps(path, wl, nxt, args.steps, False)
+        nxt += args.steps
+        untimed = {"ms_per_step": 1e3 * u_el / args.steps, "value": args.steps * cfg.W * cfg.N / u_el}
 
     # secondary figure: the same steps with the exact fixed-point exit (Lloyd
     # passes after the first that moves no row are skipped per window; the
@@ -442,14 +585,10 @@ def main():
     fpx = None
     if not args.no_fixed_point:
         path.spec.kmeans_flags = P.PS_KMEANS_FIXED_POINT_EXIT
-        torch.cuda.synchronize()
-        f0 = time.perf_counter()
-        for i in range(total, total + args.steps):
-            path.step(*wl.inputs(i))
-        torch.cuda.synchronize()
-        f1 = time.perf_counter()
+        f_el, _, _ = timed_steps(path, wl, nxt, args.steps, False)
+        nxt += args.steps
         path.spec.kmeans_flags = 0
-        fpx = {"value": args.steps * cfg.W * cfg.N / (f1 - f0), "ms_per_step": 1e3 * (f1 - f0) / args.steps}
+        fpx = {"value": args.steps * cfg.W * cfg.N / f_el, "ms_per_step": 1e3 * f_el / args.steps}
         print(f"[bench] fixed-point exit: {fpx['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
 
     # secondary figure: the same steps replayed from HIP graphs (one graph per
@@ -468,6 +607,7 @@ def main():
         g1 = time.perf_counter()
         graphed = {"value": args.steps * cfg.W * cfg.N / (g1 - g0), "ms_per_step": 1e3 * (g1 - g0) / args.steps,
                    "graphs": len(path._graphs)}
+        path._graphs.clear()
         print(f"[bench] graph replay: {graphed['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
 
     # secondary figure: the scoring half only (proxy attention and drift,
@@ -491,10 +631,18 @@ def main():
         hiding = latency_hiding(path, wl, total + args.steps, args.steps)
         print(f"[bench] hidden fraction {hiding['hidden_fraction']:.3f}", file=sys.stderr, flush=True)
 
-    cpu = None
-    if args.cpu_budget > 0:
-        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, args.cpu_budget)
+    # host copies of the sampled windows' inputs for the CPU baseline, then the
+    # device memory goes to the secondary workload
+    samples = None
+    if not args.no_cpu:
+        samples = sample_windows(cfg, wl, args.cpu_threads or cpu_threads())
+    del path, wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    secondary = None
+    if not args.no_secondary and args.config == "llada8b-long":
+        secondary = secondary_workload("llada8b-batch", args)
 
     measured = None
     if not args.no_ceilings:
@@ -502,6 +650,13 @@ def main():
         if roof:
             key = "hbm_copy_GBs" if roof["unit"] == "GB/s" else "bf16_gemm_TFLOPs"
             measured["dominant_kernel_frac_of_measured"] = roof["achieved"] / measured[key]
+
+    cpu = None
+    if samples:
+        print(f"[bench] CPU oracle baseline on {len(samples)} threads", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, samples, spec.alpha, spec.tau_s)
+        print(f"[bench] CPU oracle: {cpu['step_s']['median']:.1f} s per window-step", file=sys.stderr,
+              flush=True)
 
     line = {
         "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps,
@@ -518,8 +673,10 @@ def main():
                    "input_snapshots": n_snap, "parallelism": "single GPU"},
         "roofline": roof,
         "step_roofline": step_roof,
-        "measured_ceilings": measured,
         "cpu_baseline": cpu,
+        "secondary": secondary,
+        "measured_ceilings": measured,
+        "without_kernel_timer": untimed,
         "fixed_point_exit": fpx,
         "graph_replay": graphed,
         "scoring_only": scoring,

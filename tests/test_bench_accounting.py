@@ -73,6 +73,36 @@ def test_recorded_traffic_is_tied_to_the_sources():
     assert bench.recorded_traffic("k_keys<uint16_t>", wl) is None
 
 
+def test_compulsory_work_matches_the_per_token_layer_figures():
+    """The step's compulsory bytes per window-token-layer with the expected
+    N k / K gathered rows: 25,245 B for the 1024-token windows (K = 64,
+    k = 4) and 23,229 B for the 8192-token windows (K = 256, k = 16); flops
+    iters * 2 K d + proxy attention."""
+    for name, per_tok in (("llada8b-batch", 25_245), ("llada8b-long", 23_229)):
+        cfg = synth.CONFIGS[name]
+        M = cfg.N * cfg.k / cfg.K
+        byts, flops = bench.compulsory_work(cfg, M)
+        assert abs(byts / (cfg.W * cfg.N) - per_tok) < 1.0, (name, byts / (cfg.W * cfg.N))
+        assert flops == cfg.W * (cfg.iters * 2.0 * cfg.N * cfg.K * cfg.d
+                                 + 2.0 * cfg.Hq * cfg.Nb * cfg.K * cfg.dh)
+    # the long window is flops-bound at the published peaks, the batch bytes-bound
+    c5 = synth.CONFIGS["llada8b-long"]
+    b5, f5 = bench.compulsory_work(c5, c5.N * c5.k / c5.K)
+    assert f5 / (bench.BF16_PEAK_TFLOPS * 1e12) > b5 / (bench.HBM_PEAK_GBS * 1e9)
+    c4 = synth.CONFIGS["llada8b-batch"]
+    b4, f4 = bench.compulsory_work(c4, c4.N * c4.k / c4.K)
+    assert f4 / (bench.BF16_PEAK_TFLOPS * 1e12) < b4 / (bench.HBM_PEAK_GBS * 1e9)
+
+
+def test_headline_is_the_largest_single_gpu_workload():
+    import inspect
+    src = inspect.getsource(bench.main)
+    assert 'default="llada8b-long"' in src
+    c5 = synth.CONFIGS["llada8b-long"]
+    assert (c5.W, c5.N, c5.d, c5.K, c5.k, c5.iters) == (128, 8192, 4096, 256, 16, 8)
+    assert c5.name == "llada8b-32layers-4seq-N8192-K256"
+
+
 def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
