@@ -48,11 +48,14 @@ _lib = None
 
 
 def lib():
+    """The oracle's shared library; PSO_ORACLE_LIB names another build of the
+    same source to load instead (the sanitizer test's instrumented build)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("PSO_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int
         SP = ctypes.POINTER(_CShape)
