@@ -26,8 +26,11 @@ PS_F32, PS_BF16 = 0, 1
 PS_INIT_GIVEN, PS_INIT_STRIDED, PS_INIT_FARTHEST = 0, 1, 2
 PS_SCORE_KL_SHARE, PS_SCORE_KL_SHARE_ABS, PS_SCORE_ATTN_WEIGHTED = 0, 1, 2
 PS_KMEANS_DEFAULT, PS_KMEANS_FIXED_POINT_EXIT = 0, 1
+PS_ERR_SCRATCH_LIMIT = 9
+PS_STATIC_SCRATCH_BYTES = 64 << 20     # the library's static K-Means scratch per device
 
-EXPORTS = ("ps_status_string", "ps_workspace_size", "ps_kmeans_fit", "ps_residual_nvfp4",
+EXPORTS = ("ps_status_string", "ps_workspace_size", "ps_kmeans_fit", "ps_kmeans_fit_static",
+           "ps_residual_nvfp4",
            "ps_proxy_attn", "ps_drift_kl", "ps_topk_clusters", "ps_refresh_gather",
            "ps_drift_cosine", "ps_commit_block", "ps_commit_suffix", "ps_profile_begin", "ps_profile_end", "ps_profile_summary")
 
@@ -70,6 +73,8 @@ def lib():
         L.ps_workspace_size.argtypes = [SP, I, ctypes.POINTER(ctypes.c_size_t)]
         L.ps_kmeans_fit.argtypes = [SP, I, P, P, I, ctypes.c_int32, ctypes.c_uint32, P, P, P, P, P,
                                     P, P, ctypes.c_size_t, P]
+        L.ps_kmeans_fit_static.argtypes = [SP, I, P, P, I, ctypes.c_int32, ctypes.c_uint32, P, P, P, P,
+                                           P, P, P]
         L.ps_residual_nvfp4.argtypes = [SP, I, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.ps_proxy_attn.argtypes = [SP, I, P, P, ctypes.c_float, P, P, I, P, P, P, P]
         L.ps_drift_kl.argtypes = [SP, P, P, I, P, P, P, P]
@@ -185,6 +190,21 @@ def ps_kmeans_fit(s: Shape, dtype, H, Kr, init, iters, C, assign, counts, row_no
         _ptr(counts, s.W * s.K, 4, "counts"), _ptr(row_norm, s.W * s.N, 4, "row_norm"),
         _ptr(Ck, s.W * s.K * KV, e, "Ck", True), _ptr(objective, s.W, 8, "objective", True),
         _ptr(ws, wsb, 1, "ws"), ws.numel(), _stream(stream)), "ps_kmeans_fit")
+
+
+def ps_kmeans_fit_static(s: Shape, dtype, H, Kr, init, iters, C, assign, counts, row_norm, Ck=None,
+                         objective=None, stream=None, flags=0):
+    """ps_kmeans_fit without a workspace: the library's static per-device
+    scratch (PS_STATIC_SCRATCH_BYTES) serves instead; nothing is allocated."""
+    e = _es(dtype)
+    KV = s.Hkv * s.dh
+    _check(lib().ps_kmeans_fit_static(
+        _cs(s), dtype, _ptr(H, s.W * s.N * s.d, e, "H"),
+        _ptr(Kr, s.W * s.N * KV, e, "Kr", True), init, iters, flags,
+        _ptr(C, s.W * s.K * s.d, 4, "C"), _ptr(assign, s.W * s.N, 4, "assign"),
+        _ptr(counts, s.W * s.K, 4, "counts"), _ptr(row_norm, s.W * s.N, 4, "row_norm"),
+        _ptr(Ck, s.W * s.K * KV, e, "Ck", True), _ptr(objective, s.W, 8, "objective", True),
+        _stream(stream)), "ps_kmeans_fit_static")
 
 
 def ps_residual_nvfp4(s: Shape, dtype, H, row_norm, C, assign, codes, bscale, rscale, ws=None,

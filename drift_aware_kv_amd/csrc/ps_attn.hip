@@ -1118,6 +1118,9 @@ extern "C" const char* ps_status_string(ps_status st)
     case PS_ERR_WORKSPACE: return "PS_ERR_WORKSPACE: workspace missing or too small";
     case PS_ERR_DEVICE: return "PS_ERR_DEVICE: a HIP launch or runtime call failed";
     case PS_ERR_MEMORY: return "PS_ERR_MEMORY: a buffer is neither device memory nor device-mapped pinned host memory";
+    case PS_ERR_SCRATCH_LIMIT:
+        return "PS_ERR_SCRATCH_LIMIT: the shape needs more K-Means scratch than the static scratch holds "
+               "(PS_STATIC_SCRATCH_BYTES); use ps_kmeans_fit with a workspace";
     }
     return "unknown ps_status";
 }

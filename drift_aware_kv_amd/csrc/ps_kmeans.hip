@@ -19,6 +19,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 using namespace ps;
 
 // Tile shape of the assignment kernel: 16-token blocks per wave for K <= 64
@@ -1268,10 +1270,12 @@ extern "C" ps_status ps_workspace_size(const ps_shape* s, ps_dtype dtype, size_t
     return PS_OK;
 }
 
-extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void* H, const void* Kr,
-                                   ps_init init, int32_t iters, uint32_t flags, float* C, int32_t* assign,
-                                   int32_t* counts, float* row_norm, void* Ck, double* objective,
-                                   void* ws, size_t ws_bytes, void* stream)
+namespace {
+
+// every host-known check of a K-Means call except the workspace's
+ps_status kmeans_fit_check(const ps_shape* s, ps_dtype dtype, const void* H, const void* Kr, ps_init init,
+                           int32_t iters, uint32_t flags, const float* C, const int32_t* assign,
+                           const int32_t* counts, const float* row_norm, const void* Ck, const double* objective)
 {
     using namespace ps_host;
     if (!s || !H || !C || !assign || !counts || !row_norm) return PS_ERR_NULL;
@@ -1288,6 +1292,18 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
         !aligned16(row_norm) || (Kr && (!aligned16(Kr) || !aligned16(Ck))) ||
         (objective && !aligned16(objective)))
         return PS_ERR_ALIGN;
+    return PS_OK;
+}
+
+ps_status kmeans_fit_impl(const ps_shape* s, ps_dtype dtype, const void* H, const void* Kr, ps_init init,
+                          int32_t iters, uint32_t flags, float* C, int32_t* assign, int32_t* counts,
+                          float* row_norm, void* Ck, double* objective, void* ws, size_t ws_bytes,
+                          void* stream)
+{
+    using namespace ps_host;
+    ps_status st = kmeans_fit_check(s, dtype, H, Kr, init, iters, flags, C, assign, counts, row_norm, Ck,
+                                    objective);
+    if (st != PS_OK) return st;
     const KmWs need = km_layout(s, dtype, nullptr);
     if (!ws || ws_bytes < need.bytes) return PS_ERR_WORKSPACE;
     if (!aligned16(ws)) return PS_ERR_ALIGN;
@@ -1361,4 +1377,69 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
     if (objective)
         PS_LAUNCH("k_objective", k_objective, dim3((W + 63) / 64), dim3(64), 0, stm, L.nrm, objective, W, K);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void* H, const void* Kr,
+                                   ps_init init, int32_t iters, uint32_t flags, float* C, int32_t* assign,
+                                   int32_t* counts, float* row_norm, void* Ck, double* objective,
+                                   void* ws, size_t ws_bytes, void* stream)
+{
+    return kmeans_fit_impl(s, dtype, H, Kr, init, iters, flags, C, assign, counts, row_norm, Ck, objective, ws,
+                           ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the K-Means scratch lives in a file-scope device
+// array, one copy per device, whose device address is looked up once per
+// device (in host code the array's name is not a device address).  Every
+// kernel writes the scratch it later reads within the same call, so the
+// previous call's contents are never read; calls that overlap on one device
+// share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[PS_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// device address of `scratch` on the current device
+ps_status static_scratch(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return PS_ERR_DEVICE;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return PS_ERR_DEVICE;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PS_OK;
+}
+
+}  // namespace
+
+extern "C" ps_status ps_kmeans_fit_static(const ps_shape* s, ps_dtype dtype, const void* H, const void* Kr,
+                                          ps_init init, int32_t iters, uint32_t flags, float* C,
+                                          int32_t* assign, int32_t* counts, float* row_norm, void* Ck,
+                                          double* objective, void* stream)
+{
+    ps_status st = kmeans_fit_check(s, dtype, H, Kr, init, iters, flags, C, assign, counts, row_norm, Ck,
+                                    objective);
+    if (st != PS_OK) return st;
+    if (km_layout(s, dtype, nullptr).bytes > (size_t)PS_STATIC_SCRATCH_BYTES) return PS_ERR_SCRATCH_LIMIT;
+    if (s->W == 0) return PS_OK;
+    void* ws = nullptr;
+    if ((st = static_scratch(&ws)) != PS_OK) return st;
+    return kmeans_fit_impl(s, dtype, H, Kr, init, iters, flags, C, assign, counts, row_norm, Ck, objective, ws,
+                           (size_t)PS_STATIC_SCRATCH_BYTES, stream);
 }

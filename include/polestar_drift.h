@@ -54,8 +54,10 @@ typedef enum {
     PS_ERR_RANGE = 5,     /* a scalar argument is out of range (iters, k, ...) */
     PS_ERR_WORKSPACE = 6, /* ws is NULL or smaller than ps_workspace_size      */
     PS_ERR_DEVICE = 7,    /* a HIP launch or runtime call failed               */
-    PS_ERR_MEMORY = 8     /* a pointer the GPU must read is neither device
+    PS_ERR_MEMORY = 8,    /* a pointer the GPU must read is neither device
                              memory nor pinned host memory mapped for it   */
+    PS_ERR_SCRATCH_LIMIT = 9  /* the shape needs more scratch than the
+                             static scratch of ps_kmeans_fit_static holds  */
 } ps_status;
 
 typedef enum { PS_F32 = 0, PS_BF16 = 1 } ps_dtype;
@@ -132,6 +134,30 @@ ps_status ps_kmeans_fit(const ps_shape* shape, ps_dtype dtype, const void* H, co
                         int32_t* counts,
                         float* row_norm, void* Ck, double* objective, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* Bytes of the library's static K-Means scratch, one copy per device. */
+#define PS_STATIC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * ps_kmeans_fit_static -- ps_kmeans_fit for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation and results, with the
+ * scratch taken from a static device array of PS_STATIC_SCRATCH_BYTES that
+ * the library holds on each device it runs on until the process ends.  The
+ * call allocates and frees nothing; the caller still passes every input and
+ * output.  A shape whose ps_kmeans_fit workspace would exceed that size
+ * (ps_workspace_size gives the larger of two needs; this call needs only
+ * the K-Means part, e.g. about 2.1 MiB per window of 8192 rows x 4096 with
+ * 256 clusters, 0.55 MiB per window of 1024 rows x 4096 with 64) returns
+ * PS_ERR_SCRATCH_LIMIT before anything is enqueued.  Every call on a device
+ * uses that device's one array: calls that overlap on one device (several
+ * streams or threads at once) race, so a caller serialises them.  Other
+ * arguments, limits and errors as ps_kmeans_fit.
+ */
+ps_status ps_kmeans_fit_static(const ps_shape* shape, ps_dtype dtype, const void* H, const void* Kr,
+                               ps_init init, int32_t iters, uint32_t flags, float* C, int32_t* assign,
+                               int32_t* counts, float* row_norm, void* Ck, double* objective,
+                               void* stream);
 
 /*
  * ps_residual_nvfp4 -- NVFP4 coding of each row's residual to its centre

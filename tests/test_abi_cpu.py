@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIBPATH = os.path.join(ROOT, "drift_aware_kv_amd", "libpolestar_drift.so")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, RANGE, WORKSPACE, DEVICE, MEMORY = range(9)
+OK, NULL, SHAPE, DTYPE, ALIGN, RANGE, WORKSPACE, DEVICE, MEMORY, SCRATCH_LIMIT = range(10)
 
 
 def declared_functions():
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_status_strings(L):
     import drift_aware_kv_amd as P
-    for st in range(9):
+    for st in range(10):
         assert P.status_string(st).startswith("PS_")
     assert "unknown" in P.status_string(99)
 
@@ -108,6 +108,33 @@ def test_kmeans_fit_argument_checks(L):
     assert _fit(L, s, ws_bytes=16) == WORKSPACE
     # W = 0 is a valid no-op and enqueues nothing
     assert _fit(L, _shape(W=0)) == OK
+
+
+def _fit_static(L, shape, dtype=1, H=FAKE, Kr=None, init=1, iters=2, C=FAKE, Ck=None, flags=0):
+    return L.ps_kmeans_fit_static(ctypes.byref(shape), dtype, H, Kr, init, iters, flags, C, FAKE, FAKE, FAKE,
+                                  Ck, None, None)
+
+
+def test_kmeans_fit_static_argument_checks(L):
+    """The allocation-free variant checks the same arguments before it looks
+    up its scratch, and refuses a shape whose K-Means scratch exceeds the
+    static array (512 windows of 1024 x 4096 with 64 clusters need 256 MiB of
+    bf16 centres alone)."""
+    import drift_aware_kv_amd as P
+    s = _shape()
+    assert _fit_static(L, s, H=None) == NULL
+    assert _fit_static(L, s, Kr=FAKE, Ck=None) == NULL
+    assert _fit_static(L, s, dtype=3) == DTYPE
+    assert _fit_static(L, _shape(K=65)) == SHAPE
+    assert _fit_static(L, s, iters=0) == RANGE
+    assert _fit_static(L, s, H=MISALIGNED) == ALIGN
+    big = _shape(W=512, N=1024, d=4096, K=64)
+    assert _fit_static(L, big) == SCRATCH_LIMIT
+    n = ctypes.c_size_t(0)
+    assert L.ps_workspace_size(ctypes.byref(big), 1, ctypes.byref(n)) == OK
+    assert n.value > P.PS_STATIC_SCRATCH_BYTES
+    assert "static scratch" in P.status_string(SCRATCH_LIMIT)
+    assert _fit_static(L, _shape(W=0)) == OK       # nothing to do: no device touched
 
 
 def test_residual_argument_checks(L):
