@@ -64,9 +64,14 @@ def kernel_work(name, cfg, gathered=None):
         return W * N * KV * e + W * N * 4 + W * K * KV * e, W * N * KV * 1.0
     if name.startswith("k_proxy"):
         # Q and the keys read, log-probabilities written, and (after window
-        # formation, the drift fused into the epilogue) the previous step's read
-        return (W * cfg.Nb * cfg.Hq * cfg.dh * e + W * K * KV * e + 2 * L * 4,
+        # formation, the drift fused into the epilogue) the previous step's
+        # read; the head-parallel form leaves the drift to k_drift_kl
+        prev = 0 if name.endswith("/heads") else L * 4
+        return (W * cfg.Nb * cfg.Hq * cfg.dh * e + W * K * KV * e + L * 4 + prev,
                 2.0 * W * cfg.Hq * cfg.Nb * K * cfg.dh)
+    if name.startswith("k_drift_scores"):
+        # both distributions and the rows' drifts read, scores and D_i written
+        return 2 * L * 4 + W * cfg.Hq * cfg.Nb * 4 + W * (K + cfg.Nb) * 4, L * 4.0
     if name.startswith("k_drift_kl"):
         return 2 * L * 4 + W * (cfg.Hq * cfg.Nb + cfg.Nb + K) * 4, L * 4.0
     if name.startswith("k_bucket"):
@@ -116,31 +121,39 @@ def compulsory_work(cfg, gathered):
 
 
 PROFILES = os.path.join(HERE, "profiles")
-KERNEL_SOURCES = [os.path.join(HERE, "drift_aware_kv_amd", "csrc", f)
-                  for f in ("ps_kmeans.hip", "ps_common.h")]
+CSRC = os.path.join(HERE, "drift_aware_kv_amd", "csrc")
+DEFAULT_SOURCES = ("ps_kmeans.hip", "ps_common.h")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=DEFAULT_SOURCES):
+    """SHA-256 of the given kernel source files (under csrc/), in order."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+    for f in sources:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
 
 
 def recorded_traffic(kernel_name, cfg_name):
-    """HBM bytes per launch of a K-Means kernel from the committed rocprofv3
-    counter summaries (profiles/traffic_*.txt), if one was taken on this
-    kernel source, kernel and workload; else None."""
+    """HBM bytes per launch of a library kernel from the committed rocprofv3
+    counter summaries (profiles/traffic_*.txt), if one was taken on the
+    current text of the sources it names (`sources=`, default the K-Means
+    source and the shared header), on this kernel and workload; else None."""
     import glob
-    src = kernel_source_hash()
     for path in sorted(glob.glob(os.path.join(PROFILES, "traffic_*.txt"))):
         try:
             kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
         except (OSError, ValueError):
             continue
-        if kv.get("source_sha256") == src and kv.get("workload") == cfg_name and kv.get("kernel") == kernel_name:
-            return float(kv["traffic_bytes_per_launch"])
+        if kv.get("workload") != cfg_name or kv.get("kernel") != kernel_name:
+            continue
+        sources = tuple(x for x in kv.get("sources", ",".join(DEFAULT_SOURCES)).split(",") if x)
+        try:
+            if kv.get("source_sha256") != kernel_source_hash(sources):
+                continue
+        except OSError:
+            continue
+        return float(kv["traffic_bytes_per_launch"])
     return None
 
 
@@ -395,20 +408,29 @@ def kernel_figures(cfg, prof, steps, gathered, ms_per_step):
     figures against the compulsory work, from the kernel timer's summary of
     the timed steps."""
     kernels = {k: v for k, v in prof.items() if not k.startswith("#")}
+
+    def done(v):
+        """Part of its launches' work a kernel did: the Lloyd passes skip the
+        windows at a fixed point and count the tiles they process."""
+        return v[4] / v[5] if len(v) > 5 and v[5] else 1.0
+
     breakdown = {}
     for k, v in sorted(kernels.items(), key=lambda kv: -kv[1][1]):
         breakdown[k] = {"launches": v[0], "avg_ms": v[1] / v[0], "total_ms_per_step": v[1] / steps}
+        if len(v) > 5 and v[5]:
+            breakdown[k]["work_fraction"] = done(v)
         work = kernel_work(k, cfg, gathered)
         if work and not k.startswith("k_update"):   # the update's later passes re-sum dirty clusters only
-            breakdown[k]["algorithmic_GB_per_launch"] = work[0] / 1e9
-            breakdown[k]["achieved_GBs"] = work[0] / (v[1] / v[0] * 1e-3) / 1e9
+            breakdown[k]["algorithmic_GB_per_launch"] = work[0] * done(v) / 1e9
+            breakdown[k]["achieved_GBs"] = work[0] * done(v) / (v[1] / v[0] * 1e-3) / 1e9
     roof = None
     if kernels:
-        name, (n, tot, mn, mx) = max(kernels.items(), key=lambda kv: kv[1][1])
+        name, v = max(kernels.items(), key=lambda kv: kv[1][1])
+        n, tot = v[0], v[1]
         work = kernel_work(name, cfg, gathered)
         avg_s = tot / n / 1e3
         if work:
-            byts, flops = work
+            byts, flops = work[0] * done(v), work[1] * done(v)
             ai = flops / byts
             if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
                 ach = flops / avg_s / 1e12
@@ -419,24 +441,32 @@ def kernel_figures(cfg, prof, steps, gathered, ms_per_step):
                 roof = {"kernel": name, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
             roof.update({"algorithmic_bytes_per_launch": byts, "flops_per_launch": flops,
-                         "avg_launch_ms": avg_s * 1e3, "launches": n,
+                         "avg_launch_ms": avg_s * 1e3, "launches": n, "work_fraction": done(v),
                          "mfma_frac": flops / avg_s / 1e12 / BF16_PEAK_TFLOPS})
-            roof["traffic"] = recorded_traffic(name, cfg.name)
+            # the counters were taken with every launch doing its full work
+            roof["traffic"] = recorded_traffic(name, cfg.name) if done(v) == 1.0 else None
     # the whole step against the method's compulsory bytes and flops (H read
     # once per step); the bytes the kernels move by their own accounting (H
     # streamed once per Lloyd pass, by the coder, ...) are given beside it
+    # (with the fixed-point exit the flops are those of the passes that ran,
+    # counted by the Lloyd kernels, not the full iters x 2NKd)
     cb, cf = compulsory_work(cfg, gathered)
     t = ms_per_step * 1e-3
-    hbm, mfma = cb / t / 1e9 / HBM_PEAK_GBS, cf / t / 1e12 / BF16_PEAK_TFLOPS
-    moved = 0.0
-    for kname, (n, tot, mn, mx) in kernels.items():
+    moved, ran = 0.0, 0.0
+    for kname, v in kernels.items():
         work = kernel_work(kname, cfg, gathered)
         if work:
-            moved += work[0] * (steps if kname.startswith("k_update") else n)
+            moved += work[0] * (steps if kname.startswith("k_update") else v[0] * done(v))
+            if kname.startswith("k_assign") or kname.startswith("k_proxy"):
+                ran += work[1] * v[0] * done(v)
+    ran = ran / steps if kernels else cf
+    hbm, mfma = cb / t / 1e9 / HBM_PEAK_GBS, ran / t / 1e12 / BF16_PEAK_TFLOPS
+    t_roof = max(ran / (BF16_PEAK_TFLOPS * 1e12), cb / (HBM_PEAK_GBS * 1e9))
     step_roof = {"compulsory_bytes_per_step": cb, "compulsory_flops_per_step": cf,
-                 "bound": "mfma" if cf / (BF16_PEAK_TFLOPS * 1e12) > cb / (HBM_PEAK_GBS * 1e9) else "hbm",
-                 "hbm_frac": hbm, "mfma_frac": mfma, "frac": max(hbm, mfma),
-                 "roofline_ms_per_step": 1e3 * max(cf / (BF16_PEAK_TFLOPS * 1e12), cb / (HBM_PEAK_GBS * 1e9)),
+                 "executed_flops_per_step": ran,
+                 "bound": "mfma" if ran / (BF16_PEAK_TFLOPS * 1e12) > cb / (HBM_PEAK_GBS * 1e9) else "hbm",
+                 "hbm_frac": hbm, "mfma_frac": mfma, "frac": t_roof / t,
+                 "roofline_ms_per_step": 1e3 * t_roof,
                  "kernel_bytes_per_step": moved / steps if kernels else None}
     return roof, step_roof, breakdown
 
@@ -502,8 +532,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the secondary figure on the 512-window LLaDA-8B batch")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timer")
-    ap.add_argument("--no-fixed-point", action="store_true",
-                    help="skip the secondary timing with the exact fixed-point exit")
+    ap.add_argument("--no-all-passes", action="store_true",
+                    help="skip the secondary timing with every Lloyd pass of every window run in full")
     ap.add_argument("--cluster-score", default="kl", choices=["kl", "cosine"],
                     help="rank clusters by drift share (the method) or by centre movement "
                          "(the cosine-dissimilarity variant)")
@@ -579,17 +609,21 @@ def main():
         nxt += args.steps
         untimed = {"ms_per_step": 1e3 * u_el / args.steps, "value": args.steps * cfg.W * cfg.N / u_el}
 
-    # secondary figure: the same steps with the exact fixed-point exit (Lloyd
-    # passes after the first that moves no row are skipped per window; the
-    # results are bit-identical to running every pass)
-    fpx = None
-    if not args.no_fixed_point:
-        path.spec.kmeans_flags = P.PS_KMEANS_FIXED_POINT_EXIT
-        f_el, _, _ = timed_steps(path, wl, nxt, args.steps, False)
+    # secondary figure: the same steps with every Lloyd pass of every window
+    # run in full (the headline skips a window's passes after one that moves
+    # no row; the results are bit-identical), with its own kernel table
+    allp = None
+    if not args.no_all_passes:
+        path.spec.kmeans_flags = P.PS_KMEANS_ALL_PASSES
+        a_el, a_ms, a_prof = timed_steps(path, wl, nxt, args.steps, not args.no_profile,
+                                         64 * args.steps * (cfg.iters + 8))
         nxt += args.steps
-        path.spec.kmeans_flags = 0
-        fpx = {"value": args.steps * cfg.W * cfg.N / f_el, "ms_per_step": 1e3 * f_el / args.steps}
-        print(f"[bench] fixed-point exit: {fpx['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+        path.spec.kmeans_flags = P.PS_KMEANS_DEFAULT
+        a_roof, a_step, a_kern = kernel_figures(cfg, a_prof, args.steps, gathered, 1e3 * a_el / args.steps)
+        allp = {"value": args.steps * cfg.W * cfg.N / a_el, "ms_per_step": 1e3 * a_el / args.steps,
+                "roofline": a_roof, "step_roofline": a_step,
+                "kernels_ms_per_step": {k: v["total_ms_per_step"] for k, v in a_kern.items()}}
+        print(f"[bench] every Lloyd pass in full: {allp['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
 
     # secondary figure: the same steps replayed from HIP graphs (one graph per
     # input snapshot and step parity, captured in two untimed passes)
@@ -666,6 +700,8 @@ def main():
         "config": {"workload": cfg.name, "windows": cfg.W, "window_tokens": cfg.N, "hidden": cfg.d,
                    "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.dh, "block": cfg.Nb,
                    "clusters": cfg.K, "top_k": cfg.k, "lloyd_iters": cfg.iters,
+                   "lloyd_exit": "a window's passes after one that moves no row are skipped (results "
+                                 "bit-identical to running every pass; all_lloyd_passes times that)",
                    "drift": f"{cfg.drift} {cfg.drift_frac:.0%} rows x {cfg.drift_mag}",
                    "cluster_score": args.cluster_score, "residual_store": args.residual_store,
                    "commit": {"alpha": spec.alpha, "tau_s": spec.tau_s,
@@ -677,7 +713,7 @@ def main():
         "secondary": secondary,
         "measured_ceilings": measured,
         "without_kernel_timer": untimed,
-        "fixed_point_exit": fpx,
+        "all_lloyd_passes": allp,
         "graph_replay": graphed,
         "scoring_only": scoring,
         "step_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1]},

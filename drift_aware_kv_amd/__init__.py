@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(HERE, "libpolestar_drift.so")
 PS_F32, PS_BF16 = 0, 1
 PS_INIT_GIVEN, PS_INIT_STRIDED, PS_INIT_FARTHEST = 0, 1, 2
 PS_SCORE_KL_SHARE, PS_SCORE_KL_SHARE_ABS, PS_SCORE_ATTN_WEIGHTED = 0, 1, 2
-PS_KMEANS_DEFAULT, PS_KMEANS_FIXED_POINT_EXIT = 0, 1
+PS_KMEANS_DEFAULT, PS_KMEANS_FIXED_POINT_EXIT, PS_KMEANS_ALL_PASSES = 0, 1, 2
 PS_ERR_SCRATCH_LIMIT = 9
 PS_STATIC_SCRATCH_BYTES = 64 << 20     # the library's static K-Means scratch per device
 
@@ -104,7 +104,10 @@ def profile_end():
 
 
 def profile_summary():
-    """{kernel name: (launches, total_ms, min_ms, max_ms)}, plus '#dropped'."""
+    """{kernel name: (launches, total_ms, min_ms, max_ms, units_done, units)},
+    plus '#dropped'.  units is the work of the kernel's launches in the units
+    it counts (tiles, rows, clusters) and units_done the part it processed; both
+    0 for kernels whose launches always do their full work."""
     buf = ctypes.create_string_buffer(1 << 16)
     _check(lib().ps_profile_summary(buf, len(buf)), "ps_profile_summary")
     out = {}
@@ -112,8 +115,8 @@ def profile_summary():
         f = line.split("\t")
         if f[0] == "#dropped":
             out["#dropped"] = int(f[1])
-        elif len(f) == 5:
-            out[f[0]] = (int(f[1]), float(f[2]), float(f[3]), float(f[4]))
+        elif len(f) == 7:
+            out[f[0]] = (int(f[1]), float(f[2]), float(f[3]), float(f[4]), int(f[5]), int(f[6]))
     return out
 
 

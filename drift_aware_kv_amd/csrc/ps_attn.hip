@@ -35,7 +35,11 @@ __device__ __forceinline__ float score_term(int kind, float p, float t, float D)
 // queries (shuffles) and waves (LDS) in a fixed order.  With several groups a
 // running max and sum are kept across groups, the raw logits are parked in
 // the output row and rebased in a second pass by the lane that wrote them, and
-// the drift runs as a separate pass (fused = 0).
+// the drift runs as a separate pass (fused = 0).  With hsplit the grid has a
+// second dimension over groups of four heads and every wave computes one head
+// of its window; the per-cluster scores sum over all heads, so there the
+// kernel stops at each row's drift D_{h,i} (fused = 2, written to D_hi) and
+// k_drift_scores adds the scores up.
 // ---------------------------------------------------------------------------
 template <int KB, int NBQ>
 __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__ Q,
@@ -43,7 +47,7 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
                                                      float* __restrict__ logp, const float* __restrict__ prev,
                                                      int kind, int fused, float* __restrict__ D_hi,
                                                      float* __restrict__ D_i, float* __restrict__ score,
-                                                     int Hq, int Hkv, int dh, int Nb, int K)
+                                                     int Hq, int Hkv, int dh, int Nb, int K, int hsplit)
 {
     constexpr int GK = 16 * KB;
     __shared__ float sred[4][GK];
@@ -70,7 +74,9 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
     // where used
     constexpr bool kEarlyPrev = KB * NBQ <= 8;
     const bool early = kEarlyPrev && fused && prev != nullptr && ngroups == 1;
-    for (int h = wave; h < Hq; h += 4) {
+    const int h0 = hsplit ? 4 * (int)blockIdx.y + wave : wave;
+    const int hstep = hsplit ? Hq : 4;
+    for (int h = h0; h < Hq; h += hstep) {
         const int g = h / G;
         float M[NBQ], S[NBQ];
 #pragma unroll
@@ -235,10 +241,13 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
                     if (prev) {
                         D = tsum + __shfl_xor(tsum, 16, 64);
                         D = D + __shfl_xor(D, 32, 64);
+                        if (fused == 1) {
 #pragma unroll
-                        for (int mb = 0; mb < KB; ++mb)
+                            for (int mb = 0; mb < KB; ++mb)
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) sacc[mb][r] += score_term(kind, pv[mb][r], tv[mb][r], D);
+                                for (int r = 0; r < 4; ++r)
+                                    sacc[mb][r] += score_term(kind, pv[mb][r], tv[mb][r], D);
+                        }
                     }
                     if (iv) {
                         dacc[nb] += D;
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
             }
         }
     }
-    if (!fused) return;
+    if (fused != 1) return;
     // scores: sum over the 16 query lanes, then over the four waves in order
 #pragma unroll
     for (int mb = 0; mb < KB; ++mb)
@@ -794,6 +803,60 @@ __global__ __launch_bounds__(256) void k_drift_kl(const float* __restrict__ cur,
         score[(size_t)w * K + k] = (((sp[k] + sp[K + k]) + sp[2 * K + k]) + sp[3 * K + k]) * invH;
 }
 
+// ---------------------------------------------------------------------------
+// per-cluster scores and per-token drift from stored distributions and the
+// per-row drifts D_hi (which the head-parallel proxy kernel writes): grid
+// (W, K / 64), lane l of every wave owns cluster 64 blockIdx.y + l, wave v
+// the rows (h, i) = v, v + 4, ... in order (8 rows' loads in flight), the four
+// waves' sums combined in order; blockIdx.y == 0 also averages D_hi over the
+// heads for D_i.  The order of every sum depends on the shape only.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_drift_scores(const float* __restrict__ cur,
+                                                       const float* __restrict__ prev,
+                                                       const float* __restrict__ D_hi, int kind,
+                                                       float* __restrict__ D_i, float* __restrict__ score,
+                                                       int Hq, int Nb, int K)
+{
+    __shared__ float part[4][64];
+    const int w = blockIdx.x, lane = lane_id(), wave = threadIdx.x >> 6;
+    const int k = 64 * (int)blockIdx.y + lane;
+    const bool kv = k < K;
+    const int kc = kv ? k : K - 1;
+    const int rows = Hq * Nb;
+    const size_t base = (size_t)w * rows * K;
+    const float* Dw = D_hi + (size_t)w * rows;
+    float acc = 0.0f;
+    constexpr int U = 8;
+    for (int r0 = wave; r0 < rows; r0 += 4 * U) {
+        float lc[U], lp[U], dv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = min(r0 + 4 * u, rows - 1);
+            lc[u] = cur[base + (size_t)r * K + kc];
+            lp[u] = prev[base + (size_t)r * K + kc];
+            dv[u] = Dw[r];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (r0 + 4 * u >= rows) break;
+            const float p = exp_hw(lc[u]);
+            acc += score_term(kind, p, p * (lc[u] - lp[u]), dv[u]);
+        }
+    }
+    part[wave][lane] = acc;
+    __syncthreads();
+    const float invH = 1.0f / (float)Hq;
+    if (threadIdx.x < 64 && kv)
+        score[(size_t)w * K + k] = (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) * invH;
+    if (blockIdx.y == 0) {
+        for (int i = threadIdx.x; i < Nb; i += 256) {
+            float sum = 0.0f;
+            for (int h = 0; h < Hq; ++h) sum += Dw[h * Nb + i];
+            D_i[(size_t)w * Nb + i] = sum * invH;
+        }
+    }
+}
+
 // Cosine-dissimilarity drift of each cluster: one wave per (window, cluster),
 // 16-byte loads of both unit centres, products and sums in fp64 (each fp32
 // product is exact in fp64), one wave reduction, then 1 - dot rounded once.
@@ -938,10 +1001,18 @@ int attn_device_cus()
 // kernel at K = 64, dh = 128 when its two waves per window give every SIMD
 // a wave (four per compute unit); with fewer windows, or other shapes whose
 // operands fit, the four-wave pipelined kernel; otherwise k_proxy_bf16.
+// Above 64 clusters (hsplit) every (window, head) gets its own wave and the
+// drift follows in its own pass, whatever the number of windows.
 template <int KB, int NBQ>
 void launch_proxy(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, const float* prev,
                   int kind, int fused, float* D_hi, float* D_i, float* score, hipStream_t st)
 {
+    if (fused != 1) {
+        PS_LAUNCH("k_proxy_bf16<KB, NBQ>/heads", (k_proxy_bf16<KB, NBQ>), dim3(s->W, (s->Hq + 3) / 4), dim3(256), 0,
+                  st, (const uint16_t*)Q, (const uint16_t*)Ck, sigma, logp, prev, kind, fused, D_hi, D_i, score,
+                  s->Hq, s->Hkv, s->dh, s->Nb, s->K, 1);
+        return;
+    }
     if constexpr (KB == 4 && NBQ <= 2) {
         if (fused && prev && s->dh == 128 && s->K == 64 && 2 * (int64_t)s->W >= 4 * (int64_t)attn_device_cus()) {
             PS_LAUNCH("k_proxy_rows<NBQ>", k_proxy_rows<NBQ>, dim3(s->W), dim3(128), 0, st, (const uint16_t*)Q,
@@ -959,7 +1030,7 @@ void launch_proxy(const ps_shape* s, const void* Q, const void* Ck, float sigma,
     }
     PS_LAUNCH("k_proxy_bf16<KB, NBQ>", (k_proxy_bf16<KB, NBQ>), dim3(s->W), dim3(256), 0, st, (const uint16_t*)Q,
               (const uint16_t*)Ck, sigma, logp, prev, kind, fused, D_hi, D_i, score, s->Hq, s->Hkv, s->dh, s->Nb,
-              s->K);
+              s->K, 0);
 }
 
 template <int KB>
@@ -1046,11 +1117,22 @@ extern "C" ps_status ps_proxy_attn(const ps_shape* s, ps_dtype dtype, const void
     if (s->W == 0) return PS_OK;
     hipStream_t stm = (hipStream_t)stream;
     (void)hipGetLastError();
-    bool fused = false;
+    bool fused = false, heads = false, rowdrift = false;
     if (dtype == PS_BF16) {
         const int kb = (s->K + 15) / 16;
-        fused = kb <= 16;  // one cluster group: drift in the epilogue
-        const int f = fused ? 1 : 0;
+        // Up to 64 clusters the drift is fused into one workgroup per window.
+        // Above, the (window, head) pairs spread over the device, each wave
+        // writing its rows' drifts to D_hi, and k_drift_scores adds up the
+        // scores (the one-workgroup form leaves most compute units idle
+        // there); without D_hi to hold the rows' drifts, the fused form up to
+        // 256 clusters, and above 256 clusters (several cluster groups, whose
+        // rows are finished only after all groups) a drift pass of its own.
+        // The choice depends on the shape and on D_hi only, never on the
+        // number of windows.
+        heads = kb > 4 && (!logp_prev || D_hi || kb > 16);
+        rowdrift = heads && logp_prev && kb <= 16;
+        fused = !heads && kb <= 16;
+        const int f = rowdrift ? 2 : (fused ? 1 : 0);
         const int k = (int)kind;
         if (kb <= 1)       launch_proxy_nb<1>(s, Q, Ck, softmax_scale, logp_cur, logp_prev, k, f, D_hi, D_i, score, stm);
         else if (kb <= 2)  launch_proxy_nb<2>(s, Q, Ck, softmax_scale, logp_cur, logp_prev, k, f, D_hi, D_i, score, stm);
@@ -1063,7 +1145,10 @@ extern "C" ps_status ps_proxy_attn(const ps_shape* s, ps_dtype dtype, const void
                   (const float*)Ck, softmax_scale, logp_cur, s->Hq, s->Hkv, s->dh, s->Nb, s->K);
     }
     if (!fused) {
-        if (logp_prev) {
+        if (rowdrift) {
+            PS_LAUNCH("k_drift_scores", k_drift_scores, dim3(s->W, (s->K + 63) / 64), dim3(256), 0, stm, logp_cur,
+                      logp_prev, D_hi, (int)kind, D_i, score, s->Hq, s->Nb, s->K);
+        } else if (logp_prev) {
             enqueue_drift(s, logp_cur, logp_prev, kind, D_hi, D_i, score, stm);
         } else {
             enqueue_zero(D_i, (size_t)s->W * s->Nb, stm);

@@ -35,6 +35,7 @@ using namespace ps;
 #define PS_ASSIGN_DK 64
 #endif
 
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
                                                       float* __restrict__ row_norm, int N, int d,
                                                       int K, int tiles, int nblocks,
                                                       int32_t* __restrict__ dirty,
-                                                      const int32_t* __restrict__ conv)
+                                                      const int32_t* __restrict__ conv, int* __restrict__ work)
 {
     constexpr int DK = PS_ASSIGN_DK;       // d elements per LDS stage
     constexpr int NS = DK / 32;            // MFMA k-steps per stage
@@ -193,6 +194,7 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int w = L / tiles, tile = L - w * tiles;
     if (!FIRST && conv[w]) return;  // window at a fixed point: nothing can change
+    if (work && threadIdx.x == 0) atomicAdd(work, 1);   // kernel timer: one tile processed
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const uint16_t* Hw = H + (size_t)w * N * d;
@@ -386,13 +388,14 @@ __global__ __launch_bounds__(512) void k_assign_wide(const uint16_t* __restrict_
                                                       int32_t* __restrict__ assign,
                                                       float* __restrict__ row_norm, int N, int d, int K,
                                                       int tiles, int nblocks, int32_t* __restrict__ dirty,
-                                                      const int32_t* __restrict__ conv)
+                                                      const int32_t* __restrict__ conv, int* __restrict__ work)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t wlds[];
     constexpr int NS = kWideDK / 32;
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int w = L / tiles, tile = L - w * tiles;
     if (!FIRST && conv[w]) return;  // window at a fixed point: nothing can change
+    if (work && threadIdx.x == 0) atomicAdd(work, 1);   // kernel timer: one tile processed
     const int tid = threadIdx.x, lane = lane_id(), v = tid >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const int cq = v & 3, th = v >> 2;
@@ -600,7 +603,7 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
                                                           int32_t* __restrict__ assign,
                                                           float* __restrict__ row_norm, int N, int d, int K,
                                                           int tiles, int nblocks, int32_t* __restrict__ dirty,
-                                                          const int32_t* __restrict__ conv)
+                                                          const int32_t* __restrict__ conv, int* __restrict__ work)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t wlds[];
     uint8_t* const tbufs = wlds;                                  // [3][256 rows][128 B]
@@ -608,6 +611,7 @@ __global__ __launch_bounds__(512) void k_assign_wide_dma(const uint16_t* __restr
     const int L = xcd_remap(blockIdx.x, nblocks);
     const int w = L / tiles, tile = L - w * tiles;
     if (!FIRST && conv[w]) return;  // window at a fixed point: nothing can change
+    if (work && threadIdx.x == 0) atomicAdd(work, 1);   // kernel timer: one tile processed
     const int tid = threadIdx.x, lane = lane_id(), v = tid >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const int cq = v & 3, th = v >> 2;
@@ -803,12 +807,16 @@ __global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ H,
                                                      int32_t* __restrict__ assign,
                                                      float* __restrict__ row_norm, int W, int N, int d,
                                                      int K, int first, int32_t* __restrict__ dirty,
-                                                     const int32_t* __restrict__ conv)
+                                                     const int32_t* __restrict__ conv, int* __restrict__ work)
 {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (row >= (int64_t)W * N) return;
-    const int w = (int)(row / N);
-    if (!first && conv[w]) return;
+    const int w = (int)(min(row, (int64_t)W * N - 1) / N);
+    const bool active = row < (int64_t)W * N && (first || !conv[w]);
+    if (work) {   // kernel timer: rows processed
+        const uint64_t b = __ballot(active);
+        if (lane_id() == 0 && b) atomicAdd(work, __popcll(b));
+    }
+    if (!active) return;
     const float* h = H + (size_t)row * d;
     const float* Cw = C + (size_t)w * K * d;
     float bestv = -INFINITY;
@@ -836,9 +844,9 @@ __global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ H,
 // ---------------------------------------------------------------------------
 // bucket: stable counting sort of rows by cluster, one wave per window.
 // After the first iteration, a window none of whose clusters changed keeps its
-// member lists (they are a function of the unchanged assignment); with the
-// fixed-point exit enabled it is also marked converged, which makes every
-// later assignment pass of that window a no-op (the iteration would reproduce
+// member lists (they are a function of the unchanged assignment) and, unless
+// every pass is to run in full, is marked converged, which makes every later
+// assignment pass of that window a no-op (the iteration would reproduce
 // exactly the same centres and assignments).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_bucket(const int32_t* __restrict__ assign, int32_t* __restrict__ perm,
@@ -1007,13 +1015,14 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
                                                  const int32_t* __restrict__ offs, float* __restrict__ C,
                                                  uint16_t* __restrict__ Cb, int32_t* __restrict__ counts,
                                                  double* __restrict__ nrm_out, int32_t* __restrict__ dirty,
-                                                 int N, int d, int K, int nblocks, int all)
+                                                 int N, int d, int K, int nblocks, int all, int* __restrict__ work)
 {
     __shared__ double red[4];
     const int Lg = xcd_remap(blockIdx.x, nblocks);
     const int w = Lg / K, k = Lg - w * K;
     // an unchanged member set gives a bit-identical sum: keep the centre
     if (!all && !dirty[(size_t)w * K + k]) return;
+    if (work && threadIdx.x == 0) atomicAdd(work, 1);   // kernel timer: one cluster re-summed
     const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
     const int32_t* pm = perm + (size_t)w * N;
     const T* Hw = H + (size_t)w * N * d;
@@ -1173,8 +1182,8 @@ void launch_update(const ps_shape* s, const void* H, const float* rn, const KmWs
                    int32_t* counts, int all, hipStream_t st)
 {
     const int nblocks = s->W * s->K;
-    PS_LAUNCH("k_update<T, CH>", (k_update<T, CH>), dim3(nblocks), dim3(256), 0, st, (const T*)H, rn, ws.perm,
-                       ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, s->N, s->d, s->K, nblocks, all);
+    PS_LAUNCH_COUNTED("k_update<T, CH>", nblocks, (k_update<T, CH>), dim3(nblocks), dim3(256), 0, st, (const T*)H,
+                      rn, ws.perm, ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, s->N, s->d, s->K, nblocks, all);
 }
 
 template <bool FIRST>
@@ -1196,20 +1205,23 @@ void launch_assign_wide(const ps_shape* s, const void* H, const KmWs& ws, int32_
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds) == hipSuccess &&
                       hipFuncSetAttribute((const void*)k_assign_wide<false>,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds) == hipSuccess;
-        dma_ok[dev] = hipFuncSetAttribute((const void*)k_assign_wide_dma<FIRST>,
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDmaLds) == hipSuccess
+        const int lds = (int)kDmaLds;
+        dma_ok[dev] = hipFuncSetAttribute((const void*)k_assign_wide_dma<true>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess &&
+                      hipFuncSetAttribute((const void*)k_assign_wide_dma<false>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess
                           ? 1 : -1;
         (void)hipGetLastError();
     }
     if (s->d % kDmaDK == 0 && known && dma_ok[dev] == 1) {
-        PS_LAUNCH(FIRST ? "k_assign_wide_dma<true>" : "k_assign_wide_dma<false>", k_assign_wide_dma<FIRST>,
-                  dim3(nblocks), dim3(512), kDmaLds, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K,
-                  tiles, nblocks, ws.dirty, ws.conv);
+        PS_LAUNCH_COUNTED(FIRST ? "k_assign_wide_dma<true>" : "k_assign_wide_dma<false>", nblocks,
+                          k_assign_wide_dma<FIRST>, dim3(nblocks), dim3(512), kDmaLds, st, (const uint16_t*)H, ws.Cb,
+                          assign, rn, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
         return;
     }
-    PS_LAUNCH(FIRST ? "k_assign_wide<true>" : "k_assign_wide<false>", k_assign_wide<FIRST>, dim3(nblocks),
-              dim3(512), kWideLds, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks,
-              ws.dirty, ws.conv);
+    PS_LAUNCH_COUNTED(FIRST ? "k_assign_wide<true>" : "k_assign_wide<false>", nblocks, k_assign_wide<FIRST>,
+                      dim3(nblocks), dim3(512), kWideLds, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d,
+                      s->K, tiles, nblocks, ws.dirty, ws.conv);
 }
 
 template <int KB, int NB>
@@ -1219,12 +1231,13 @@ void launch_assign_bf16(const ps_shape* s, const void* H, const float* C, const 
     const int tiles = (s->N + 64 * NB - 1) / (64 * NB);
     const int nblocks = s->W * tiles;
     if (first)
-        PS_LAUNCH("k_assign_bf16<KB, NB, true>", (k_assign_bf16<KB, NB, true>), dim3(nblocks), dim3(256), 0, st,
-                  (const uint16_t*)H, (const void*)C, assign, rn, s->N, s->d, s->K, tiles, nblocks, ws.dirty,
-                  ws.conv);
+        PS_LAUNCH_COUNTED("k_assign_bf16<KB, NB, true>", nblocks, (k_assign_bf16<KB, NB, true>), dim3(nblocks),
+                          dim3(256), 0, st, (const uint16_t*)H, (const void*)C, assign, rn, s->N, s->d, s->K, tiles,
+                          nblocks, ws.dirty, ws.conv);
     else
-        PS_LAUNCH("k_assign_bf16<KB, NB, false>", (k_assign_bf16<KB, NB, false>), dim3(nblocks), dim3(256), 0, st,
-                  (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
+        PS_LAUNCH_COUNTED("k_assign_bf16<KB, NB, false>", nblocks, (k_assign_bf16<KB, NB, false>), dim3(nblocks),
+                          dim3(256), 0, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks,
+                          ws.dirty, ws.conv);
 }
 
 // compute units of the current device (cached per device; 256 if unknown)
@@ -1286,7 +1299,8 @@ ps_status kmeans_fit_check(const ps_shape* s, ps_dtype dtype, const void* H, con
     if (Kr && (st = check_heads(s)) != PS_OK) return st;
     if (iters < 1) return PS_ERR_RANGE;
     if (init != PS_INIT_GIVEN && init != PS_INIT_STRIDED && init != PS_INIT_FARTHEST) return PS_ERR_RANGE;
-    if (flags & ~(uint32_t)PS_KMEANS_FIXED_POINT_EXIT) return PS_ERR_RANGE;
+    if (flags & ~(uint32_t)(PS_KMEANS_FIXED_POINT_EXIT | PS_KMEANS_ALL_PASSES)) return PS_ERR_RANGE;
+    if ((flags & PS_KMEANS_FIXED_POINT_EXIT) && (flags & PS_KMEANS_ALL_PASSES)) return PS_ERR_RANGE;
     if (s->d > 8192) return PS_ERR_SHAPE;  // update kernel: at most 4 chunks of 2048 per thread
     if (!aligned16(H) || !aligned16(C) || !aligned16(assign) || !aligned16(counts) ||
         !aligned16(row_norm) || (Kr && (!aligned16(Kr) || !aligned16(Ck))) ||
@@ -1334,8 +1348,10 @@ ps_status kmeans_fit_impl(const ps_shape* s, ps_dtype dtype, const void* H, cons
     const int KBn = (K + 15) / 16;
     // Iteration 0 assigns against the incoming centres and rebuilds every
     // cluster (the rows themselves are new).  Later iterations mark the two
-    // clusters of every row that moves; only those are rebuilt.
-    const int fpx = (flags & PS_KMEANS_FIXED_POINT_EXIT) ? 1 : 0;
+    // clusters of every row that moves; only those are rebuilt, and a window
+    // whose last iteration moved no row is at a fixed point: its later
+    // iterations are skipped (unless PS_KMEANS_ALL_PASSES), bit-identically.
+    const int fpx = (flags & PS_KMEANS_ALL_PASSES) ? 0 : 1;
     for (int it = 0; it < iters; ++it) {
         const int first = it == 0;
         if (bf) {
@@ -1347,8 +1363,8 @@ ps_status kmeans_fit_impl(const ps_shape* s, ps_dtype dtype, const void* H, cons
             else               launch_assign_wide<false>(s, H, L, assign, row_norm, stm);
         } else {
             const int64_t rows = (int64_t)W * N;
-            PS_LAUNCH("k_assign_f32", k_assign_f32, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stm,
-                      (const float*)H, C, assign, row_norm, W, N, d, K, first, L.dirty, L.conv);
+            PS_LAUNCH_COUNTED("k_assign_f32", rows, k_assign_f32, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                              stm, (const float*)H, C, assign, row_norm, W, N, d, K, first, L.dirty, L.conv);
         }
         PS_LAUNCH("k_bucket", k_bucket, dim3(W), dim3(64), 0, stm, assign, L.perm, L.offs, L.dirty, L.conv, N, K,
                   first, fpx);

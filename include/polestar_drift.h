@@ -77,11 +77,18 @@ typedef enum {
     PS_SCORE_ATTN_WEIGHTED = 2
 } ps_score;
 
-/* ps_kmeans_fit flags.  PS_KMEANS_FIXED_POINT_EXIT: once an iteration moves
- * no row of a window, every later iteration would reproduce the same centres
- * and assignments exactly, so the remaining passes of that window are skipped;
- * results are bit-identical to running all iterations. */
-typedef enum { PS_KMEANS_DEFAULT = 0, PS_KMEANS_FIXED_POINT_EXIT = 1 } ps_kmeans_flags;
+/* ps_kmeans_fit flags.  By default (PS_KMEANS_DEFAULT, or the same behaviour
+ * named explicitly: PS_KMEANS_FIXED_POINT_EXIT), once an iteration moves no
+ * row of a window, every later iteration would reproduce the same centres and
+ * assignments exactly, so the remaining passes of that window are skipped;
+ * results are bit-identical to running all iterations.  PS_KMEANS_ALL_PASSES
+ * runs every pass of every window in full (same results; for timing and
+ * testing).  Both bits together: PS_ERR_RANGE. */
+typedef enum {
+    PS_KMEANS_DEFAULT = 0,
+    PS_KMEANS_FIXED_POINT_EXIT = 1,
+    PS_KMEANS_ALL_PASSES = 2
+} ps_kmeans_flags;
 
 typedef struct {
     int32_t W;   /* windows                                    */
@@ -340,13 +347,20 @@ ps_status ps_commit_suffix(const ps_shape* shape, const int32_t* assign, const i
 
 /*
  * Kernel timer (instrumentation, not part of the method; off by default).
- * ps_profile_begin creates 2*max_launches HIP events on the current device and
- * switches recording on: from then on every kernel the calls above enqueue is
- * bracketed by two events on the stream it runs on (launches past the
- * capacity are counted as dropped).  ps_profile_end switches recording off.
- * ps_profile_summary waits for the recorded events and writes one text line
- * per kernel, "name\tlaunches\ttotal_ms\tmin_ms\tmax_ms", then
- * "#dropped\t<n>"; PS_ERR_RANGE if `len` is too small.  Not thread-safe.
+ * ps_profile_begin creates 2*max_launches HIP events and a device counter per
+ * launch on the current device and switches recording on: from then on every
+ * kernel the calls above enqueue is bracketed by two events on the stream it
+ * runs on (launches past the capacity are counted as dropped), and the
+ * kernels whose work depends on the data (the Lloyd passes, which skip the
+ * windows at a fixed point; the centre update, which re-sums only changed
+ * clusters) count the units of work they process.  ps_profile_end switches
+ * recording off.  ps_profile_summary waits for the recorded events and
+ * writes one text line per kernel,
+ * "name\tlaunches\ttotal_ms\tmin_ms\tmax_ms\tunits_done\tunits", then
+ * "#dropped\t<n>"; units is the total work of the kernel's launches (tiles,
+ * rows or clusters), units_done the part processed, both 0 for kernels that
+ * always do their full work; PS_ERR_RANGE if `len` is too small.  Not
+ * thread-safe; not for use under graph capture.
  */
 ps_status ps_profile_begin(int32_t max_launches);
 ps_status ps_profile_end(void);

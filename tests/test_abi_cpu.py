@@ -102,7 +102,8 @@ def test_kmeans_fit_argument_checks(L):
     assert _fit(L, _shape(dh=12), Kr=FAKE, Ck=FAKE) == SHAPE         # dh % 8
     assert _fit(L, s, iters=0) == RANGE
     assert _fit(L, s, init=9) == RANGE
-    assert _fit(L, s, flags=2) == RANGE                     # unknown flag bit
+    assert _fit(L, s, flags=4) == RANGE                     # unknown flag bit
+    assert _fit(L, s, flags=3) == RANGE                     # fixed-point exit and all passes at once
     assert _fit(L, s, H=MISALIGNED) == ALIGN
     assert _fit(L, s, ws=None) == WORKSPACE
     assert _fit(L, s, ws_bytes=16) == WORKSPACE

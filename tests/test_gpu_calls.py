@@ -138,9 +138,10 @@ ITER_CASES = [("ragged-bf16", 3, 300, 80, 37, True), ("llada-rows", 2, 1024, 409
 
 @pytest.mark.parametrize("case", ITER_CASES, ids=[c[0] for c in ITER_CASES])
 def test_iteration_paths_agree(P, case):
-    """One call of n iterations (later iterations re-sum only the clusters
-    whose members changed), n calls of one iteration (every cluster re-summed
-    each time), and n iterations with the fixed-point exit must give
+    """One call of n iterations with every pass in full (later iterations
+    re-sum only the clusters whose members changed), n calls of one iteration
+    (every cluster re-summed each time), and n iterations with the default
+    fixed-point exit (a window's passes stop once one moves no row) must give
     bit-identical centres, assignments, counts, keys and objective."""
     name, W, N, d, K, bf = case
     say("iteration paths", name)
@@ -165,11 +166,11 @@ def test_iteration_paths_agree(P, case):
                         st["obj"], st["ws"], flags=flags)
 
     A, B, X = fresh(), fresh(), fresh()
-    run(A, P.PS_INIT_STRIDED, n, 0)
-    run(B, P.PS_INIT_STRIDED, 1, 0)
+    run(A, P.PS_INIT_STRIDED, n, P.PS_KMEANS_ALL_PASSES)
+    run(B, P.PS_INIT_STRIDED, 1, P.PS_KMEANS_ALL_PASSES)
     for _ in range(n - 1):
-        run(B, P.PS_INIT_GIVEN, 1, 0)
-    run(X, P.PS_INIT_STRIDED, n, P.PS_KMEANS_FIXED_POINT_EXIT)
+        run(B, P.PS_INIT_GIVEN, 1, P.PS_KMEANS_ALL_PASSES)
+    run(X, P.PS_INIT_STRIDED, n, P.PS_KMEANS_DEFAULT)      # windows stop at their fixed point
     torch.cuda.synchronize()
     for key in ("C", "a", "cnt", "Ck", "obj", "rn"):
         a, b, x = host(A[key]), host(B[key]), host(X[key])
@@ -381,6 +382,13 @@ def test_proxy_attn_and_drift(P, case, kind):
     assert close(host(Dhi), kl["D_hi"])
     assert close(host(Di), kl["D_i"])
     assert close(host(sc), kl["score"])
+    # without D_hi (above 64 clusters the rows' drifts then cannot go through
+    # it, and another kernel form runs): the same results
+    Di2, sc2 = torch.zeros_like(Di), torch.zeros_like(sc)
+    P.ps_proxy_attn(s, dt, dev(Q), dev(Ck), sigma, lc, dev(prev), kind, None, Di2, sc2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(lc), gl)
+    assert close(host(Di2), kl["D_i"]) and close(host(sc2), kl["score"])
     # window formation: no previous distribution -> zeros
     P.ps_proxy_attn(s, dt, dev(Q), dev(Ck), sigma, lc, None, kind, Dhi, Di, sc)
     torch.cuda.synchronize()

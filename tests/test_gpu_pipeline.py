@@ -391,3 +391,31 @@ def test_windows_are_independent_of_the_batch(P):
             a = host(getattr(batch, name))[w:w + 1]
             b = host(getattr(alone, name))
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (w, name)
+
+
+@pytest.mark.parametrize("name,W,steps", [("llada8b-batch", 48, 4), ("llada8b-long", 6, 3)])
+def test_fixed_point_exit_equals_every_pass_over_steps(P, name, W, steps):
+    """Whole steps with the default K-Means (a window's Lloyd passes stop once
+    one moves no row) and with every pass run in full, on the same device
+    inputs (the benchmark's generator, fewer windows): every output of every
+    step bit-identical."""
+    from drift_aware_kv_amd.pipeline import DriftPath, StepSpec
+    from synth.device import DeviceWorkload
+    cfg = synth.CONFIGS[name].with_(W=W)
+    wl = DeviceWorkload(cfg, steps)
+    paths = []
+    for flags in (P.PS_KMEANS_DEFAULT, P.PS_KMEANS_ALL_PASSES):
+        spec = StepSpec(W=W, N=cfg.N, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, dh=cfg.dh, Nb=cfg.Nb, K=cfg.K,
+                        k=cfg.k, iters=cfg.iters, bf16=True, softmax_scale=cfg.softmax_scale,
+                        block_start=cfg.block_start, kmeans_flags=flags)
+        paths.append(DriftPath(spec))
+    names = ("C", "assign", "counts", "row_norm", "Ck", "codes", "bscale", "rscale", "D_i", "score", "idx",
+             "pos", "count", "H_hat", "K_out", "V_out", "commit_block", "commit_suffix", "suffix_flag")
+    for t in range(steps):
+        say(f"  {name} step {t}")
+        for p in paths:
+            p.step(*wl.inputs(t))
+        torch.cuda.synchronize()
+        for key in names:
+            a, b = host(getattr(paths[0], key)), host(getattr(paths[1], key))
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (t, key)
