@@ -64,10 +64,9 @@ def kernel_work(name, cfg, gathered=None):
         return W * N * KV * e + W * N * 4 + W * K * KV * e, W * N * KV * 1.0
     if name.startswith("k_proxy"):
         # Q and the keys read, log-probabilities written, and (after window
-        # formation, the drift fused into the epilogue) the previous step's
-        # read; the head-parallel form leaves the drift to k_drift_kl
-        prev = 0 if name.endswith("/heads") else L * 4
-        return (W * cfg.Nb * cfg.Hq * cfg.dh * e + W * K * KV * e + L * 4 + prev,
+        # formation, for the drift: fused, or each row's drift in the
+        # head-parallel form) the previous step's read
+        return (W * cfg.Nb * cfg.Hq * cfg.dh * e + W * K * KV * e + 2 * L * 4,
                 2.0 * W * cfg.Hq * cfg.Nb * K * cfg.dh)
     if name.startswith("k_drift_scores"):
         # both distributions and the rows' drifts read, scores and D_i written

@@ -65,12 +65,16 @@ def test_gather_scales_with_the_rows_selected():
 
 
 def test_recorded_traffic_is_tied_to_the_sources():
-    name, wl = "k_assign_bf16<KB, NB, false>", CFG.name
-    got = bench.recorded_traffic(name, wl)
-    if got is not None:       # the committed counters match the committed kernel sources
-        assert 0.99 < got / bench.kernel_work(name, CFG)[0] < 1.05
-    assert bench.recorded_traffic(name, "another-workload") is None
-    assert bench.recorded_traffic("k_keys<uint16_t>", wl) is None
+    c5 = synth.CONFIGS["llada8b-long"]
+    for name, cfg, lo, hi in (("k_assign_bf16<KB, NB, true>", CFG, 0.99, 1.05),
+                              ("k_residual_grouped<T, BPL, FULL>", CFG, 0.99, 1.15),
+                              ("k_assign_wide_dma<true>", c5, 0.99, 1.05),
+                              ("k_residual_grouped<T, BPL, FULL>", c5, 0.99, 1.15)):
+        got = bench.recorded_traffic(name, cfg.name)
+        if got is not None:       # the committed counters match the committed kernel sources
+            assert lo < got / bench.kernel_work(name, cfg)[0] < hi, name
+        assert bench.recorded_traffic(name, "another-workload") is None
+    assert bench.recorded_traffic("k_keys<uint16_t>", CFG.name) is None
 
 
 def test_compulsory_work_matches_the_per_token_layer_figures():
