@@ -292,6 +292,115 @@ __global__ __launch_bounds__(256) void k_proxy_bf16(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// proxy attention above 64 clusters, head-parallel, for K = 16 KB and
+// dh = 128: one wave per (window, head, block of 16 queries), four per
+// workgroup, the query blocks of a head in neighbouring waves (the second
+// wave's key rows come from L2).  The wave loads its 16 query rows whole
+// (four 16-byte pieces per lane, all in flight at once), then streams the
+// head's key rows 16 at a time, also whole, through a ring of P blocks in
+// registers, so that P blocks are in flight while one block's 4 MFMAs run;
+// at two waves per SIMD one wave's epilogue overlaps the other's stream.  The
+// previous step's log-probabilities of the 16 queries are all requested
+// before the softmax.  Every logit accumulates the same k-steps in the same
+// order as in k_proxy_bf16, and the softmax, drift and D_{h,i} follow the
+// same per-lane order, so the results are the same bit for bit.
+// ---------------------------------------------------------------------------
+template <int KB>
+__global__ __launch_bounds__(256) void k_proxy_head(const uint16_t* __restrict__ Q,
+                                                     const uint16_t* __restrict__ Ck, float sigma,
+                                                     float* __restrict__ logp, const float* __restrict__ prev,
+                                                     float* __restrict__ D_hi, int units, int Hq, int Hkv, int Nb,
+                                                     int nqb)
+{
+    constexpr int DS = 4;                      // 32-wide k-steps of dh = 128
+    constexpr int K = 16 * KB;
+    constexpr int P = KB < 6 ? KB : 6;         // key blocks in flight
+    const int lane = lane_id(), q = lane >> 4, r16 = lane & 15;
+    const int unit = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (unit >= units) return;
+    const int pair = unit / nqb, qb = unit - pair * nqb;
+    const int w = pair / Hq, h = pair - w * Hq, g = h / (Hq / Hkv);
+    const int i = 16 * qb + r16;
+    const bool iv = i < Nb;
+    uint4 qv[DS];
+    {
+        const uint16_t* qr = Q + (((size_t)w * Nb + min(i, Nb - 1)) * Hq + h) * 128 + 8 * q;
+#pragma unroll
+        for (int u = 0; u < DS; ++u) qv[u] = *reinterpret_cast<const uint4*>(qr + 32 * u);
+    }
+    const uint16_t* kr = Ck + (((size_t)w * K + r16) * Hkv + g) * 128 + 8 * q;
+    const size_t kblock = (size_t)16 * Hkv * 128;  // 16 key rows
+    uint4 cv[P][DS];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int u = 0; u < DS; ++u) cv[p][u] = *reinterpret_cast<const uint4*>(kr + p * kblock + 32 * u);
+    if (!iv)
+#pragma unroll
+        for (int u = 0; u < DS; ++u) qv[u] = make_uint4(0, 0, 0, 0);
+    floatx4 acc[KB];
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb) {
+        acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < DS; ++u)
+            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cv[mb % P][u]),
+                                                              __builtin_bit_cast(bf16x8, qv[u]), acc[mb], 0, 0, 0);
+        if (mb + P < KB) {
+#pragma unroll
+            for (int u = 0; u < DS; ++u)
+                cv[mb % P][u] = *reinterpret_cast<const uint4*>(kr + (mb + P) * kblock + 32 * u);
+        }
+    }
+    const size_t row = (((size_t)w * Hq + h) * Nb + (iv ? i : Nb - 1)) * K;
+    float4 pp[KB];
+    if (prev) {
+#pragma unroll
+        for (int mb = 0; mb < KB; ++mb) pp[mb] = *reinterpret_cast<const float4*>(prev + row + 16 * mb + 4 * q);
+    }
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float z = acc[mb][r] * sigma;
+            acc[mb][r] = z;
+            zmax = fmaxf(zmax, z);
+        }
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+    float se = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) se += exp_hw(acc[mb][r] - zmax);
+    se += __shfl_xor(se, 16, 64);
+    se += __shfl_xor(se, 32, 64);
+    // with a single group of clusters the running sum of k_proxy_bf16 is
+    // se * 2^0 = se exactly, and its running max is zmax
+    const float lse = zmax + log_hw(se);
+    float* out = logp + row;
+    float tsum = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb) {
+        float lv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lv[r] = acc[mb][r] - lse;
+        if (iv) *reinterpret_cast<float4*>(out + 16 * mb + 4 * q) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+        if (prev) {
+            const float pq[4] = {pp[mb].x, pp[mb].y, pp[mb].z, pp[mb].w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tsum += iv ? exp_hw(lv[r]) * (lv[r] - pq[r]) : 0.0f;
+        }
+    }
+    if (prev) {
+        float D = tsum + __shfl_xor(tsum, 16, 64);
+        D = D + __shfl_xor(D, 32, 64);
+        if (iv && D_hi && q == 0) D_hi[((size_t)w * Hq + h) * Nb + i] = D;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // proxy attention, bf16, with the drift fused, software-pipelined over heads.
 // For one cluster group (K <= 16*KB), dh <= 128 and a previous step, the
 // same per-lane arithmetic as k_proxy_bf16 in the same order (identical
@@ -806,18 +915,24 @@ __global__ __launch_bounds__(256) void k_drift_kl(const float* __restrict__ cur,
 // ---------------------------------------------------------------------------
 // per-cluster scores and per-token drift from stored distributions and the
 // per-row drifts D_hi (which the head-parallel proxy kernel writes): grid
-// (W, K / 64), lane l of every wave owns cluster 64 blockIdx.y + l, wave v
-// the rows (h, i) = v, v + 4, ... in order (8 rows' loads in flight), the four
-// waves' sums combined in order; blockIdx.y == 0 also averages D_hi over the
-// heads for D_i.  The order of every sum depends on the shape only.
+// (W, K / 64) of 16-wave workgroups, lane l of every wave owns cluster
+// 64 blockIdx.y + l, wave v the rows (h, i) = v, v + 16, ... in order (8
+// rows' loads in flight: 16 waves keep enough bytes in flight when a single
+// window gives only K / 64 workgroups), the 16 waves' sums combined in order;
+// blockIdx.y == 0 also averages D_hi over the heads for D_i.  The order of
+// every sum depends on the shape only.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_drift_scores(const float* __restrict__ cur,
-                                                       const float* __restrict__ prev,
-                                                       const float* __restrict__ D_hi, int kind,
-                                                       float* __restrict__ D_i, float* __restrict__ score,
-                                                       int Hq, int Nb, int K)
+constexpr int kScoreWaves = 16;
+
+__global__ __launch_bounds__(64 * kScoreWaves) void k_drift_scores(const float* __restrict__ cur,
+                                                                    const float* __restrict__ prev,
+                                                                    const float* __restrict__ D_hi, int kind,
+                                                                    float* __restrict__ D_i,
+                                                                    float* __restrict__ score, int Hq, int Nb,
+                                                                    int K)
 {
-    __shared__ float part[4][64];
+    constexpr int NW = kScoreWaves;
+    __shared__ float part[NW][64];
     const int w = blockIdx.x, lane = lane_id(), wave = threadIdx.x >> 6;
     const int k = 64 * (int)blockIdx.y + lane;
     const bool kv = k < K;
@@ -827,18 +942,18 @@ __global__ __launch_bounds__(256) void k_drift_scores(const float* __restrict__ 
     const float* Dw = D_hi + (size_t)w * rows;
     float acc = 0.0f;
     constexpr int U = 8;
-    for (int r0 = wave; r0 < rows; r0 += 4 * U) {
+    for (int r0 = wave; r0 < rows; r0 += NW * U) {
         float lc[U], lp[U], dv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int r = min(r0 + 4 * u, rows - 1);
+            const int r = min(r0 + NW * u, rows - 1);
             lc[u] = cur[base + (size_t)r * K + kc];
             lp[u] = prev[base + (size_t)r * K + kc];
             dv[u] = Dw[r];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (r0 + 4 * u >= rows) break;
+            if (r0 + NW * u >= rows) break;
             const float p = exp_hw(lc[u]);
             acc += score_term(kind, p, p * (lc[u] - lp[u]), dv[u]);
         }
@@ -846,10 +961,14 @@ __global__ __launch_bounds__(256) void k_drift_scores(const float* __restrict__ 
     part[wave][lane] = acc;
     __syncthreads();
     const float invH = 1.0f / (float)Hq;
-    if (threadIdx.x < 64 && kv)
-        score[(size_t)w * K + k] = (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) * invH;
+    if (threadIdx.x < 64 && kv) {
+        float sum = part[0][lane];
+#pragma unroll
+        for (int v = 1; v < NW; ++v) sum += part[v][lane];
+        score[(size_t)w * K + k] = sum * invH;
+    }
     if (blockIdx.y == 0) {
-        for (int i = threadIdx.x; i < Nb; i += 256) {
+        for (int i = threadIdx.x; i < Nb; i += 64 * NW) {
             float sum = 0.0f;
             for (int h = 0; h < Hq; ++h) sum += Dw[h * Nb + i];
             D_i[(size_t)w * Nb + i] = sum * invH;
@@ -1001,12 +1120,24 @@ int attn_device_cus()
 // kernel at K = 64, dh = 128 when its two waves per window give every SIMD
 // a wave (four per compute unit); with fewer windows, or other shapes whose
 // operands fit, the four-wave pipelined kernel; otherwise k_proxy_bf16.
-// Above 64 clusters (hsplit) every (window, head) gets its own wave and the
-// drift follows in its own pass, whatever the number of windows.
+// Above 64 clusters every (window, head) gets its own wave and the drift
+// follows in its own pass, whatever the number of windows: k_proxy_head (one
+// wave per block of 16 queries) at K = 128 or 256 and dh = 128, otherwise
+// k_proxy_bf16 with hsplit.
 template <int KB, int NBQ>
 void launch_proxy(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, const float* prev,
                   int kind, int fused, float* D_hi, float* D_i, float* score, hipStream_t st)
 {
+    if constexpr (KB > 4) {
+        const int nqb = (s->Nb + 15) / 16;
+        const int64_t units = (int64_t)s->W * s->Hq * nqb;
+        if (fused != 1 && s->K == 16 * KB && s->dh == 128 && units <= INT32_MAX - 3) {
+            PS_LAUNCH("k_proxy_head<KB>", (k_proxy_head<KB>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st,
+                      (const uint16_t*)Q, (const uint16_t*)Ck, sigma, logp, fused == 2 ? prev : nullptr,
+                      fused == 2 ? D_hi : nullptr, (int)units, s->Hq, s->Hkv, s->Nb, nqb);
+            return;
+        }
+    }
     if (fused != 1) {
         PS_LAUNCH("k_proxy_bf16<KB, NBQ>/heads", (k_proxy_bf16<KB, NBQ>), dim3(s->W, (s->Hq + 3) / 4), dim3(256), 0,
                   st, (const uint16_t*)Q, (const uint16_t*)Ck, sigma, logp, prev, kind, fused, D_hi, D_i, score,
@@ -1146,7 +1277,7 @@ extern "C" ps_status ps_proxy_attn(const ps_shape* s, ps_dtype dtype, const void
     }
     if (!fused) {
         if (rowdrift) {
-            PS_LAUNCH("k_drift_scores", k_drift_scores, dim3(s->W, (s->K + 63) / 64), dim3(256), 0, stm, logp_cur,
+            PS_LAUNCH("k_drift_scores", k_drift_scores, dim3(s->W, (s->K + 63) / 64), dim3(64 * kScoreWaves), 0, stm, logp_cur,
                       logp_prev, D_hi, (int)kind, D_i, score, s->Hq, s->Nb, s->K);
         } else if (logp_prev) {
             enqueue_drift(s, logp_cur, logp_prev, kind, D_hi, D_i, score, stm);

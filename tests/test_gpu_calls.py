@@ -347,6 +347,8 @@ ATT_CASES = [
     ("dream-gqa", 1, 32, 28, 4, 128, 128, True),
     ("ragged", 3, 13, 6, 3, 24, 37, True),
     ("k256", 1, 32, 8, 8, 128, 256, True),
+    ("k128-nb5", 3, 5, 6, 3, 128, 128, True),      # one query block, 18 (window, head) pairs
+    ("k256-nb50", 2, 50, 4, 2, 128, 256, True),    # four query blocks, the last ragged
     ("k1000", 1, 5, 2, 1, 32, 1000, True),
     ("f32", 2, 16, 1, 1, 64, 8, False),
 ]
@@ -389,9 +391,11 @@ def test_proxy_attn_and_drift(P, case, kind):
     torch.cuda.synchronize()
     assert np.array_equal(host(lc), gl)
     assert close(host(Di2), kl["D_i"]) and close(host(sc2), kl["score"])
-    # window formation: no previous distribution -> zeros
+    # window formation: no previous distribution -> zeros, the same logits
+    lc.zero_()
     P.ps_proxy_attn(s, dt, dev(Q), dev(Ck), sigma, lc, None, kind, Dhi, Di, sc)
     torch.cuda.synchronize()
+    assert np.array_equal(host(lc), gl)
     assert not host(Di).any() and not host(sc).any() and not host(Dhi).any()
 
 
