@@ -547,10 +547,13 @@ __global__ __launch_bounds__(64) void k_gather_select(const int32_t* __restrict_
     if (lane == 0) count[w] = running;
 }
 
-// rebuild / copy the gathered rows; grid (G, W), each workgroup strides over
-// slots.  A slot's reads (codes, block scales, centre row, K and V rows; up
-// to 512 pieces of each per round) are all issued before its first store, so
-// a workgroup waits on memory once per round rather than once per piece.
+// rebuild / copy the gathered rows: G workgroups per window, each striding
+// over the window's slots.  A slot's reads (codes, block scales, centre row,
+// K and V rows; up to 512 pieces of each per round) are all issued before its
+// first store, so a workgroup waits on memory once per round rather than once
+// per piece.  After the XCD remap a window's workgroups are consecutive, so
+// they run on one XCD and the centre rows of its selected clusters, read once
+// per gathered row, come from that XCD's L2 after the first.
 template <typename T>
 __global__ __launch_bounds__(256) void k_gather_rows(const int32_t* __restrict__ pos,
                                                       const int32_t* __restrict__ count, int cap,
@@ -562,16 +565,18 @@ __global__ __launch_bounds__(256) void k_gather_rows(const int32_t* __restrict__
                                                       const float* __restrict__ row_norm,
                                                       T* __restrict__ H_hat, const T* __restrict__ Kc,
                                                       const T* __restrict__ Vc, T* __restrict__ K_out,
-                                                      T* __restrict__ V_out, int N, int d, int K, int KV)
+                                                      T* __restrict__ V_out, int N, int d, int K, int KV,
+                                                      int G, int nblocks)
 {
-    const int w = blockIdx.y, tid = threadIdx.x;
+    const int L = xcd_remap(blockIdx.x, nblocks);
+    const int w = L / G, gb = L - w * G, tid = threadIdx.x;
     const int cnt = count[w];
     const int M = cnt < cap ? cnt : cap;
     const int nh = H_hat ? (d >> 3) : 0;                              // 8-element chunks
     const int npc = (int)((size_t)KV * sizeof(T) / 16);               // 16-byte pieces of a K/V row
     const int nk = Kc ? npc : 0, nv = Vc ? npc : 0;
     const int rounds = (max(nh, max(nk, nv)) + 511) / 512;
-    for (int slot = blockIdx.x; slot < M; slot += gridDim.x) {
+    for (int slot = gb; slot < M; slot += G) {
         const int j = pos[(size_t)w * cap + slot];
         const size_t row = (size_t)w * N + j;
         const size_t orow = (size_t)w * cap + slot;
@@ -769,20 +774,22 @@ extern "C" ps_status ps_refresh_gather(const ps_shape* s, ps_dtype dtype, const 
     (void)hipGetLastError();
     PS_LAUNCH("k_gather_select", k_gather_select, dim3(s->W), dim3(64), 0, stm, assign, idx, k, cap, pos, count, s->N, s->K);
     if (cap > 0 && (H_hat || Kc || Vc)) {
-        // about one slot per workgroup at the mean selection size (N k / K rows)
+        // two workgroups per slot at the mean selection size (N k / K rows)
         const int64_t expect = ((int64_t)s->N * k + s->K - 1) / s->K;
         int G = (int)std::min<int64_t>(2 * expect, 65535);
         if (G < 1) G = 1;
         if (G > cap) G = cap;
+        G = (int)std::max<int64_t>(1, std::min<int64_t>(G, INT32_MAX / std::max(s->W, 1)));
+        const int nblocks = G * s->W;
         const int KV = (Kc || Vc) ? s->Hkv * s->dh : 0;
         if (dtype == PS_BF16)
-            PS_LAUNCH("k_gather_rows<uint16_t>", k_gather_rows<uint16_t>, dim3(G, s->W), dim3(256), 0, stm, pos, count, cap, assign,
-                               codes, bscale, rscale, C, row_norm, (uint16_t*)H_hat, (const uint16_t*)Kc,
-                               (const uint16_t*)Vc, (uint16_t*)K_out, (uint16_t*)V_out, s->N, s->d, s->K, KV);
+            PS_LAUNCH("k_gather_rows<uint16_t>", k_gather_rows<uint16_t>, dim3(nblocks), dim3(256), 0, stm, pos, count,
+                      cap, assign, codes, bscale, rscale, C, row_norm, (uint16_t*)H_hat, (const uint16_t*)Kc,
+                      (const uint16_t*)Vc, (uint16_t*)K_out, (uint16_t*)V_out, s->N, s->d, s->K, KV, G, nblocks);
         else
-            PS_LAUNCH("k_gather_rows<float>", k_gather_rows<float>, dim3(G, s->W), dim3(256), 0, stm, pos, count, cap, assign,
-                               codes, bscale, rscale, C, row_norm, (float*)H_hat, (const float*)Kc,
-                               (const float*)Vc, (float*)K_out, (float*)V_out, s->N, s->d, s->K, KV);
+            PS_LAUNCH("k_gather_rows<float>", k_gather_rows<float>, dim3(nblocks), dim3(256), 0, stm, pos, count, cap,
+                      assign, codes, bscale, rscale, C, row_norm, (float*)H_hat, (const float*)Kc, (const float*)Vc,
+                      (float*)K_out, (float*)V_out, s->N, s->d, s->K, KV, G, nblocks);
     }
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
 }

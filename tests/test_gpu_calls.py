@@ -497,6 +497,7 @@ def test_refresh_gather_bit_exact(P, bf, cap_mode, store):
     q = O.residual_nvfp4(so, O.BF16 if bf else O.F32, H, rn, C, assign)
     idx = np.stack([rng.choice(K, k, replace=False) for _ in range(W)]).astype(np.int32)
     idx[2, 0] = K + 3   # out of range: selects nothing
+    idx[1, 1] = idx[1, 0]   # selected twice: selects it once
     Kc = rnd_bf16(rng, (W, N, Hkv, dh)) if bf else rng.standard_normal((W, N, Hkv, dh)).astype(np.float32)
     Vc = rnd_bf16(rng, (W, N, Hkv, dh)) if bf else rng.standard_normal((W, N, Hkv, dh)).astype(np.float32)
     cap = {"ample": N, "short": 17, "zero": 0}[cap_mode]
@@ -536,6 +537,7 @@ GATHER_PART_CASES = [
     ("v-only", True, 4096, 32, 128, (False, False, True)),
     ("kv-long-rows", True, 256, 64, 160, (False, True, True)),   # 1280 pieces: three rounds
     ("f32-d4160-all", False, 4160, 4, 64, (True, True, True)),   # ragged second round
+    ("d8320-h-only", True, 8320, 8, 128, (True, False, False)),  # centre past 8192 elements read per row
 ]
 
 
@@ -590,6 +592,40 @@ def test_refresh_gather_rows_and_partial_outputs(P, case):
         if want_v:
             assert np.array_equal(host(Vo)[w, :m].view(u), r["V_out"][w, :m].view(u))
             assert not host(Vo)[w, m:].any()
+
+
+def test_refresh_gather_many_windows(P):
+    """Enough (window, selected cluster) pairs that each gets one workgroup
+    (fewer pairs split a cluster's members over several)."""
+    rng = np.random.default_rng(16)
+    W, N, d, K, k, Hkv, dh = 160, 96, 64, 8, 4, 1, 16
+    say("gather many windows", W)
+    H = O.f32_to_bf16(rng.standard_normal((W, N, d)).astype(np.float32))
+    rn = np.sqrt((bf16f(H).astype(np.float64) ** 2).sum(-1)).astype(np.float32)
+    C = rng.standard_normal((W, K, d)).astype(np.float32)
+    C /= np.linalg.norm(C, axis=-1, keepdims=True)
+    assign = rng.integers(0, K, (W, N)).astype(np.int32)
+    so = O.Shape(W=W, N=N, d=d, Hq=Hkv, Hkv=Hkv, dh=dh, K=K)
+    q = O.residual_nvfp4(so, O.BF16, H, rn, C, assign)
+    idx = np.stack([rng.choice(K, k, replace=False) for _ in range(W)]).astype(np.int32)
+    Kc, Vc = rnd_bf16(rng, (W, N, Hkv, dh)), rnd_bf16(rng, (W, N, Hkv, dh))
+    r = O.refresh_gather(so, O.BF16, assign, idx, k, N, q["codes"], q["bscale"], q["rscale"], C, rn, True, Kc, Vc)
+    s = P.Shape(W=W, N=N, d=d, Hq=Hkv, Hkv=Hkv, dh=dh, K=K)
+    pos = torch.full((W, N), -1, dtype=torch.int32, device="cuda")
+    count = torch.zeros(W, dtype=torch.int32, device="cuda")
+    Hh = torch.zeros(W, N, d, dtype=torch.bfloat16, device="cuda")
+    Ko = torch.zeros(W, N, Hkv, dh, dtype=torch.bfloat16, device="cuda")
+    Vo = torch.zeros(W, N, Hkv, dh, dtype=torch.bfloat16, device="cuda")
+    P.ps_refresh_gather(s, P.PS_BF16, dev(assign), dev(idx), k, N, pos, count, dev(q["codes"]),
+                        dev(q["bscale"]), dev(q["rscale"]), dev(C), dev(rn), Hh, dev(Kc), dev(Vc), Ko, Vo)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(count), r["count"])
+    for w in range(W):
+        m = int(r["count"][w])
+        assert np.array_equal(host(pos)[w, :m], r["pos"][w, :m])
+        assert np.array_equal(host(Hh)[w, :m].view(np.uint16), r["H_hat"][w, :m].view(np.uint16))
+        assert np.array_equal(host(Ko)[w, :m], r["K_out"][w, :m])
+        assert np.array_equal(host(Vo)[w, :m], r["V_out"][w, :m])
 
 
 def test_w_zero_is_a_no_op(P):
