@@ -842,64 +842,87 @@ __global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ H,
 }
 
 // ---------------------------------------------------------------------------
-// bucket: stable counting sort of rows by cluster, one wave per window.
-// After the first iteration, a window none of whose clusters changed keeps its
-// member lists (they are a function of the unchanged assignment) and, unless
-// every pass is to run in full, is marked converged, which makes every later
-// assignment pass of that window a no-op (the iteration would reproduce
-// exactly the same centres and assignments).
+// bucket: stable counting sort of rows by cluster, one 8-wave workgroup per
+// window.  Wave v owns the v-th of eight consecutive row ranges: it counts its
+// rows per cluster into its own LDS histogram; the cluster offsets are the
+// prefix over clusters of the totals, and wave v's first slot in cluster c is
+// offs[c] plus the counts of waves 0..v-1 in c; then each wave writes its rows
+// in ascending order (lanes of one cluster ranked by a match-any ballot).  So
+// every cluster lists its members in ascending row order, as a sequential
+// sort would.  After the first iteration, a window none of whose clusters
+// changed keeps its member lists (they are a function of the unchanged
+// assignment) and, unless every pass is to run in full, is marked converged,
+// which makes every later assignment pass of that window a no-op (the
+// iteration would reproduce exactly the same centres and assignments).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_bucket(const int32_t* __restrict__ assign, int32_t* __restrict__ perm,
-                                                int32_t* __restrict__ offs, const int32_t* __restrict__ dirty,
-                                                int32_t* __restrict__ conv, int N, int K, int first,
-                                                int fixed_point_exit)
+constexpr int kBucketWaves = 8;
+
+__global__ __launch_bounds__(64 * kBucketWaves) void k_bucket(const int32_t* __restrict__ assign,
+                                                               int32_t* __restrict__ perm,
+                                                               int32_t* __restrict__ offs,
+                                                               const int32_t* __restrict__ dirty,
+                                                               int32_t* __restrict__ conv, int N, int K, int first,
+                                                               int fixed_point_exit)
 {
-    __shared__ int cur[kMaxK];
-    const int w = blockIdx.x, lane = lane_id();
+    constexpr int NW = kBucketWaves;
+    __shared__ int cnt[NW][kMaxK];
+    const int w = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     if (first) {
-        if (lane == 0) conv[w] = 0;
+        if (tid == 0) conv[w] = 0;
     } else {
         if (conv[w]) return;
         bool any = false;
-        for (int k = lane; k < K; k += 64) any |= dirty[(size_t)w * K + k] != 0;
-        if (!__ballot(any)) {
-            if (fixed_point_exit && lane == 0) conv[w] = 1;
+        for (int k = tid; k < K; k += 64 * NW) any |= dirty[(size_t)w * K + k] != 0;
+        if (!__syncthreads_or(any)) {
+            if (fixed_point_exit && tid == 0) conv[w] = 1;
             return;
         }
     }
     const int32_t* a = assign + (size_t)w * N;
-    for (int k = lane; k < K; k += 64) cur[k] = 0;
+    const int seg = (N + 64 * NW - 1) / (64 * NW) * 64;
+    const int j0 = min(wave * seg, N), j1 = min(j0 + seg, N);
+    for (int k = lane; k < K; k += 64) cnt[wave][k] = 0;
     __syncthreads();
-    for (int j = lane; j < N; j += 64) {
+    for (int j = j0 + lane; j < j1; j += 64) {
         int c = a[j];
         c = (c < 0 || c >= K) ? 0 : c;
-        atomicAdd(&cur[c], 1);
+        atomicAdd(&cnt[wave][c], 1);
     }
     __syncthreads();
-    int running = 0;
-    for (int base = 0; base < K; base += 64) {
-        const int k = base + lane;
-        const int v = k < K ? cur[k] : 0;
-        int incl = v;
+    if (wave == 0) {
+        int running = 0;
+        for (int base = 0; base < K; base += 64) {
+            const int k = base + lane;
+            int v = 0;
+            if (k < K)
+                for (int u = 0; u < NW; ++u) v += cnt[u][k];
+            int incl = v;
 #pragma unroll
-        for (int s = 1; s < 64; s <<= 1) {
-            const int o = __shfl_up(incl, s, 64);
-            if (lane >= s) incl += o;
+            for (int s = 1; s < 64; s <<= 1) {
+                const int o = __shfl_up(incl, s, 64);
+                if (lane >= s) incl += o;
+            }
+            const int excl = running + incl - v;
+            if (k < K) {
+                offs[(size_t)w * (K + 1) + k] = excl;
+                int start = excl;
+                for (int u = 0; u < NW; ++u) {
+                    const int t = cnt[u][k];
+                    cnt[u][k] = start;
+                    start += t;
+                }
+            }
+            running += __shfl(incl, 63, 64);
         }
-        const int excl = running + incl - v;
-        if (k < K) {
-            offs[(size_t)w * (K + 1) + k] = excl;
-            cur[k] = excl;
-        }
-        running += __shfl(incl, 63, 64);
+        if (lane == 0) offs[(size_t)w * (K + 1) + K] = running;
     }
-    if (lane == 0) offs[(size_t)w * (K + 1) + K] = running;
     __syncthreads();
     const int nbits = K > 1 ? 32 - __clz(K - 1) : 0;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < N; base += 64) {
+    int* cur = cnt[wave];
+    for (int base = j0; base < j1; base += 64) {
         const int j = base + lane;
-        const bool valid = j < N;
+        const bool valid = j < j1;
         int c = valid ? a[j] : 0;
         c = (c < 0 || c >= K) ? 0 : c;
         uint64_t peers = __ballot(valid);
@@ -913,12 +936,14 @@ __global__ __launch_bounds__(64) void k_bucket(const int32_t* __restrict__ assig
             total = __popcll(peers);
             start = cur[c];
         }
-        __syncthreads();
+        // every lane has read its cluster's start before the last of its
+        // peers moves it (the wave's LDS accesses complete in order)
+        __builtin_amdgcn_wave_barrier();
         if (valid) {
             perm[(size_t)w * N + start + rank] = j;
             if (rank == total - 1) cur[c] = start + total;
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -1131,13 +1156,20 @@ __global__ __launch_bounds__(256) void k_keys(const T* __restrict__ Kr, const in
     }
 }
 
-__global__ void k_objective(const double* __restrict__ nrm, double* __restrict__ obj, int W, int K)
+// objective of each window: sum over clusters of the fp64 norms of the
+// centre sums, added in ascending cluster order by one lane after the wave
+// has staged the window's K norms in LDS with coalesced loads
+__global__ __launch_bounds__(64) void k_objective(const double* __restrict__ nrm, double* __restrict__ obj, int K)
 {
-    const int w = blockIdx.x * blockDim.x + threadIdx.x;
-    if (w >= W) return;
-    double s = 0.0;
-    for (int k = 0; k < K; ++k) s += nrm[(size_t)w * K + k];
-    obj[w] = s;
+    __shared__ double v[kMaxK];
+    const int w = blockIdx.x, lane = lane_id();
+    for (int k = lane; k < K; k += 64) v[k] = nrm[(size_t)w * K + k];
+    __syncthreads();
+    if (lane == 0) {
+        double s = 0.0;
+        for (int k = 0; k < K; ++k) s += v[k];
+        obj[w] = s;
+    }
 }
 
 // workspace layout
@@ -1366,7 +1398,7 @@ ps_status kmeans_fit_impl(const ps_shape* s, ps_dtype dtype, const void* H, cons
             PS_LAUNCH_COUNTED("k_assign_f32", rows, k_assign_f32, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
                               stm, (const float*)H, C, assign, row_norm, W, N, d, K, first, L.dirty, L.conv);
         }
-        PS_LAUNCH("k_bucket", k_bucket, dim3(W), dim3(64), 0, stm, assign, L.perm, L.offs, L.dirty, L.conv, N, K,
+        PS_LAUNCH("k_bucket", k_bucket, dim3(W), dim3(64 * kBucketWaves), 0, stm, assign, L.perm, L.offs, L.dirty, L.conv, N, K,
                   first, fpx);
         if (bf) {
             switch (CH) {
@@ -1391,7 +1423,7 @@ ps_status kmeans_fit_impl(const ps_shape* s, ps_dtype dtype, const void* H, cons
         else    PS_LAUNCH("k_keys<float>", k_keys<float>, dim3(nblocks), dim3(256), 0, stm, (const float*)Kr, L.perm, L.offs, (float*)Ck, N, KV, K, nblocks);
     }
     if (objective)
-        PS_LAUNCH("k_objective", k_objective, dim3((W + 63) / 64), dim3(64), 0, stm, L.nrm, objective, W, K);
+        PS_LAUNCH("k_objective", k_objective, dim3(W), dim3(64), 0, stm, L.nrm, objective, K);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
 }
 

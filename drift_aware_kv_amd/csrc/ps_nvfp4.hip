@@ -514,28 +514,53 @@ __global__ __launch_bounds__(256) void k_residual_listed(const T* __restrict__ H
     }
 }
 
-// stable compaction of the members of the selected clusters, one wave per window
-__global__ __launch_bounds__(64) void k_gather_select(const int32_t* __restrict__ assign,
-                                                       const int32_t* __restrict__ idx, int k, int cap,
-                                                       int32_t* __restrict__ pos, int32_t* __restrict__ count,
-                                                       int N, int K)
+// stable compaction of the members of the selected clusters, one 8-wave
+// workgroup per window: wave v owns the v-th of eight consecutive row ranges,
+// counts its members, and writes them from the count of waves 0..v-1 on, in
+// ascending order (a ballot prefix within each 64 rows)
+constexpr int kSelectWaves = 8;
+
+__global__ __launch_bounds__(64 * kSelectWaves) void k_gather_select(const int32_t* __restrict__ assign,
+                                                                      const int32_t* __restrict__ idx, int k,
+                                                                      int cap, int32_t* __restrict__ pos,
+                                                                      int32_t* __restrict__ count, int N, int K)
 {
+    constexpr int NW = kSelectWaves;
     __shared__ uint8_t sel[kMaxK];
-    const int w = blockIdx.x, lane = lane_id();
-    for (int c = lane; c < K; c += 64) sel[c] = 0;
+    __shared__ int wcnt[NW];
+    const int w = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    for (int c = tid; c < K; c += 64 * NW) sel[c] = 0;
     __syncthreads();
-    for (int r = lane; r < k; r += 64) {
+    for (int r = tid; r < k; r += 64 * NW) {
         const int c = idx[(size_t)w * k + r];
         if (c >= 0 && c < K) sel[c] = 1;
     }
     __syncthreads();
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int32_t* a = assign + (size_t)w * N;
-    int running = 0;
-    for (int base = 0; base < N; base += 64) {
+    const int seg = (N + 64 * NW - 1) / (64 * NW) * 64;
+    const int j0 = min(wave * seg, N), j1 = min(j0 + seg, N);
+    int mine = 0;
+    for (int base = j0; base < j1; base += 64) {
         const int j = base + lane;
         bool p = false;
-        if (j < N) {
+        if (j < j1) {
+            const int c = a[j];
+            p = c >= 0 && c < K && sel[c];
+        }
+        mine += __popcll(__ballot(p));
+    }
+    if (lane == 0) wcnt[wave] = mine;
+    __syncthreads();
+    int running = 0, total = 0;
+    for (int v = 0; v < NW; ++v) {
+        if (v < wave) running += wcnt[v];
+        total += wcnt[v];
+    }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = j0; base < j1; base += 64) {
+        const int j = base + lane;
+        bool p = false;
+        if (j < j1) {
             const int c = a[j];
             p = c >= 0 && c < K && sel[c];
         }
@@ -544,7 +569,7 @@ __global__ __launch_bounds__(64) void k_gather_select(const int32_t* __restrict_
         if (p && slot < cap) pos[(size_t)w * cap + slot] = j;
         running += __popcll(m);
     }
-    if (lane == 0) count[w] = running;
+    if (tid == 0) count[w] = total;
 }
 
 // rebuild / copy the gathered rows: G workgroups per window, each striding
@@ -772,7 +797,7 @@ extern "C" ps_status ps_refresh_gather(const ps_shape* s, ps_dtype dtype, const 
     }
     hipStream_t stm = (hipStream_t)stream;
     (void)hipGetLastError();
-    PS_LAUNCH("k_gather_select", k_gather_select, dim3(s->W), dim3(64), 0, stm, assign, idx, k, cap, pos, count, s->N, s->K);
+    PS_LAUNCH("k_gather_select", k_gather_select, dim3(s->W), dim3(64 * kSelectWaves), 0, stm, assign, idx, k, cap, pos, count, s->N, s->K);
     if (cap > 0 && (H_hat || Kc || Vc)) {
         // two workgroups per slot at the mean selection size (N k / K rows)
         const int64_t expect = ((int64_t)s->N * k + s->K - 1) / s->K;
