@@ -168,12 +168,12 @@ __global__ __launch_bounds__(256) void k_centres_to_bf16(const float* __restrict
 // reads); each wave streams its token rows straight into registers one chunk
 // ahead (NB*2 16-byte loads per lane per chunk, each load covering 16 rows x
 // 64 contiguous bytes).  FIRST: the first iteration of a call, which also
-// writes the fp64 row norms and marks nothing, and takes the caller's fp32
-// centres as `Cop`, rounding each staged piece to bf16 on its way to LDS (the
-// same rounding as the stored copy, which the first update then writes for
-// every cluster); later iterations take that bf16 copy, mark the old and new
-// cluster of every row that moves and skip windows at a fixed point.
-template <int KB, int NB, bool FIRST>
+// writes the fp64 row norms and marks nothing; later iterations mark the old
+// and new cluster of every row that moves and skip windows at a fixed point.
+// F32C: `Cop` is the caller's fp32 centres, each staged piece rounded to bf16
+// on its way to LDS (the same rounding as the stored copy, which the first
+// update then writes for every cluster); otherwise `Cop` is that bf16 copy.
+template <int KB, int NB, bool FIRST, bool F32C>
 __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict__ H,
                                                       const void* __restrict__ Cop,
                                                       int32_t* __restrict__ assign,
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
         // before a chunk's MFMAs covers that chunk's loads only, not the next
         // chunk's, which stay in flight.
         uint4 cpre[PIECES];
-        float4 cpre32[FIRST ? PIECES : 1][2];
+        float4 cpre32[F32C ? PIECES : 1][2];
         uint4 hcur[NB][NS], hnext[NB][NS];
         auto load_c = [&](int c0) {
 #pragma unroll
@@ -239,9 +239,9 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
                 const int piece = min(p * 256 + (int)threadIdx.x, NPIECE - 1);
                 const int row = piece / (DK / 8), col = (piece % (DK / 8)) * 8;
                 const size_t off = (size_t)min(cg + row, K - 1) * d + min(c0 + col, d - 8);
-                if (FIRST) {
-                    cpre32[FIRST ? p : 0][0] = *reinterpret_cast<const float4*>(Cf + off);
-                    cpre32[FIRST ? p : 0][1] = *reinterpret_cast<const float4*>(Cf + off + 4);
+                if (F32C) {
+                    cpre32[F32C ? p : 0][0] = *reinterpret_cast<const float4*>(Cf + off);
+                    cpre32[F32C ? p : 0][1] = *reinterpret_cast<const float4*>(Cf + off + 4);
                 } else {
                     cpre[p] = *reinterpret_cast<const uint4*>(Cw + off);
                 }
@@ -253,8 +253,8 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
                 const int piece = p * 256 + threadIdx.x;
                 const int row = piece / (DK / 8), col = (piece % (DK / 8)) * 8;
                 const bool ok = cg + row < K && c0 + col < d;
-                if (FIRST) {
-                    const float4 a = cpre32[FIRST ? p : 0][0], b = cpre32[FIRST ? p : 0][1];
+                if (F32C) {
+                    const float4 a = cpre32[F32C ? p : 0][0], b = cpre32[F32C ? p : 0][1];
                     cpre[p] = make_uint4(f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16),
                                          f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16),
                                          f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16),
@@ -1262,14 +1262,18 @@ void launch_assign_bf16(const ps_shape* s, const void* H, const float* C, const 
 {
     const int tiles = (s->N + 64 * NB - 1) / (64 * NB);
     const int nblocks = s->W * tiles;
-    if (first)
-        PS_LAUNCH_COUNTED("k_assign_bf16<KB, NB, true>", nblocks, (k_assign_bf16<KB, NB, true>), dim3(nblocks),
-                          dim3(256), 0, st, (const uint16_t*)H, (const void*)C, assign, rn, s->N, s->d, s->K, tiles,
-                          nblocks, ws.dirty, ws.conv);
+    if (first == 1)
+        PS_LAUNCH_COUNTED("k_assign_bf16<KB, NB, true>", nblocks, (k_assign_bf16<KB, NB, true, true>),
+                          dim3(nblocks), dim3(256), 0, st, (const uint16_t*)H, (const void*)C, assign, rn, s->N,
+                          s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
+    else if (first)
+        PS_LAUNCH_COUNTED("k_assign_bf16<KB, NB, true>/bf16", nblocks, (k_assign_bf16<KB, NB, true, false>),
+                          dim3(nblocks), dim3(256), 0, st, (const uint16_t*)H, (const void*)ws.Cb, assign, rn, s->N,
+                          s->d, s->K, tiles, nblocks, ws.dirty, ws.conv);
     else
-        PS_LAUNCH_COUNTED("k_assign_bf16<KB, NB, false>", nblocks, (k_assign_bf16<KB, NB, false>), dim3(nblocks),
-                          dim3(256), 0, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d, s->K, tiles, nblocks,
-                          ws.dirty, ws.conv);
+        PS_LAUNCH_COUNTED("k_assign_bf16<KB, NB, false>", nblocks, (k_assign_bf16<KB, NB, false, false>),
+                          dim3(nblocks), dim3(256), 0, st, (const uint16_t*)H, ws.Cb, assign, rn, s->N, s->d,
+                          s->K, tiles, nblocks, ws.dirty, ws.conv);
 }
 
 // compute units of the current device (cached per device; 256 if unknown)
@@ -1291,16 +1295,24 @@ int device_cus()
 // launch would leave compute units idle (few windows): a quarter of the
 // tokens per workgroup and four times the workgroups.  The number of tokens
 // a wave owns does not change any score's accumulation order, so both give
-// bit-identical results.
+// bit-identical results.  Such a small launch is bound by its few compute
+// units' load rate, so its first pass reads the bf16 copy of the centres
+// (written by k_centres_to_bf16 before it: half the bytes of the fp32
+// centres, the same rounding); `first` is 1 for the fp32 operand, 2 for that.
+bool assign_bf16_small(const ps_shape* s, int NB)
+{
+    const int64_t tiles = (int64_t)s->W * ((s->N + 64 * NB - 1) / (64 * NB));
+    return NB > 1 && tiles < device_cus();
+}
+
 template <int KB, int NB>
 void launch_assign_bf16_fit(const ps_shape* s, const void* H, const float* C, const KmWs& ws, int32_t* assign,
                             float* rn, int first, hipStream_t st)
 {
-    const int64_t tiles = (int64_t)s->W * ((s->N + 64 * NB - 1) / (64 * NB));
-    if (NB > 1 && tiles < device_cus())
-        launch_assign_bf16<KB, 1>(s, H, C, ws, assign, rn, first, st);
+    if (assign_bf16_small(s, NB))
+        launch_assign_bf16<KB, 1>(s, H, C, ws, assign, rn, first ? 2 : 0, st);
     else
-        launch_assign_bf16<KB, NB>(s, H, C, ws, assign, rn, first, st);
+        launch_assign_bf16<KB, NB>(s, H, C, ws, assign, rn, first ? 1 : 0, st);
 }
 
 }  // namespace
@@ -1369,15 +1381,17 @@ ps_status kmeans_fit_impl(const ps_shape* s, ps_dtype dtype, const void* H, cons
         if (bf) PS_LAUNCH("k_init_farthest<uint16_t>", k_init_farthest<uint16_t>, dim3(W), dim3(256), shm, stm, (const uint16_t*)H, C, L.fm, L.fn, N, d, K);
         else    PS_LAUNCH("k_init_farthest<float>", k_init_farthest<float>, dim3(W), dim3(256), shm, stm, (const float*)H, C, L.fm, L.fn, N, d, K);
     }
-    if (bf && K > 128) {
-        // the tile kernels above 128 clusters read the bf16 copy from the
-        // first pass on; below, the first pass rounds the fp32 centres itself
+    const int KBn = (K + 15) / 16;
+    const bool small = KBn <= 8 && assign_bf16_small(s, KBn <= 4 ? PS_ASSIGN_NB_SMALLK : PS_ASSIGN_NB_LARGEK);
+    if (bf && (K > 128 || small)) {
+        // the tile kernels above 128 clusters, and a launch too small to fill
+        // the device, read the bf16 copy from the first pass on; otherwise the
+        // first pass rounds the fp32 centres itself
         const size_t n8 = (size_t)W * K * d / 8;
         const int blocks = (int)std::min<size_t>((n8 + 255) / 256, 8192);
         PS_LAUNCH("k_centres_to_bf16", k_centres_to_bf16, dim3(blocks), dim3(256), 0, stm, C, L.Cb, n8);
     }
     const int CH = (d + 2047) / 2048;
-    const int KBn = (K + 15) / 16;
     // Iteration 0 assigns against the incoming centres and rebuilds every
     // cluster (the rows themselves are new).  Later iterations mark the two
     // clusters of every row that moves; only those are rebuilt, and a window
