@@ -35,6 +35,9 @@ def test_assign_pass_bytes_and_flops():
     # the first pass reads the fp32 centres
     first, _ = bench.kernel_work("k_assign_bf16<KB, NB, true>", CFG)
     assert first == byts + W * K * d * 2
+    # ... unless the launch is small and reads the bf16 copy
+    small_first, _ = bench.kernel_work("k_assign_bf16<KB, NB, true>/bf16", CFG)
+    assert small_first == byts
 
 
 def test_coder_bytes():
@@ -48,11 +51,15 @@ def test_coder_bytes():
 
 def test_proxy_counts_the_previous_distribution():
     L = CFG.W * CFG.Hq * CFG.Nb * CFG.K
-    byts, flops = bench.kernel_work("k_proxy_bf16<KB, NBQ>", CFG)
     q = CFG.W * CFG.Nb * CFG.Hq * CFG.dh * 2
     ck = CFG.W * CFG.K * CFG.Hkv * CFG.dh * 2
-    assert byts == q + ck + 2 * L * 4
-    assert flops == 2.0 * CFG.W * CFG.Hq * CFG.Nb * CFG.K * CFG.dh
+    for name in ("k_proxy_bf16<KB, NBQ>", "k_proxy_rows<NBQ>", "k_proxy_head<KB>"):
+        byts, flops = bench.kernel_work(name, CFG)
+        assert byts == q + ck + 2 * L * 4, name
+        assert flops == 2.0 * CFG.W * CFG.Hq * CFG.Nb * CFG.K * CFG.dh
+    # the score pass reads both distributions and the rows' drifts once
+    byts, _ = bench.kernel_work("k_drift_scores", CFG)
+    assert byts == 2 * L * 4 + CFG.W * CFG.Hq * CFG.Nb * 4 + CFG.W * (CFG.K + CFG.Nb) * 4
 
 
 def test_gather_scales_with_the_rows_selected():
