@@ -349,6 +349,8 @@ ATT_CASES = [
     ("k256", 1, 32, 8, 8, 128, 256, True),
     ("k128-nb5", 3, 5, 6, 3, 128, 128, True),      # one query block, 18 (window, head) pairs
     ("k256-nb50", 2, 50, 4, 2, 128, 256, True),    # four query blocks, the last ragged
+    ("k200", 2, 20, 6, 2, 128, 200, True),         # head-split general kernel; ragged last score block
+    ("k80-dh64", 1, 16, 4, 4, 64, 80, True),       # the same with dh = 64
     ("k1000", 1, 5, 2, 1, 32, 1000, True),
     ("f32", 2, 16, 1, 1, 64, 8, False),
 ]
