@@ -50,7 +50,7 @@ __global__ __launch_bounds__(64) void k_commit_block(const float* __restrict__ D
 // One workgroup per window: member and suffix-member counts of every cluster
 // in LDS (integer atomics, so the counts are exact), then the top-k test and
 // the confidence mask.
-__global__ __launch_bounds__(256) void k_commit_suffix(const int32_t* __restrict__ assign,
+__global__ __launch_bounds__(1024) void k_commit_suffix(const int32_t* __restrict__ assign,
                                                        const int32_t* __restrict__ idx, int k, int N,
                                                        int K, int first,
                                                        const float* __restrict__ conf, float tau_s,
@@ -132,7 +132,7 @@ extern "C" ps_status ps_commit_suffix(const ps_shape* s, const int32_t* assign, 
     if (s->W == 0) return PS_OK;
     hipStream_t stm = (hipStream_t)stream;
     (void)hipGetLastError();
-    PS_LAUNCH("k_commit_suffix", k_commit_suffix, dim3(s->W), dim3(256), 0, stm, assign, idx, k,
+    PS_LAUNCH("k_commit_suffix", k_commit_suffix, dim3(s->W), dim3(1024), 0, stm, assign, idx, k,
               s->N, s->K, block_start + s->Nb, conf, tau_s, flag, commit);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
 }
