@@ -913,6 +913,106 @@ __global__ __launch_bounds__(256) void k_drift_kl(const float* __restrict__ cur,
 }
 
 // ---------------------------------------------------------------------------
+// per-cluster scores and per-token drift in the fused kernels' order, from the
+// stored distributions and the per-row drifts D_hi: one four-wave workgroup
+// per window at K = 16 KB clusters.  Wave v takes heads v, v + 4, ... in
+// order (the fused kernels' head streams), lane l the clusters
+// 16 mb + 4 (l / 16) + r of queries 16 nb + (l % 16), and adds, head by head
+// and query block by query block, exactly the terms k_proxy_bf16 adds in
+// registers (the same exponential of the same stored log-probability, the
+// same product, the same drift D_{h,i}, zero terms for rows past Nb); then
+// the same butterfly over the 16 query lanes and the same sum over the four
+// waves.  So a window's scores and D_i do not depend on whether its
+// log-probabilities came from the fused kernels or from k_proxy_head.  The
+// next head's values are requested before the current head's terms.
+// ---------------------------------------------------------------------------
+template <int KB, int NBQ>
+__global__ __launch_bounds__(256) void k_drift_scores_streams(const float* __restrict__ cur,
+                                                               const float* __restrict__ prev,
+                                                               const float* __restrict__ D_hi, int kind,
+                                                               float* __restrict__ D_i, float* __restrict__ score,
+                                                               int Hq, int Nb)
+{
+    constexpr int K = 16 * KB;
+    __shared__ float sred[4][K];
+    __shared__ float dred[4][16 * NBQ];
+    const int w = blockIdx.x, lane = lane_id(), wave = threadIdx.x >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    float sacc[KB][4];
+    float dacc[NBQ];
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[mb][r] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) dacc[nb] = 0.0f;
+    float4 lc[2][NBQ][KB], lp[2][NBQ][KB];
+    float dv[2][NBQ];
+    auto load = [&](int h, int b) {
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) {
+            const int i = min(16 * nb + r16, Nb - 1);
+            const size_t rowi = ((size_t)w * Hq + h) * Nb + i;
+#pragma unroll
+            for (int mb = 0; mb < KB; ++mb) {
+                lc[b][nb][mb] = *reinterpret_cast<const float4*>(cur + rowi * K + 16 * mb + 4 * q);
+                lp[b][nb][mb] = *reinterpret_cast<const float4*>(prev + rowi * K + 16 * mb + 4 * q);
+            }
+            dv[b][nb] = D_hi[rowi];
+        }
+    };
+    auto add = [&](int b) {
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) {
+            const bool iv = 16 * nb + r16 < Nb;
+            const float D = iv ? dv[b][nb] : 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < KB; ++mb) {
+                const float lv[4] = {lc[b][nb][mb].x, lc[b][nb][mb].y, lc[b][nb][mb].z, lc[b][nb][mb].w};
+                const float pq[4] = {lp[b][nb][mb].x, lp[b][nb][mb].y, lp[b][nb][mb].z, lp[b][nb][mb].w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pv = iv ? exp_hw(lv[r]) : 0.0f;
+                    const float tv = iv ? pv * (lv[r] - pq[r]) : 0.0f;
+                    sacc[mb][r] += score_term(kind, pv, tv, D);
+                }
+            }
+            if (iv) dacc[nb] += D;
+        }
+    };
+    if (wave < Hq) load(wave, 0);
+    for (int h = wave; h < Hq; h += 8) {
+        if (h + 4 < Hq) load(h + 4, 1);
+        add(0);
+        if (h + 4 >= Hq) break;
+        if (h + 8 < Hq) load(h + 8, 0);
+        add(1);
+    }
+    // scores: sum over the 16 query lanes, then over the four waves in order
+#pragma unroll
+    for (int mb = 0; mb < KB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = sacc[mb][r];
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            v += __shfl_xor(v, 4, 64);
+            v += __shfl_xor(v, 8, 64);
+            if (r16 == 0) sred[wave][16 * mb + 4 * q + r] = v;
+        }
+    if (q == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) dred[wave][16 * nb + r16] = dacc[nb];
+    }
+    __syncthreads();
+    const float invH = 1.0f / (float)Hq;
+    for (int k = threadIdx.x; k < K; k += 256)
+        score[(size_t)w * K + k] = (((sred[0][k] + sred[1][k]) + sred[2][k]) + sred[3][k]) * invH;
+    for (int i = threadIdx.x; i < Nb; i += 256)
+        D_i[(size_t)w * Nb + i] = (((dred[0][i] + dred[1][i]) + dred[2][i]) + dred[3][i]) * invH;
+}
+
+// ---------------------------------------------------------------------------
 // per-cluster scores and per-token drift from stored distributions and the
 // per-row drifts D_hi (which the head-parallel proxy kernel writes): grid
 // (W, K / 64) of 16-wave workgroups, lane l of every wave owns cluster
@@ -1124,10 +1224,34 @@ int attn_device_cus()
 // follows in its own pass, whatever the number of windows: k_proxy_head (one
 // wave per block of 16 queries) at K = 128 or 256 and dh = 128, otherwise
 // k_proxy_bf16 with hsplit.
+void enqueue_zero(float* p, size_t n, hipStream_t st);
+
 template <int KB, int NBQ>
 void launch_proxy(const ps_shape* s, const void* Q, const void* Ck, float sigma, float* logp, const float* prev,
                   int kind, int fused, float* D_hi, float* D_i, float* score, hipStream_t st)
 {
+    if constexpr (KB <= 4) {
+        // a few windows (most compute units idle under one workgroup per
+        // window): one wave per (window, head, 16 queries), then the scores
+        // and D_i in the fused kernels' order from the rows' drifts, so the
+        // results are those of the fused kernels bit for bit
+        const int nqb = (s->Nb + 15) / 16;
+        const int64_t units = (int64_t)s->W * s->Hq * nqb;
+        if (fused == 1 && D_hi && s->K == 16 * KB && s->dh == 128 && 4 * (int64_t)s->W < attn_device_cus()) {
+            PS_LAUNCH("k_proxy_head<KB>", (k_proxy_head<KB>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st,
+                      (const uint16_t*)Q, (const uint16_t*)Ck, sigma, logp, prev, prev ? D_hi : nullptr, (int)units,
+                      s->Hq, s->Hkv, s->Nb, nqb);
+            if (prev) {
+                PS_LAUNCH("k_drift_scores_streams<KB, NBQ>", (k_drift_scores_streams<KB, NBQ>), dim3(s->W), dim3(256),
+                          0, st, logp, prev, D_hi, kind, D_i, score, s->Hq, s->Nb);
+            } else {
+                enqueue_zero(D_i, (size_t)s->W * s->Nb, st);
+                enqueue_zero(score, (size_t)s->W * s->K, st);
+                enqueue_zero(D_hi, (size_t)s->W * s->Hq * s->Nb, st);
+            }
+            return;
+        }
+    }
     if constexpr (KB > 4) {
         const int nqb = (s->Nb + 15) / 16;
         const int64_t units = (int64_t)s->W * s->Hq * nqb;
@@ -1258,8 +1382,9 @@ extern "C" ps_status ps_proxy_attn(const ps_shape* s, ps_dtype dtype, const void
         // there); without D_hi to hold the rows' drifts, the fused form up to
         // 256 clusters, and above 256 clusters (several cluster groups, whose
         // rows are finished only after all groups) a drift pass of its own.
-        // The choice depends on the shape and on D_hi only, never on the
-        // number of windows.
+        // These choices depend on the shape and on D_hi only, never on the
+        // number of windows; below 65 clusters a few windows run head-parallel
+        // with the fused form's score order (launch_proxy), bit-identical.
         heads = kb > 4 && (!logp_prev || D_hi || kb > 16);
         rowdrift = heads && logp_prev && kb <= 16;
         fused = !heads && kb <= 16;

@@ -351,6 +351,8 @@ ATT_CASES = [
     ("k256-nb50", 2, 50, 4, 2, 128, 256, True),    # four query blocks, the last ragged
     ("k200", 2, 20, 6, 2, 128, 200, True),         # head-split general kernel; ragged last score block
     ("k80-dh64", 1, 16, 4, 4, 64, 80, True),       # the same with dh = 64
+    ("k32-nb20", 3, 20, 8, 2, 128, 32, True),      # a few windows below 65 clusters: head-parallel
+    ("k16", 1, 8, 4, 4, 128, 16, True),
     ("k1000", 1, 5, 2, 1, 32, 1000, True),
     ("f32", 2, 16, 1, 1, 64, 8, False),
 ]
@@ -393,6 +395,10 @@ def test_proxy_attn_and_drift(P, case, kind):
     torch.cuda.synchronize()
     assert np.array_equal(host(lc), gl)
     assert close(host(Di2), kl["D_i"]) and close(host(sc2), kl["score"])
+    if bf and K <= 64:
+        # below 65 clusters both forms add the scores and D_i in one order
+        assert np.array_equal(host(Di2).view(np.uint32), host(Di).view(np.uint32))
+        assert np.array_equal(host(sc2).view(np.uint32), host(sc).view(np.uint32))
     # window formation: no previous distribution -> zeros, the same logits
     lc.zero_()
     P.ps_proxy_attn(s, dt, dev(Q), dev(Ck), sigma, lc, None, kind, Dhi, Di, sc)
