@@ -353,6 +353,8 @@ ATT_CASES = [
     ("k80-dh64", 1, 16, 4, 4, 64, 80, True),       # the same with dh = 64
     ("k32-nb20", 3, 20, 8, 2, 128, 32, True),      # a few windows below 65 clusters: head-parallel
     ("k16", 1, 8, 4, 4, 128, 16, True),
+    ("k64-hq6-gqa", 2, 32, 6, 3, 128, 64, True),  # heads per wave stream uneven (2, 2, 1, 1)
+    ("k256-mqa", 2, 32, 8, 1, 128, 256, True),     # one KV head for all query heads
     ("k1000", 1, 5, 2, 1, 32, 1000, True),
     ("f32", 2, 16, 1, 1, 64, 8, False),
 ]
