@@ -392,31 +392,25 @@ __global__ __launch_bounds__(256) void k_residual(const T* __restrict__ H, const
 // order within a cluster is unspecified: no result depends on it).
 // Assignments outside [0, K) count as cluster 0, as the coder reads them.
 // One workgroup per window; the first also clears the count of listed rows.
-__global__ __launch_bounds__(256) void k_group_rows(const int32_t* __restrict__ assign,
-                                                     int32_t* __restrict__ perm, int32_t* __restrict__ listed,
-                                                     int N, int K)
+__global__ __launch_bounds__(1024) void k_group_rows(const int32_t* __restrict__ assign,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ listed,
+                                                      int N, int K)
 {
     __shared__ int base[kMaxK];
-    __shared__ int wsum[4];
+    __shared__ int wsum[16];
     const int w = blockIdx.x, t = threadIdx.x;
     if (w == 0 && t == 0) *listed = 0;
-    for (int c = t; c < K; c += 256) base[c] = 0;
+    for (int c = t; c < K; c += 1024) base[c] = 0;
     __syncthreads();
     const int32_t* a = assign + (size_t)w * N;
-    for (int j = t; j < N; j += 256) {
+    for (int j = t; j < N; j += 1024) {
         const int c = a[j];
         atomicAdd(&base[(unsigned)c < (unsigned)K ? c : 0], 1);
     }
     __syncthreads();
-    // exclusive prefix sum of the counts; thread t owns clusters 4t .. 4t + 3
-    int v[4], sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = 4 * t + i;
-        v[i] = c < K ? base[c] : 0;
-        sum += v[i];
-    }
-    int x = sum;
+    // exclusive prefix sum of the counts; thread t owns cluster t
+    const int v = t < K ? base[t] : 0;
+    int x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(x, o, 64);
@@ -424,16 +418,11 @@ __global__ __launch_bounds__(256) void k_group_rows(const int32_t* __restrict__ 
     }
     if ((t & 63) == 63) wsum[t >> 6] = x;
     __syncthreads();
-    int off = x - sum;
+    int off = x - v;
     for (int q = 0; q < (t >> 6); ++q) off += wsum[q];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = 4 * t + i;
-        if (c < K) base[c] = off;
-        off += v[i];
-    }
+    if (t < K) base[t] = off;
     __syncthreads();
-    for (int j = t; j < N; j += 256) {
+    for (int j = t; j < N; j += 1024) {
         const int c = a[j];
         const int p = atomicAdd(&base[(unsigned)c < (unsigned)K ? c : 0], 1);
         perm[(size_t)w * N + p] = j;
@@ -676,7 +665,7 @@ void launch_residual_grouped(const ps_shape* s, const void* H, const float* rn, 
     int32_t* perm = ws;
     int32_t* list = ws + rows;
     int32_t* listed = ws + 2 * rows;
-    PS_LAUNCH("k_group_rows", k_group_rows, dim3(s->W), dim3(256), 0, st, a, perm, listed, s->N, s->K);
+    PS_LAUNCH("k_group_rows", k_group_rows, dim3(s->W), dim3(1024), 0, st, a, perm, listed, s->N, s->K);
     const int tiles = (s->N + 4 * kGroupRows - 1) / (4 * kGroupRows);
     const int nblocks = s->W * tiles;
     if (s->d / 16 == 64 * BPL)
