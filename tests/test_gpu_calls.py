@@ -355,6 +355,8 @@ ATT_CASES = [
     ("k16", 1, 8, 4, 4, 128, 16, True),
     ("k64-hq6-gqa", 2, 32, 6, 3, 128, 64, True),  # heads per wave stream uneven (2, 2, 1, 1)
     ("k256-mqa", 2, 32, 8, 1, 128, 256, True),     # one KV head for all query heads
+    ("k256-nb64", 1, 64, 4, 4, 128, 256, True),    # the largest decode block the call accepts
+    ("k64-nb64", 1, 64, 8, 8, 128, 64, True),
     ("k1000", 1, 5, 2, 1, 32, 1000, True),
     ("f32", 2, 16, 1, 1, 64, 8, False),
 ]
