@@ -137,6 +137,20 @@ MUTATIONS = [
     ("unit rows by a rounded reciprocal", "return n > 0.0f ? h / n : 0.0f;", "return n > 0.0f ? h * (1.0f / n) : 0.0f;",
      [(T_km.test_strided_init_rows, ()), (T_km.test_k1_is_normalised_mean, ()),
       (T_km.test_centres_are_unit_and_member_means, ()), (T_fmt.test_nvfp4_error_bound_random_rows, ())]),
+    ("centre divided by the member count instead of its norm", "(float)(S[e] / nrm);", "(float)(S[e] / cnt);",
+     [(T_km.test_k1_is_normalised_mean, ()), (T_km.test_centres_are_unit_and_member_means, ())]),
+    ("member rows weighted by their norm instead of its reciprocal", "const double inv = 1.0 / (double)rn[j];",
+     "const double inv = (double)rn[j];",
+     [(T_km.test_k1_is_normalised_mean, ()), (T_km.test_centres_are_unit_and_member_means, ())]),
+    ("residual coded from h instead of h / n", "float x = unit_elem(ld(H, dtype, row * d + e), n);",
+     "float x = ld(H, dtype, row * d + e);",
+     [(T_fmt.test_nvfp4_round_trip_exact_on_representable_rows, ()), (T_fmt.test_nvfp4_error_bound_random_rows, ())]),
+    ("gather lists the members in descending order",
+     "        for (int j = 0; j < N; ++j) {\n            const size_t row = (size_t)w * N + j;\n"
+     "            int a = assign[row];\n            if (a < 0 || a >= K || !sel[a]) continue;",
+     "        for (int j = N - 1; j >= 0; --j) {\n            const size_t row = (size_t)w * N + j;\n"
+     "            int a = assign[row];\n            if (a < 0 || a >= K || !sel[a]) continue;",
+     [(T_tg.test_gather_matches_set_filter, ("ample",)), (T_tg.test_gather_matches_set_filter, ("short",))]),
 ]
 
 
