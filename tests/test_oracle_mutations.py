@@ -151,6 +151,11 @@ MUTATIONS = [
      "        for (int j = N - 1; j >= 0; --j) {\n            const size_t row = (size_t)w * N + j;\n"
      "            int a = assign[row];\n            if (a < 0 || a >= K || !sel[a]) continue;",
      [(T_tg.test_gather_matches_set_filter, ("ample",)), (T_tg.test_gather_matches_set_filter, ("short",))]),
+    ("queries read head-major", "const size_t qo = (((size_t)w * Nb + i) * Hq + h) * dh;",
+     "const size_t qo = (((size_t)w * Hq + h) * Nb + i) * dh;",
+     [(T_attn.test_k_equals_n_is_textbook_attention, (4, 4)), (T_attn.test_k_equals_n_is_textbook_attention, (6, 2))]),
+    ("log-sum-exp without the max shift", "const double lse = zmax + log(se);", "const double lse = log(se);",
+     [(T_attn.test_logp_normalised, ()), (T_attn.test_k_equals_n_is_textbook_attention, (4, 4))]),
 ]
 
 
