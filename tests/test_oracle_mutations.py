@@ -156,6 +156,16 @@ MUTATIONS = [
      [(T_attn.test_k_equals_n_is_textbook_attention, (4, 4)), (T_attn.test_k_equals_n_is_textbook_attention, (6, 2))]),
     ("log-sum-exp without the max shift", "const double lse = zmax + log(se);", "const double lse = log(se);",
      [(T_attn.test_logp_normalised, ()), (T_attn.test_k_equals_n_is_textbook_attention, (4, 4))]),
+    ("block scale from the first half of the block",
+     "for (int e = 16 * b; e < 16 * b + 16; ++e)\n                    if (fabsf(r[e]) > Ab) Ab = fabsf(r[e]);",
+     "for (int e = 16 * b; e < 16 * b + 8; ++e)\n                    if (fabsf(r[e]) > Ab) Ab = fabsf(r[e]);",
+     [(T_fmt.test_nvfp4_round_trip_exact_on_representable_rows, ()), (T_fmt.test_nvfp4_error_bound_random_rows, ())]),
+    ("code nibbles swapped", "cr[e / 2] = (uint8_t)(lo | (hi << 4));", "cr[e / 2] = (uint8_t)(hi | (lo << 4));",
+     [(T_fmt.test_nvfp4_round_trip_exact_on_representable_rows, ()), (T_fmt.test_nvfp4_error_bound_random_rows, ())]),
+    ("row norm skips the last element",
+     "    for (int e = 0; e < d; ++e) {\n        double h = (double)ld(H, dtype, row_off + (size_t)e);",
+     "    for (int e = 0; e < d - 1; ++e) {\n        double h = (double)ld(H, dtype, row_off + (size_t)e);",
+     [(T_km.test_row_norms_fp64_exact_on_small_integers, ())]),
 ]
 
 
