@@ -55,6 +55,12 @@ def kernel_work(name, cfg, gathered=None):
         # clusters reads the fp32 centres
         ce = 4 if (name.startswith("k_assign_bf16") and name.endswith("true>")) else e
         return W * N * d * e + W * K * d * ce + W * N * 4, 2.0 * W * N * K * d
+    if name.startswith("k_update_code"):
+        # the first update (every cluster rebuilt) and the NVFP4 codes and
+        # scales of every row, coded against the new centres; the rows are
+        # read once (coding re-reads them from the caches)
+        return (W * N * d * e + 2 * W * N * 4 + W * K * d * (4 + e) + W * (K + 1) * 4
+                + W * N * d // 2 + W * N * d // 16 + W * N * 4, W * N * d * 10.0)
     if name.startswith("k_update"):
         return W * N * d * e + 2 * W * N * 4 + W * K * d * (4 + e) + W * (K + 1) * 4, W * N * d * 2.0
     if name.startswith("k_residual_grouped") or name.startswith("k_residual<"):
@@ -419,7 +425,7 @@ def kernel_figures(cfg, prof, steps, gathered, ms_per_step):
         if len(v) > 5 and v[5]:
             breakdown[k]["work_fraction"] = done(v)
         work = kernel_work(k, cfg, gathered)
-        if work and not k.startswith("k_update"):   # the update's later passes re-sum dirty clusters only
+        if work:   # scaled by the part of the work done (the later updates re-sum changed clusters only)
             breakdown[k]["algorithmic_GB_per_launch"] = work[0] * done(v) / 1e9
             breakdown[k]["achieved_GBs"] = work[0] * done(v) / (v[1] / v[0] * 1e-3) / 1e9
     roof = None
@@ -455,7 +461,7 @@ def kernel_figures(cfg, prof, steps, gathered, ms_per_step):
     for kname, v in kernels.items():
         work = kernel_work(kname, cfg, gathered)
         if work:
-            moved += work[0] * (steps if kname.startswith("k_update") else v[0] * done(v))
+            moved += work[0] * v[0] * done(v)
             if kname.startswith("k_assign") or kname.startswith("k_proxy"):
                 ran += work[1] * v[0] * done(v)
     ran = ran / steps if kernels else cf

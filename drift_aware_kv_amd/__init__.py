@@ -30,7 +30,7 @@ PS_ERR_SCRATCH_LIMIT = 9
 PS_STATIC_SCRATCH_BYTES = 64 << 20     # the library's static K-Means scratch per device
 
 EXPORTS = ("ps_status_string", "ps_workspace_size", "ps_kmeans_fit", "ps_kmeans_fit_static",
-           "ps_residual_nvfp4",
+           "ps_kmeans_fit_nvfp4", "ps_residual_nvfp4",
            "ps_proxy_attn", "ps_drift_kl", "ps_topk_clusters", "ps_refresh_gather",
            "ps_drift_cosine", "ps_commit_block", "ps_commit_suffix", "ps_profile_begin", "ps_profile_end", "ps_profile_summary")
 
@@ -75,6 +75,8 @@ def lib():
                                     P, P, ctypes.c_size_t, P]
         L.ps_kmeans_fit_static.argtypes = [SP, I, P, P, I, ctypes.c_int32, ctypes.c_uint32, P, P, P, P,
                                            P, P, P]
+        L.ps_kmeans_fit_nvfp4.argtypes = [SP, I, P, P, I, ctypes.c_int32, ctypes.c_uint32, P, P, P, P, P,
+                                          P, P, P, P, P, ctypes.c_size_t, P]
         L.ps_residual_nvfp4.argtypes = [SP, I, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.ps_proxy_attn.argtypes = [SP, I, P, P, ctypes.c_float, P, P, I, P, P, P, P]
         L.ps_drift_kl.argtypes = [SP, P, P, I, P, P, P, P]
@@ -208,6 +210,26 @@ def ps_kmeans_fit_static(s: Shape, dtype, H, Kr, init, iters, C, assign, counts,
         _ptr(counts, s.W * s.K, 4, "counts"), _ptr(row_norm, s.W * s.N, 4, "row_norm"),
         _ptr(Ck, s.W * s.K * KV, e, "Ck", True), _ptr(objective, s.W, 8, "objective", True),
         _stream(stream)), "ps_kmeans_fit_static")
+
+
+def ps_kmeans_fit_nvfp4(s: Shape, dtype, H, Kr, init, iters, C, assign, counts, row_norm, codes, bscale,
+                        rscale, Ck=None, objective=None, ws=None, stream=None, flags=0):
+    """ps_kmeans_fit followed by ps_residual_nvfp4 of its outputs, in one call
+    (the same results); ws of at least ps_workspace_size bytes."""
+    e = _es(dtype)
+    KV = s.Hkv * s.dh
+    wsb = ps_workspace_size(s, dtype)
+    if ws is None:
+        raise ValueError("ws is required (see workspace())")
+    _check(lib().ps_kmeans_fit_nvfp4(
+        _cs(s), dtype, _ptr(H, s.W * s.N * s.d, e, "H"),
+        _ptr(Kr, s.W * s.N * KV, e, "Kr", True), init, iters, flags,
+        _ptr(C, s.W * s.K * s.d, 4, "C"), _ptr(assign, s.W * s.N, 4, "assign"),
+        _ptr(counts, s.W * s.K, 4, "counts"), _ptr(row_norm, s.W * s.N, 4, "row_norm"),
+        _ptr(Ck, s.W * s.K * KV, e, "Ck", True), _ptr(objective, s.W, 8, "objective", True),
+        _ptr(codes, s.W * s.N * s.d // 2, 1, "codes"), _ptr(bscale, s.W * s.N * s.d // 16, 1, "bscale"),
+        _ptr(rscale, s.W * s.N, 4, "rscale"),
+        _ptr(ws, wsb, 1, "ws"), ws.numel(), _stream(stream)), "ps_kmeans_fit_nvfp4")
 
 
 def ps_residual_nvfp4(s: Shape, dtype, H, row_norm, C, assign, codes, bscale, rscale, ws=None,

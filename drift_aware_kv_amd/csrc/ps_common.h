@@ -204,4 +204,11 @@ inline ps_status check_heads(const ps_shape* s)
 
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The exact NVFP4 coder over the bf16 rows listed in list[0 .. *listed)
+// (rows of up to 4096 elements), against their clusters' centres in C.
+// Enqueued on st.
+void residual_listed(const ps_shape* s, const uint16_t* H, const float* row_norm, const float* C,
+                     const int32_t* assign, const int32_t* list, const int32_t* listed, uint8_t* codes,
+                     uint8_t* bscale, float* rscale, hipStream_t st);
+
 }  // namespace ps_host

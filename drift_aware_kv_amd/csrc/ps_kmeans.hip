@@ -16,6 +16,7 @@
 //           first iteration only clusters whose member set changed run.
 // After the last iteration the keys kernel averages the member key rows.
 #include "ps_common.h"
+#include "ps_nvfp4_row.h"
 
 #include <math.h>
 
@@ -862,13 +863,14 @@ __global__ __launch_bounds__(64 * kBucketWaves) void k_bucket(const int32_t* __r
                                                                int32_t* __restrict__ offs,
                                                                const int32_t* __restrict__ dirty,
                                                                int32_t* __restrict__ conv, int N, int K, int first,
-                                                               int fixed_point_exit)
+                                                               int fixed_point_exit, int32_t* __restrict__ listed)
 {
     constexpr int NW = kBucketWaves;
     __shared__ int cnt[NW][kMaxK];
     const int w = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     if (first) {
         if (tid == 0) conv[w] = 0;
+        if (listed && w == 0 && tid == 0) *listed = 0;   // rows listed by the coding update
     } else {
         if (conv[w]) return;
         bool any = false;
@@ -1040,7 +1042,8 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
                                                  const int32_t* __restrict__ offs, float* __restrict__ C,
                                                  uint16_t* __restrict__ Cb, int32_t* __restrict__ counts,
                                                  double* __restrict__ nrm_out, int32_t* __restrict__ dirty,
-                                                 int N, int d, int K, int nblocks, int all, int* __restrict__ work)
+                                                 int32_t* __restrict__ stale, int N, int d, int K, int nblocks,
+                                                 int all, int* __restrict__ work)
 {
     __shared__ double red[4];
     const int Lg = xcd_remap(blockIdx.x, nblocks);
@@ -1048,6 +1051,8 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
     // an unchanged member set gives a bit-identical sum: keep the centre
     if (!all && !dirty[(size_t)w * K + k]) return;
     if (work && threadIdx.x == 0) atomicAdd(work, 1);   // kernel timer: one cluster re-summed
+    // a centre rebuilt after the update that coded the rows: its members are coded again
+    if (stale && threadIdx.x == 0) stale[(size_t)w * K + k] = 1;
     const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
     const int32_t* pm = perm + (size_t)w * N;
     const T* Hw = H + (size_t)w * N * d;
@@ -1113,6 +1118,166 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
             }
         }
     }
+}
+
+// The member rows pm[beg .. end) of one cluster (rows of one window: Hw,
+// rn, window row offset wrow) coded against the centre cs (LDS, fp32) by the
+// workgroup's four waves, one row per wave at a time, with the coder's fast
+// path; rows it declines are listed for the exact coder.
+template <int BPL, bool FULL>
+__device__ __forceinline__ void code_members(const uint16_t* __restrict__ Hw, const float* __restrict__ rn,
+                                             const int32_t* __restrict__ pm, int beg, int end, const float* cs,
+                                             uint8_t* __restrict__ codes, uint8_t* __restrict__ bscale,
+                                             float* __restrict__ rscale, int32_t* __restrict__ list,
+                                             int32_t* __restrict__ listed, size_t wrow, int d)
+{
+    const int lane = lane_id(), nb = d >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    for (int m = beg + wave; m < end; m += 4) {
+        const int j = pm[m];
+        const size_t row = wrow + j;
+        uint4 hq[BPL][2];
+        load_hblocks<uint16_t, 64, BPL>(Hw + (size_t)j * d, lane, nb, hq);
+        // the centre's blocks from LDS for each row (registers stay free between rows)
+        float cv[BPL][16];
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+            const float4* cp = reinterpret_cast<const float4*>(cs + 16 * min(lane + 64 * b, nb - 1));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = cp[q];
+                cv[b][4 * q] = v.x; cv[b][4 * q + 1] = v.y; cv[b][4 * q + 2] = v.z; cv[b][4 * q + 3] = v.w;
+            }
+        }
+        if (!residual_row_fast<uint16_t, 1, BPL, FULL>(hq, cv, rn[j], codes + row * (size_t)(d >> 1),
+                                                       bscale + row * (size_t)(d >> 4), rscale + row, d, nullptr)) {
+            if (lane == 0) list[atomicAdd(listed, 1)] = (int32_t)row;
+        }
+    }
+}
+
+// The first update of a call that also codes the residuals (bf16 rows of up
+// to 4096 elements): each workgroup rebuilds its cluster's centre exactly as
+// k_update does (every cluster, as in any first update), then its four waves
+// code the cluster's member rows against that centre with the coder's fast
+// path, one row per wave at a time, while the rows just summed are still in
+// the caches.  Rows the fast path declines are listed for the exact coder.
+// A later update that rebuilds a centre marks it `stale`; after the last
+// iteration only those clusters' rows are coded again, so every row ends up
+// coded against the final centre of its final cluster, as a separate coder
+// call would code it.  Three workgroups per compute unit (168 registers).
+template <int CH, int BPL, bool FULL>
+__global__ __launch_bounds__(256, 3) void k_update_code(const uint16_t* __restrict__ H,
+                                                        const float* __restrict__ row_norm,
+                                                        const int32_t* __restrict__ perm,
+                                                        const int32_t* __restrict__ offs, float* __restrict__ C,
+                                                        uint16_t* __restrict__ Cb, int32_t* __restrict__ counts,
+                                                        double* __restrict__ nrm_out, int32_t* __restrict__ dirty,
+                                                        int32_t* __restrict__ stale, uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ bscale, float* __restrict__ rscale,
+                                                        int32_t* __restrict__ list, int32_t* __restrict__ listed,
+                                                        int N, int d, int K, int nblocks)
+{
+    __shared__ double red[4];
+    __shared__ int mid[256];
+    __shared__ double mw[256];
+    __shared__ int wcnt[4];
+    __shared__ float cs[4096];                   // the centre, for the coding waves
+    const int Lg = xcd_remap(blockIdx.x, nblocks);
+    const int w = Lg / K, k = Lg - w * K;
+    const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
+    const int32_t* pm = perm + (size_t)w * N;
+    const uint16_t* Hw = H + (size_t)w * N * d;
+    const float* rn = row_norm + (size_t)w * N;
+
+    double acc[CH][8];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[c][i] = 0.0;
+    for (int b0 = beg; b0 < end; b0 += 256) {
+        const int nv = stage_members(pm, b0, end, mid, mw, wcnt, [&](int j, double& wt) {
+            const float n = rn[j];
+            if (!(n > 0.0f)) return false;
+            wt = 1.0 / (double)n;
+            return true;
+        });
+        member_sums<uint16_t, CH, true>(Hw, d, 0, mid, mw, nv, acc);
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fma(acc[c][i], acc[c][i], ss);
+    ss = wave_sum_d(ss);
+    if (lane_id() == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const double nrm = sqrt(red[0] + red[1] + red[2] + red[3]);
+    const int nk = end - beg;
+    if (threadIdx.x == 0) {
+        counts[(size_t)w * K + k] = nk;
+        nrm_out[(size_t)w * K + k] = nrm;
+        dirty[(size_t)w * K + k] = 0;
+        stale[(size_t)w * K + k] = 0;
+    }
+    const bool fresh = nk > 0 && nrm > 0.0;
+    float* c_at = C + ((size_t)w * K + k) * d;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int e = (threadIdx.x + 256 * c) * 8;
+        if (e < d) {
+            float v[8];
+            if (fresh) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = (float)(acc[c][i] / nrm);
+                store8(c_at + e, v);
+            } else {
+                load8(c_at + e, v);              // a kept centre
+            }
+            if (Cb) store8(Cb + ((size_t)w * K + k) * d + e, v);
+            if (nk > 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) cs[e + i] = v[i];
+            }
+        }
+    }
+    if (nk == 0) return;                         // workgroup-uniform
+    __syncthreads();
+    code_members<BPL, FULL>(Hw, rn, pm, beg, end, cs, codes, bscale, rscale, list, listed, (size_t)w * N, d);
+}
+
+// Coding again after the last iteration: one workgroup per (window, cluster)
+// of a cluster rebuilt after the coding update (stale); the others exit at
+// once.  The centre is the final one in C.
+template <int BPL, bool FULL>
+__global__ __launch_bounds__(256, 3) void k_code_stale(const uint16_t* __restrict__ H,
+                                                       const float* __restrict__ row_norm,
+                                                       const int32_t* __restrict__ perm,
+                                                       const int32_t* __restrict__ offs,
+                                                       const float* __restrict__ C,
+                                                       const int32_t* __restrict__ stale,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ bscale,
+                                                       float* __restrict__ rscale, int32_t* __restrict__ list,
+                                                       int32_t* __restrict__ listed, int N, int d, int K,
+                                                       int nblocks, int* __restrict__ work)
+{
+    __shared__ float cs[4096];
+    const int Lg = xcd_remap(blockIdx.x, nblocks);
+    const int w = Lg / K, k = Lg - w * K;
+    if (!stale[(size_t)w * K + k]) return;
+    const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
+    if (end == beg) return;
+    if (work && threadIdx.x == 0) atomicAdd(work, 1);   // kernel timer: one cluster coded
+    const float* c = C + ((size_t)w * K + k) * d;
+    for (int e = 8 * (int)threadIdx.x; e < d; e += 8 * 256) {
+        float v[8];
+        load8(c + e, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cs[e + i] = v[i];
+    }
+    __syncthreads();
+    code_members<BPL, FULL>(H + (size_t)w * N * d, row_norm + (size_t)w * N, perm + (size_t)w * N, beg, end, cs,
+                            codes, bscale, rscale, list, listed, (size_t)w * N, d);
 }
 
 // centroid keys: mean of the member key rows, fp64 in ascending member order,
@@ -1182,10 +1347,14 @@ struct KmWs {
     double* nrm;
     double* fm;
     float* fn;
+    int32_t* stale;    // with coding: clusters rebuilt after the coding update
+    int32_t* list;     // with coding: rows for the exact coder (a row at most twice:
+                       // by the coding update and again if its cluster is rebuilt), and their count
+    int32_t* listed;
     size_t bytes;
 };
 
-KmWs km_layout(const ps_shape* s, int dtype, void* base)
+KmWs km_layout(const ps_shape* s, int dtype, void* base, bool coding = false)
 {
     using ps_host::round256;
     const size_t W = (size_t)s->W, N = (size_t)s->N, K = (size_t)s->K, d = (size_t)s->d;
@@ -1205,6 +1374,11 @@ KmWs km_layout(const ps_shape* s, int dtype, void* base)
     L.nrm = (double*)take(W * K * 8);
     L.fm = (double*)take(W * N * 8);
     L.fn = (float*)take(W * N * 4);
+    if (coding) {
+        L.stale = (int32_t*)take(W * K * 4);
+        L.list = (int32_t*)take(2 * W * N * 4);
+        L.listed = (int32_t*)take(16);
+    }
     L.bytes = off;
     return L;
 }
@@ -1215,7 +1389,52 @@ void launch_update(const ps_shape* s, const void* H, const float* rn, const KmWs
 {
     const int nblocks = s->W * s->K;
     PS_LAUNCH_COUNTED("k_update<T, CH>", nblocks, (k_update<T, CH>), dim3(nblocks), dim3(256), 0, st, (const T*)H,
-                      rn, ws.perm, ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, s->N, s->d, s->K, nblocks, all);
+                      rn, ws.perm, ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, ws.stale, s->N, s->d, s->K, nblocks,
+                      all);
+}
+
+// outputs of the residual coding folded into a K-Means call
+struct Coding {
+    uint8_t* codes;
+    uint8_t* bscale;
+    float* rscale;
+};
+
+// The coding update applies to bf16 rows of up to 4096 elements (the
+// coder's one-wave-per-row form) on batches of fewer than 2^31 rows.
+bool coding_update_fits(const ps_shape* s, ps_dtype dtype)
+{
+    return dtype == PS_BF16 && s->d <= 4096 && (int64_t)s->W * s->N < ((int64_t)1 << 31);
+}
+
+template <int CH, int BPL>
+void launch_update_code(const ps_shape* s, const void* H, const float* rn, const KmWs& ws, float* C,
+                        int32_t* counts, const Coding& cd, hipStream_t st)
+{
+    const int nblocks = s->W * s->K;
+    if (s->d / 16 == 64 * BPL)
+        PS_LAUNCH("k_update_code<CH, BPL, FULL>", (k_update_code<CH, BPL, true>), dim3(nblocks), dim3(256), 0, st,
+                  (const uint16_t*)H, rn, ws.perm, ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, ws.stale, cd.codes,
+                  cd.bscale, cd.rscale, ws.list, ws.listed, s->N, s->d, s->K, nblocks);
+    else
+        PS_LAUNCH("k_update_code<CH, BPL, FULL>", (k_update_code<CH, BPL, false>), dim3(nblocks), dim3(256), 0, st,
+                  (const uint16_t*)H, rn, ws.perm, ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, ws.stale, cd.codes,
+                  cd.bscale, cd.rscale, ws.list, ws.listed, s->N, s->d, s->K, nblocks);
+}
+
+template <int BPL>
+void launch_code_stale(const ps_shape* s, const void* H, const float* rn, const KmWs& ws, const float* C,
+                       const Coding& cd, hipStream_t st)
+{
+    const int nblocks = s->W * s->K;
+    if (s->d / 16 == 64 * BPL)
+        PS_LAUNCH_COUNTED("k_code_stale<BPL, FULL>", nblocks, (k_code_stale<BPL, true>), dim3(nblocks), dim3(256), 0,
+                          st, (const uint16_t*)H, rn, ws.perm, ws.offs, C, ws.stale, cd.codes, cd.bscale, cd.rscale,
+                          ws.list, ws.listed, s->N, s->d, s->K, nblocks);
+    else
+        PS_LAUNCH_COUNTED("k_code_stale<BPL, FULL>", nblocks, (k_code_stale<BPL, false>), dim3(nblocks), dim3(256), 0,
+                          st, (const uint16_t*)H, rn, ws.perm, ws.offs, C, ws.stale, cd.codes, cd.bscale, cd.rscale,
+                          ws.list, ws.listed, s->N, s->d, s->K, nblocks);
 }
 
 template <bool FIRST>
@@ -1323,7 +1542,8 @@ extern "C" ps_status ps_workspace_size(const ps_shape* s, ps_dtype dtype, size_t
     if (!ps_host::dtype_ok(dtype)) return PS_ERR_DTYPE;
     ps_status st = ps_host::check_clusters(s);
     if (st != PS_OK) return st;
-    *bytes = std::max(km_layout(s, dtype, nullptr).bytes, ps_host::residual_ws_bytes(s));
+    *bytes = std::max(km_layout(s, dtype, nullptr, coding_update_fits(s, dtype)).bytes,
+                      ps_host::residual_ws_bytes(s));
     return PS_OK;
 }
 
@@ -1353,23 +1573,26 @@ ps_status kmeans_fit_check(const ps_shape* s, ps_dtype dtype, const void* H, con
     return PS_OK;
 }
 
+// The K-Means call; with `cd`, the rows' residual coding too (the caller has
+// checked the coder's arguments and that ws holds km_layout(.., fuse) bytes).
 ps_status kmeans_fit_impl(const ps_shape* s, ps_dtype dtype, const void* H, const void* Kr, ps_init init,
                           int32_t iters, uint32_t flags, float* C, int32_t* assign, int32_t* counts,
                           float* row_norm, void* Ck, double* objective, void* ws, size_t ws_bytes,
-                          void* stream)
+                          void* stream, const Coding* cd = nullptr)
 {
     using namespace ps_host;
     ps_status st = kmeans_fit_check(s, dtype, H, Kr, init, iters, flags, C, assign, counts, row_norm, Ck,
                                     objective);
     if (st != PS_OK) return st;
-    const KmWs need = km_layout(s, dtype, nullptr);
+    const bool fuse = cd && coding_update_fits(s, dtype);
+    const KmWs need = km_layout(s, dtype, nullptr, fuse);
     if (!ws || ws_bytes < need.bytes) return PS_ERR_WORKSPACE;
     if (!aligned16(ws)) return PS_ERR_ALIGN;
     if (s->W == 0) return PS_OK;
 
     hipStream_t stm = (hipStream_t)stream;
     (void)hipGetLastError();
-    const KmWs L = km_layout(s, dtype, ws);
+    const KmWs L = km_layout(s, dtype, ws, fuse);
     const int W = s->W, N = s->N, d = s->d, K = s->K;
     const bool bf = dtype == PS_BF16;
 
@@ -1413,8 +1636,13 @@ ps_status kmeans_fit_impl(const ps_shape* s, ps_dtype dtype, const void* H, cons
                               stm, (const float*)H, C, assign, row_norm, W, N, d, K, first, L.dirty, L.conv);
         }
         PS_LAUNCH("k_bucket", k_bucket, dim3(W), dim3(64 * kBucketWaves), 0, stm, assign, L.perm, L.offs, L.dirty, L.conv, N, K,
-                  first, fpx);
-        if (bf) {
+                  first, fpx, L.listed);
+        if (fuse && first) {
+            const int nb = d / 16;
+            if (nb <= 64)       launch_update_code<1, 1>(s, H, row_norm, L, C, counts, *cd, stm);
+            else if (nb <= 128) launch_update_code<1, 2>(s, H, row_norm, L, C, counts, *cd, stm);
+            else                launch_update_code<2, 4>(s, H, row_norm, L, C, counts, *cd, stm);
+        } else if (bf) {
             switch (CH) {
             case 1: launch_update<uint16_t, 1>(s, H, row_norm, L, C, counts, first, stm); break;
             case 2: launch_update<uint16_t, 2>(s, H, row_norm, L, C, counts, first, stm); break;
@@ -1438,7 +1666,21 @@ ps_status kmeans_fit_impl(const ps_shape* s, ps_dtype dtype, const void* H, cons
     }
     if (objective)
         PS_LAUNCH("k_objective", k_objective, dim3(W), dim3(64), 0, stm, L.nrm, objective, K);
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_DEVICE;
+    if (fuse) {
+        // the rows of clusters rebuilt after the coding update, then every
+        // row the fast path declined
+        const int nb = d / 16;
+        if (nb <= 64)       launch_code_stale<1>(s, H, row_norm, L, C, *cd, stm);
+        else if (nb <= 128) launch_code_stale<2>(s, H, row_norm, L, C, *cd, stm);
+        else                launch_code_stale<4>(s, H, row_norm, L, C, *cd, stm);
+        residual_listed(s, (const uint16_t*)H, row_norm, C, assign, L.list, L.listed, cd->codes, cd->bscale,
+                        cd->rscale, stm);
+    }
+    if (hipGetLastError() != hipSuccess) return PS_ERR_DEVICE;
+    if (cd && !fuse)   // the coder as its own call, on the workspace the fit no longer needs
+        return ps_residual_nvfp4(s, dtype, H, row_norm, C, assign, cd->codes, cd->bscale, cd->rscale, ws,
+                                 ws_bytes, stream);
+    return PS_OK;
 }
 
 }  // namespace
@@ -1450,6 +1692,26 @@ extern "C" ps_status ps_kmeans_fit(const ps_shape* s, ps_dtype dtype, const void
 {
     return kmeans_fit_impl(s, dtype, H, Kr, init, iters, flags, C, assign, counts, row_norm, Ck, objective, ws,
                            ws_bytes, stream);
+}
+
+extern "C" ps_status ps_kmeans_fit_nvfp4(const ps_shape* s, ps_dtype dtype, const void* H, const void* Kr,
+                                         ps_init init, int32_t iters, uint32_t flags, float* C, int32_t* assign,
+                                         int32_t* counts, float* row_norm, void* Ck, double* objective,
+                                         uint8_t* codes, uint8_t* bscale, float* rscale, void* ws,
+                                         size_t ws_bytes, void* stream)
+{
+    using namespace ps_host;
+    ps_status st = kmeans_fit_check(s, dtype, H, Kr, init, iters, flags, C, assign, counts, row_norm, Ck,
+                                    objective);
+    if (st != PS_OK) return st;
+    if (!codes || !bscale || !rscale) return PS_ERR_NULL;
+    if (!aligned16(codes) || !aligned16(bscale) || !aligned16(rscale)) return PS_ERR_ALIGN;
+    const size_t need = std::max(km_layout(s, dtype, nullptr, coding_update_fits(s, dtype)).bytes,
+                                 residual_ws_bytes(s));
+    if (!ws || ws_bytes < need) return PS_ERR_WORKSPACE;
+    const Coding cd{codes, bscale, rscale};
+    return kmeans_fit_impl(s, dtype, H, Kr, init, iters, flags, C, assign, counts, row_norm, Ck, objective, ws,
+                           ws_bytes, stream, &cd);
 }
 
 // ---------------------------------------------------------------------------

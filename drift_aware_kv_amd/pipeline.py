@@ -32,8 +32,8 @@ import torch
 
 from . import (PS_BF16, PS_F32, PS_INIT_FARTHEST, PS_INIT_GIVEN, PS_INIT_STRIDED,
                PS_SCORE_KL_SHARE, Shape, ps_commit_block, ps_commit_suffix, ps_drift_cosine,
-               ps_kmeans_fit, ps_proxy_attn, ps_refresh_gather, ps_residual_nvfp4, ps_topk_clusters,
-               workspace)
+               ps_kmeans_fit, ps_kmeans_fit_nvfp4, ps_proxy_attn, ps_refresh_gather, ps_residual_nvfp4,
+               ps_topk_clusters, workspace)
 
 
 @dataclass
@@ -67,6 +67,7 @@ class StepSpec:
     tau_s: float = 0.9
     cluster_score: str = "kl"    # "kl" (drift share) or "cosine" (centre movement)
     residual_store: str = "device"  # "device" (HBM) or "host" (pinned host memory)
+    fused_coding: bool = True    # K-Means and the residual coding in one call (the same results)
 
     @property
     def shape(self) -> Shape:
@@ -164,7 +165,11 @@ class DriftPath:
         if cosine:
             with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
                 self.C_prev.copy_(self.C)
-        if recluster:
+        if recluster and sp.fused_coding:
+            ps_kmeans_fit_nvfp4(s, dt, H, Kr, init, sp.iters, self.C, self.assign, self.counts, self.row_norm,
+                                self.codes, self.bscale, self.rscale, self.Ck, self.objective, self.ws, stream,
+                                flags=sp.kmeans_flags)
+        elif recluster:
             ps_kmeans_fit(s, dt, H, Kr, init, sp.iters, self.C, self.assign, self.counts, self.row_norm,
                           self.Ck, self.objective, self.ws, stream, flags=sp.kmeans_flags)
             ps_residual_nvfp4(s, dt, H, self.row_norm, self.C, self.assign, self.codes, self.bscale,

@@ -104,8 +104,8 @@ typedef struct {
 /* Human-readable name of a status code (static storage). */
 const char* ps_status_string(ps_status status);
 
-/* Bytes of scratch that ps_kmeans_fit (and ps_residual_nvfp4) need for this
- * shape and dtype. */
+/* Bytes of scratch that ps_kmeans_fit, ps_kmeans_fit_nvfp4 and
+ * ps_residual_nvfp4 need for this shape and dtype. */
 ps_status ps_workspace_size(const ps_shape* shape, ps_dtype dtype, size_t* bytes);
 
 /*
@@ -165,6 +165,29 @@ ps_status ps_kmeans_fit_static(const ps_shape* shape, ps_dtype dtype, const void
                                ps_init init, int32_t iters, uint32_t flags, float* C, int32_t* assign,
                                int32_t* counts, float* row_norm, void* Ck, double* objective,
                                void* stream);
+
+/*
+ * ps_kmeans_fit_nvfp4 -- ps_kmeans_fit followed by ps_residual_nvfp4 of its
+ * outputs (H, row_norm, C, assign), in one call: the clusters of section 2.A
+ * (local window and clustering) and the NVFP4 residuals stored for them.
+ * Every output is bit-identical to the two calls made in turn.  With bf16
+ * rows of up to 4096 elements the first Lloyd update codes each cluster's
+ * member rows right after rebuilding its centre, while those rows are still
+ * cached, and after the last iteration only the rows of clusters rebuilt
+ * since are coded again; otherwise the coder runs after the fit.
+ *
+ *   codes [W][N][d/2] u8, bscale [W][N][d/16] u8, rscale [W][N] f32   out
+ *                                    (as ps_residual_nvfp4)
+ *   ws, ws_bytes                     scratch of ps_workspace_size bytes
+ *                                    (smaller or NULL: PS_ERR_WORKSPACE)
+ *   every other argument, limit and error as ps_kmeans_fit; NULL codes,
+ *   bscale or rscale: PS_ERR_NULL.
+ */
+ps_status ps_kmeans_fit_nvfp4(const ps_shape* shape, ps_dtype dtype, const void* H, const void* Kr,
+                              ps_init init, int32_t iters, uint32_t flags, float* C, int32_t* assign,
+                              int32_t* counts, float* row_norm, void* Ck, double* objective,
+                              uint8_t* codes, uint8_t* bscale, float* rscale, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /*
  * ps_residual_nvfp4 -- NVFP4 coding of each row's residual to its centre

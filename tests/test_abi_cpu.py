@@ -111,6 +111,33 @@ def test_kmeans_fit_argument_checks(L):
     assert _fit(L, _shape(W=0)) == OK
 
 
+def _fit_code(L, shape, dtype=1, H=FAKE, iters=2, codes=FAKE, bscale=FAKE, rscale=FAKE, ws=FAKE,
+              ws_bytes=1 << 30, flags=0):
+    return L.ps_kmeans_fit_nvfp4(ctypes.byref(shape), dtype, H, None, 1, iters, flags, FAKE, FAKE, FAKE, FAKE,
+                                 None, None, codes, bscale, rscale, ws, ws_bytes, None)
+
+
+def test_kmeans_fit_nvfp4_argument_checks(L):
+    """The fit-and-code call checks the K-Means arguments, then the coder's
+    outputs, then the workspace (ps_workspace_size covers both calls)."""
+    s = _shape()
+    assert _fit_code(L, s, H=None) == NULL
+    assert _fit_code(L, s, iters=0) == RANGE
+    assert _fit_code(L, _shape(K=65)) == SHAPE
+    assert _fit_code(L, s, codes=None) == NULL
+    assert _fit_code(L, s, bscale=None) == NULL
+    assert _fit_code(L, s, rscale=None) == NULL
+    assert _fit_code(L, s, rscale=MISALIGNED) == ALIGN
+    assert _fit_code(L, s, ws=None) == WORKSPACE
+    for kw in (dict(), dict(W=3, N=4000, d=16, K=1), dict(W=2, N=300, d=4096, K=64), dict(d=8192)):
+        for dt in (0, 1):
+            sh = _shape(**kw)
+            n = ctypes.c_size_t(0)
+            assert L.ps_workspace_size(ctypes.byref(sh), dt, ctypes.byref(n)) == OK
+            assert _fit_code(L, sh, dtype=dt, ws_bytes=n.value - 1) == WORKSPACE, (kw, dt)
+    assert _fit_code(L, _shape(W=0)) == OK          # nothing to do: no device touched
+
+
 def _fit_static(L, shape, dtype=1, H=FAKE, Kr=None, init=1, iters=2, C=FAKE, Ck=None, flags=0):
     return L.ps_kmeans_fit_static(ctypes.byref(shape), dtype, H, Kr, init, iters, flags, C, FAKE, FAKE, FAKE,
                                   Ck, None, None)

@@ -49,6 +49,17 @@ def test_coder_bytes():
     assert bench.kernel_work("k_residual_listed<T, CPL>", CFG) is None
 
 
+def test_coding_update_bytes():
+    """The first update that also codes the rows: the update's bytes plus the
+    codes and scales written; the rows are read once."""
+    W, N, d, K = CFG.W, CFG.N, CFG.d, CFG.K
+    upd, _ = bench.kernel_work("k_update<T, CH>", CFG)
+    both, _ = bench.kernel_work("k_update_code<CH, BPL, FULL>", CFG)
+    assert both - upd == W * N * d // 2 + W * N * d // 16 + W * N * 4
+    coder, _ = bench.kernel_work("k_residual_grouped<T, BPL, FULL>", CFG)
+    assert both < upd + coder          # neither the rows nor the centres read twice
+
+
 def test_proxy_counts_the_previous_distribution():
     L = CFG.W * CFG.Hq * CFG.Nb * CFG.K
     q = CFG.W * CFG.Nb * CFG.Hq * CFG.dh * 2
