@@ -63,6 +63,11 @@ def kernel_work(name, cfg, gathered=None):
                 + W * N * d // 2 + W * N * d // 16 + W * N * 4, W * N * d * 10.0)
     if name.startswith("k_update"):
         return W * N * d * e + 2 * W * N * 4 + W * K * d * (4 + e) + W * (K + 1) * 4, W * N * d * 2.0
+    if name.startswith("k_code_stale"):
+        # every cluster coded again (the kernel counts the clusters it codes):
+        # rows, norms and centres read, codes and scales written
+        return (W * N * d * e + 2 * W * N * 4 + W * K * d * 4 + W * (K + 1) * 4
+                + W * N * d // 2 + W * N * d // 16 + W * N * 4, W * N * d * 8.0)
     if name.startswith("k_residual_grouped") or name.startswith("k_residual<"):
         return (W * N * d * e + W * K * d * 4 + 3 * W * N * 4 + W * N * d // 2 + W * N * d // 16,
                 W * N * d * 8.0)

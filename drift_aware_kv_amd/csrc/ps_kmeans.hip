@@ -15,6 +15,10 @@
 //           fp32 centre plus its bf16 copy for the next assignment; after the
 //           first iteration only clusters whose member set changed run.
 // After the last iteration the keys kernel averages the member key rows.
+// The fit-and-code call (ps_kmeans_fit_nvfp4) replaces the first update by
+// one that also codes every cluster's member rows in NVFP4 right after
+// rebuilding its centre; later updates mark the clusters they rebuild, and
+// those clusters' rows are coded again after the last iteration.
 #include "ps_common.h"
 #include "ps_nvfp4_row.h"
 
