@@ -1038,20 +1038,20 @@ __device__ __forceinline__ int stage_members(const int32_t* __restrict__ pm, int
 }
 
 // ---------------------------------------------------------------------------
-// update: one workgroup per (window, cluster)
+// update: one workgroup per (window, cluster), or per `cpb` consecutive
+// clusters of the batch when most clusters are expected unchanged (the
+// updates after the first): fewer workgroups that exit at once
 // ---------------------------------------------------------------------------
 template <typename T, int CH>
-__global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const float* __restrict__ row_norm,
-                                                 const int32_t* __restrict__ perm,
-                                                 const int32_t* __restrict__ offs, float* __restrict__ C,
-                                                 uint16_t* __restrict__ Cb, int32_t* __restrict__ counts,
-                                                 double* __restrict__ nrm_out, int32_t* __restrict__ dirty,
-                                                 int32_t* __restrict__ stale, int N, int d, int K, int nblocks,
-                                                 int all, int* __restrict__ work)
+__device__ __forceinline__ void update_cluster(const T* __restrict__ H, const float* __restrict__ row_norm,
+                                               const int32_t* __restrict__ perm,
+                                               const int32_t* __restrict__ offs, float* __restrict__ C,
+                                               uint16_t* __restrict__ Cb, int32_t* __restrict__ counts,
+                                               double* __restrict__ nrm_out, int32_t* __restrict__ dirty,
+                                               int32_t* __restrict__ stale, int N, int d, int K, int w, int k,
+                                               int all, int* __restrict__ work)
 {
     __shared__ double red[4];
-    const int Lg = xcd_remap(blockIdx.x, nblocks);
-    const int w = Lg / K, k = Lg - w * K;
     // an unchanged member set gives a bit-identical sum: keep the centre
     if (!all && !dirty[(size_t)w * K + k]) return;
     if (work && threadIdx.x == 0) atomicAdd(work, 1);   // kernel timer: one cluster re-summed
@@ -1121,6 +1121,30 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
                 store8(Cb + ((size_t)w * K + k) * d + e, v);
             }
         }
+    }
+}
+
+template <typename T, int CH>
+__global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const float* __restrict__ row_norm,
+                                                 const int32_t* __restrict__ perm,
+                                                 const int32_t* __restrict__ offs, float* __restrict__ C,
+                                                 uint16_t* __restrict__ Cb, int32_t* __restrict__ counts,
+                                                 double* __restrict__ nrm_out, int32_t* __restrict__ dirty,
+                                                 int32_t* __restrict__ stale, int N, int d, int K, int nblocks,
+                                                 int cpb, int nclusters, int all, int* __restrict__ work)
+{
+    const int Lg = xcd_remap(blockIdx.x, nblocks);
+    const int g0 = Lg * cpb, lane = lane_id();
+    // the workgroup's clusters to rebuild, one flag load per cluster, all at once (every wave
+    // takes the same mask); cluster g of the batch is (g / K, g % K), its flag dirty[g]
+    const bool todo = lane < cpb && g0 + lane < nclusters && (all || dirty[g0 + lane] != 0);
+    const uint64_t mask = __ballot(todo);
+    for (int i = 0; i < cpb; ++i) {
+        if (!((mask >> i) & 1)) continue;        // workgroup-uniform
+        __syncthreads();                         // the previous cluster's LDS reads are done
+        const int g = g0 + i, w = g / K, k = g - w * K;
+        update_cluster<T, CH>(H, row_norm, perm, offs, C, Cb, counts, nrm_out, dirty, stale, N, d, K, w, k, all,
+                              work);
     }
 }
 
@@ -1250,9 +1274,9 @@ __global__ __launch_bounds__(256, 3) void k_update_code(const uint16_t* __restri
     code_members<BPL, FULL>(Hw, rn, pm, beg, end, cs, codes, bscale, rscale, list, listed, (size_t)w * N, d);
 }
 
-// Coding again after the last iteration: one workgroup per (window, cluster)
-// of a cluster rebuilt after the coding update (stale); the others exit at
-// once.  The centre is the final one in C.
+// Coding again after the last iteration: the rows of each cluster rebuilt
+// after the coding update (stale), against its final centre in C; a
+// workgroup takes `cpb` consecutive clusters and skips the unmarked ones.
 template <int BPL, bool FULL>
 __global__ __launch_bounds__(256, 3) void k_code_stale(const uint16_t* __restrict__ H,
                                                        const float* __restrict__ row_norm,
@@ -1263,25 +1287,32 @@ __global__ __launch_bounds__(256, 3) void k_code_stale(const uint16_t* __restric
                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ bscale,
                                                        float* __restrict__ rscale, int32_t* __restrict__ list,
                                                        int32_t* __restrict__ listed, int N, int d, int K,
-                                                       int nblocks, int* __restrict__ work)
+                                                       int nblocks, int cpb, int nclusters, int* __restrict__ work)
 {
     __shared__ float cs[4096];
     const int Lg = xcd_remap(blockIdx.x, nblocks);
-    const int w = Lg / K, k = Lg - w * K;
-    if (!stale[(size_t)w * K + k]) return;
-    const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
-    if (end == beg) return;
-    if (work && threadIdx.x == 0) atomicAdd(work, 1);   // kernel timer: one cluster coded
-    const float* c = C + ((size_t)w * K + k) * d;
-    for (int e = 8 * (int)threadIdx.x; e < d; e += 8 * 256) {
-        float v[8];
-        load8(c + e, v);
+    const int g0 = Lg * cpb, lane = lane_id();
+    // the workgroup's clusters to code, one flag load per cluster, all at once
+    const bool todo = lane < cpb && g0 + lane < nclusters && stale[g0 + lane] != 0;
+    const uint64_t mask = __ballot(todo);
+    for (int i = 0; i < cpb; ++i) {
+        if (!((mask >> i) & 1)) continue;        // workgroup-uniform
+        const int g = g0 + i, w = g / K, k = g - w * K;
+        const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
+        if (end == beg) continue;
+        if (work && threadIdx.x == 0) atomicAdd(work, 1);   // kernel timer: one cluster coded
+        __syncthreads();                         // the previous cluster's coding no longer reads cs
+        const float* c = C + ((size_t)w * K + k) * d;
+        for (int e = 8 * (int)threadIdx.x; e < d; e += 8 * 256) {
+            float v[8];
+            load8(c + e, v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cs[e + i] = v[i];
+            for (int q = 0; q < 8; ++q) cs[e + q] = v[q];
+        }
+        __syncthreads();
+        code_members<BPL, FULL>(H + (size_t)w * N * d, row_norm + (size_t)w * N, perm + (size_t)w * N, beg, end,
+                                cs, codes, bscale, rscale, list, listed, (size_t)w * N, d);
     }
-    __syncthreads();
-    code_members<BPL, FULL>(H + (size_t)w * N * d, row_norm + (size_t)w * N, perm + (size_t)w * N, beg, end, cs,
-                            codes, bscale, rscale, list, listed, (size_t)w * N, d);
 }
 
 // centroid keys: mean of the member key rows, fp64 in ascending member order,
@@ -1387,14 +1418,24 @@ KmWs km_layout(const ps_shape* s, int dtype, void* base, bool coding = false)
     return L;
 }
 
+// clusters per workgroup in the updates after the first: most clusters are
+// unchanged there, so on large batches four share a workgroup (a quarter of
+// the workgroups to dispatch); one each on small batches and in the first
+// update, where every cluster is rebuilt
+int update_cpb(const ps_shape* s, int all)
+{
+    return (!all && s->W * s->K >= 16384) ? 4 : 1;
+}
+
 template <typename T, int CH>
 void launch_update(const ps_shape* s, const void* H, const float* rn, const KmWs& ws, float* C,
                    int32_t* counts, int all, hipStream_t st)
 {
-    const int nblocks = s->W * s->K;
-    PS_LAUNCH_COUNTED("k_update<T, CH>", nblocks, (k_update<T, CH>), dim3(nblocks), dim3(256), 0, st, (const T*)H,
-                      rn, ws.perm, ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, ws.stale, s->N, s->d, s->K, nblocks,
-                      all);
+    const int nclusters = s->W * s->K, cpb = update_cpb(s, all);
+    const int nblocks = (nclusters + cpb - 1) / cpb;
+    PS_LAUNCH_COUNTED("k_update<T, CH>", nclusters, (k_update<T, CH>), dim3(nblocks), dim3(256), 0, st,
+                      (const T*)H, rn, ws.perm, ws.offs, C, ws.Cb, counts, ws.nrm, ws.dirty, ws.stale, s->N, s->d,
+                      s->K, nblocks, cpb, nclusters, all);
 }
 
 // outputs of the residual coding folded into a K-Means call
@@ -1430,15 +1471,16 @@ template <int BPL>
 void launch_code_stale(const ps_shape* s, const void* H, const float* rn, const KmWs& ws, const float* C,
                        const Coding& cd, hipStream_t st)
 {
-    const int nblocks = s->W * s->K;
+    const int nclusters = s->W * s->K, cpb = update_cpb(s, 0);
+    const int nblocks = (nclusters + cpb - 1) / cpb;
     if (s->d / 16 == 64 * BPL)
-        PS_LAUNCH_COUNTED("k_code_stale<BPL, FULL>", nblocks, (k_code_stale<BPL, true>), dim3(nblocks), dim3(256), 0,
+        PS_LAUNCH_COUNTED("k_code_stale<BPL, FULL>", nclusters, (k_code_stale<BPL, true>), dim3(nblocks), dim3(256), 0,
                           st, (const uint16_t*)H, rn, ws.perm, ws.offs, C, ws.stale, cd.codes, cd.bscale, cd.rscale,
-                          ws.list, ws.listed, s->N, s->d, s->K, nblocks);
+                          ws.list, ws.listed, s->N, s->d, s->K, nblocks, cpb, nclusters);
     else
-        PS_LAUNCH_COUNTED("k_code_stale<BPL, FULL>", nblocks, (k_code_stale<BPL, false>), dim3(nblocks), dim3(256), 0,
-                          st, (const uint16_t*)H, rn, ws.perm, ws.offs, C, ws.stale, cd.codes, cd.bscale, cd.rscale,
-                          ws.list, ws.listed, s->N, s->d, s->K, nblocks);
+        PS_LAUNCH_COUNTED("k_code_stale<BPL, FULL>", nclusters, (k_code_stale<BPL, false>), dim3(nblocks), dim3(256),
+                          0, st, (const uint16_t*)H, rn, ws.perm, ws.offs, C, ws.stale, cd.codes, cd.bscale,
+                          cd.rscale, ws.list, ws.listed, s->N, s->d, s->K, nblocks, cpb, nclusters);
 }
 
 template <bool FIRST>
