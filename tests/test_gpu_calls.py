@@ -133,7 +133,9 @@ ITER_CASES = [("ragged-bf16", 3, 300, 80, 37, True), ("llada-rows", 2, 1024, 409
               ("k300-two-groups-ragged", 1, 640, 192, 300, True),
               ("k150-one-chunk", 2, 300, 64, 150, True),
               ("k200-d96", 1, 500, 96, 200, True),   # d not a multiple of 64: register-staged passes
-              ("k200-d8192", 1, 400, 8192, 200, True)]
+              ("k200-d8192", 1, 400, 8192, 200, True),
+              # 16384 clusters in the batch: the later updates take four per workgroup
+              ("k256-w64", 64, 512, 128, 256, True)]
 
 
 @pytest.mark.parametrize("case", ITER_CASES, ids=[c[0] for c in ITER_CASES])

@@ -43,6 +43,7 @@ CASES = [
     ("k20-d3072", 1, 300, 3072, 20, True),        # 4 blocks a lane, ragged, two update chunks
     ("k8-f32", 2, 200, 64, 8, False),             # fp32: the coder runs after the fit
     ("k70-d8192", 1, 300, 8192, 70, True),        # rows over 4096: the coder runs after the fit
+    ("k256-w64", 64, 512, 256, 256, True),        # 16384 clusters: four per workgroup in the later updates
 ]
 
 OUTS = ("C", "a", "cnt", "rn", "Ck", "obj", "codes", "bsc", "rsc")
