@@ -5,7 +5,8 @@ later Lloyd updates rebuild some clusters and their rows are coded again),
 on every thread layout of the coding update (1, 2 or 4 blocks of 16 per
 lane, full rows and ragged ones), on the shapes that fall back to the coder
 after the fit (fp32, rows longer than 4096), with rows the fast path
-declines (zero rows, subnormal entries) and clusters that lose every member.
+declines (zero rows, subnormal entries), clusters that lose every member and
+clusters whose members are all zero rows (centres kept).
 The two calls are themselves checked against the oracle elsewhere; the
 pipeline's chained parity tests run the fit-and-code call against the
 oracle."""
@@ -44,6 +45,7 @@ CASES = [
     ("k8-f32", 2, 200, 64, 8, False),             # fp32: the coder runs after the fit
     ("k70-d8192", 1, 300, 8192, 70, True),        # rows over 4096: the coder runs after the fit
     ("k256-w64", 64, 512, 256, 256, True),        # 16384 clusters: four per workgroup in the later updates
+    ("k1-d48", 2, 130, 48, 1, True),              # one cluster: every row coded by one workgroup
 ]
 
 OUTS = ("C", "a", "cnt", "rn", "Ck", "obj", "codes", "bsc", "rsc")
@@ -104,6 +106,8 @@ def test_fit_and_code_matches_the_two_calls(P, case, flags):
             H32[0, 1] = 0.0
         if t == 2:
             H32[1 % W, :, :] = H32[1 % W, :1, :]    # one window of identical rows: clusters lose every member
+        if t == 1 and W >= 3:
+            H32[2] = 0.0                           # a window of zero rows: members but no sum, centres kept
         Hd = dev(_to_dtype(H32, bf))
         init = P.PS_INIT_STRIDED if t == 0 else P.PS_INIT_GIVEN
         iters = 1 if t == 3 else 8                 # one iteration: only the coding update
