@@ -962,9 +962,10 @@ __global__ __launch_bounds__(64 * kBucketWaves) void k_bucket(const int32_t* __r
 // batch: the last member again, past the row: its last 8 elements, neither
 // added), so each wait covers exactly the rows it needs.
 // ---------------------------------------------------------------------------
-template <typename T, int CH, bool WEIGHTED>
+template <typename T, int CH, bool WEIGHTED, int CACHE = 0>
 __device__ __forceinline__ void member_sums(const T* __restrict__ rows, int rowlen, int e0,
-                                            const int* mid, const double* mw, int nv, double (&acc)[CH][8])
+                                            const int* mid, const double* mw, int nv, double (&acc)[CH][8],
+                                            uint16_t* cache = nullptr)
 {
     if (nv <= 0) return;
     int off[CH];
@@ -995,6 +996,18 @@ __device__ __forceinline__ void member_sums(const T* __restrict__ rows, int rowl
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     acc[c][i] = WEIGHTED ? fma((double)X[u][c][i], wt, acc[c][i]) : acc[c][i] + (double)X[u][c][i];
+                if constexpr (CACHE > 0) {
+                    // the first CACHE members' rows kept in LDS for a later pass: the
+                    // upper halves of the fp32 values are the rows' bf16 bits
+                    if (m + u < CACHE) {
+                        uint4 q;
+                        q.x = (__float_as_uint(X[u][c][0]) >> 16) | (__float_as_uint(X[u][c][1]) & 0xffff0000u);
+                        q.y = (__float_as_uint(X[u][c][2]) >> 16) | (__float_as_uint(X[u][c][3]) & 0xffff0000u);
+                        q.z = (__float_as_uint(X[u][c][4]) >> 16) | (__float_as_uint(X[u][c][5]) & 0xffff0000u);
+                        q.w = (__float_as_uint(X[u][c][6]) >> 16) | (__float_as_uint(X[u][c][7]) & 0xffff0000u);
+                        *reinterpret_cast<uint4*>(cache + (size_t)(m + u) * rowlen + off[c]) = q;
+                    }
+                }
             }
         }
     };
@@ -1152,12 +1165,13 @@ __global__ __launch_bounds__(256) void k_update(const T* __restrict__ H, const f
 // rn, window row offset wrow) coded against the centre cs (LDS, fp32) by the
 // workgroup's four waves, one row per wave at a time, with the coder's fast
 // path; rows it declines are listed for the exact coder.
-template <int BPL, bool FULL>
+template <int BPL, bool FULL, int CACHE = 0>
 __device__ __forceinline__ void code_members(const uint16_t* __restrict__ Hw, const float* __restrict__ rn,
                                              const int32_t* __restrict__ pm, int beg, int end, const float* cs,
                                              uint8_t* __restrict__ codes, uint8_t* __restrict__ bscale,
                                              float* __restrict__ rscale, int32_t* __restrict__ list,
-                                             int32_t* __restrict__ listed, size_t wrow, int d)
+                                             int32_t* __restrict__ listed, size_t wrow, int d,
+                                             const uint16_t* rc = nullptr, const int* rc_id = nullptr)
 {
     const int lane = lane_id(), nb = d >> 4;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -1165,7 +1179,19 @@ __device__ __forceinline__ void code_members(const uint16_t* __restrict__ Hw, co
         const int j = pm[m];
         const size_t row = wrow + j;
         uint4 hq[BPL][2];
-        load_hblocks<uint16_t, 64, BPL>(Hw + (size_t)j * d, lane, nb, hq);
+        const int sl = m - beg;
+        bool cached = false;
+        if constexpr (CACHE > 0) cached = sl < CACHE && rc_id[sl] == j;   // wave-uniform
+        if (cached) {                            // the row the update kept in LDS
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+                const uint4* hp = reinterpret_cast<const uint4*>(rc + (size_t)sl * d + 16 * min(lane + 64 * b, nb - 1));
+                hq[b][0] = hp[0];
+                hq[b][1] = hp[1];
+            }
+        } else {
+            load_hblocks<uint16_t, 64, BPL>(Hw + (size_t)j * d, lane, nb, hq);
+        }
         // the centre's blocks from LDS for each row (registers stay free between rows)
         float cv[BPL][16];
 #pragma unroll
@@ -1183,6 +1209,10 @@ __device__ __forceinline__ void code_members(const uint16_t* __restrict__ Hw, co
         }
     }
 }
+
+// member rows the coding update keeps in LDS between rebuilding the centre and
+// coding them (8 KB each at 4096 elements; three workgroups still fit a CU)
+constexpr int kCodeCache = 4;
 
 // The first update of a call that also codes the residuals (bf16 rows of up
 // to 4096 elements): each workgroup rebuilds its cluster's centre exactly as
@@ -1211,6 +1241,8 @@ __global__ __launch_bounds__(256, 3) void k_update_code(const uint16_t* __restri
     __shared__ double mw[256];
     __shared__ int wcnt[4];
     __shared__ float cs[4096];                   // the centre, for the coding waves
+    __shared__ __attribute__((aligned(16))) uint16_t rc[kCodeCache * 4096];   // the first members' rows
+    __shared__ int rc_id[kCodeCache];
     const int Lg = xcd_remap(blockIdx.x, nblocks);
     const int w = Lg / K, k = Lg - w * K;
     const int beg = offs[(size_t)w * (K + 1) + k], end = offs[(size_t)w * (K + 1) + k + 1];
@@ -1230,7 +1262,13 @@ __global__ __launch_bounds__(256, 3) void k_update_code(const uint16_t* __restri
             wt = 1.0 / (double)n;
             return true;
         });
-        member_sums<uint16_t, CH, true>(Hw, d, 0, mid, mw, nv, acc);
+        if (b0 == beg) {
+            // the first batch's first rows stay in LDS (their row ids beside them)
+            if (threadIdx.x < kCodeCache) rc_id[threadIdx.x] = (int)threadIdx.x < nv ? mid[threadIdx.x] : -1;
+            member_sums<uint16_t, CH, true, kCodeCache>(Hw, d, 0, mid, mw, nv, acc, rc);
+        } else {
+            member_sums<uint16_t, CH, true>(Hw, d, 0, mid, mw, nv, acc);
+        }
     }
     double ss = 0.0;
 #pragma unroll
@@ -1271,7 +1309,8 @@ __global__ __launch_bounds__(256, 3) void k_update_code(const uint16_t* __restri
     }
     if (nk == 0) return;                         // workgroup-uniform
     __syncthreads();
-    code_members<BPL, FULL>(Hw, rn, pm, beg, end, cs, codes, bscale, rscale, list, listed, (size_t)w * N, d);
+    code_members<BPL, FULL, kCodeCache>(Hw, rn, pm, beg, end, cs, codes, bscale, rscale, list, listed,
+                                        (size_t)w * N, d, rc, rc_id);
 }
 
 // Coding again after the last iteration: the rows of each cluster rebuilt
